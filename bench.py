@@ -1,0 +1,268 @@
+"""Benchmark of the GNN-layer hot path on one MI355X.
+
+A step is one forward + backward pass of the whole model of a workload on
+its synthetic graph: halo gather (when the workload has a halo), then per
+layer the aggregation SpMM and the MFMA transform with its bias/ReLU
+epilogue, then per layer in reverse the weight-gradient product, the input
+gradient product and the transposed SpMM.  The CSR build and its schedule
+run once before the timed region (partitioning is amortised over training)
+and are reported as build_ms.
+
+Default workload: the 2.45M-node power-law graph, 3-layer GraphSAGE-mean
+100 -> 256 -> 256 -> 47 in bf16 with fp32 accumulation.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "GCN layer fwd+bwd ms; SpMM GB/s (% HBM peak) on 2.45M-node graph"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", type=int, default=4)
+    p.add_argument("--scale", type=float, default=1.0)
+    p.add_argument("--seg-len", type=int, default=1024)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU baseline sample (0: auto)")
+    return p.parse_args()
+
+
+class Model:
+    """Device-resident inputs, weights and buffers of one workload."""
+
+    def __init__(self, w, sag, torch, seg_len):
+        import numpy as np
+        dev = torch.device("cuda:0")
+        self.w, self.sag, self.torch, self.dev = w, sag, torch, dev
+        self.tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        src, dst = w.edges
+        log(f"[bench] graph: {w.n_global} ids, {src.size} edge records")
+        s_d = torch.from_numpy(src).to(dev)
+        d_d = torch.from_numpy(dst).to(dev)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.built = sag.csr_build_normalize(s_d, d_d, w.n_global, w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
+        sag.csr_schedule(self.built.A, seg_len)
+        sag.csr_schedule(self.built.AT, seg_len)
+        torch.cuda.synchronize()
+        self.build_ms = (time.perf_counter() - t0) * 1e3
+        del s_d, d_d
+        A = self.built.A
+        self.n_l, self.n_ext = A.n_rows, A.n_cols
+        self.n_h = self.n_ext - self.n_l
+        log(f"[bench] built: n_local={self.n_l} n_halo={self.n_h} nnz={A.nnz} in {self.build_ms:.1f} ms; "
+            f"schedule {sag.csr_info(A)}")
+
+        def dev_dense(x):
+            t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16) \
+                if w.dtype == "bf16" else torch.from_numpy(np.ascontiguousarray(x))
+            out = sag.empty_dense(x.shape[0], x.shape[1], self.tdt, dev)
+            out.copy_(t.to(dev))
+            return out
+
+        self.H0 = sag.empty_dense(self.n_ext, w.dims[0], self.tdt, dev)
+        self.H0[: self.n_l].copy_(dev_dense(w.features))
+        self.stale = dev_dense(w.stale) if self.n_h else None
+        self.W = [dev_dense(w.weights_stored(l)).contiguous() for l in range(w.n_layers)]
+        self.b = [torch.from_numpy(w.biases[l]).to(dev) for l in range(w.n_layers)]
+        self.G = dev_dense(w.grad_out)
+        self.fwd = sag.gcn_layer_forward if w.model == "gcn" else sag.sage_layer_forward
+        self.bwd = sag.gcn_layer_backward if w.model == "gcn" else sag.sage_layer_backward
+        # preallocated outputs and workspaces
+        self.out = [sag.empty_dense(self.n_l, w.dims[l + 1], self.tdt, dev) for l in range(w.n_layers)]
+        self.dH = [sag.empty_dense(self.n_ext if l == 0 else self.n_l, w.dims[l], self.tdt, dev)
+                   for l in range(w.n_layers)]
+        L = sag._lib.lib()
+        dt = sag.dtype_code(self.tdt)
+        kind = w.model
+        fw = max(getattr(L, f"sag_{kind}_forward_workspace_bytes")(A.ref, w.dims[l], w.dims[l + 1], dt)
+                 for l in range(w.n_layers))
+        bw = max(getattr(L, f"sag_{kind}_backward_workspace_bytes")(self.built.AT.ref, self.n_l, w.dims[l],
+                                                                     w.dims[l + 1], dt)
+                 for l in range(w.n_layers))
+        self.ws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device=dev)
+
+    def step(self):
+        w, sag = self.w, self.sag
+        if self.n_h:
+            sag.halo_gather(self.stale, self.built.halo_gid, self.H0[self.n_l:], row_base=w.stale_base)
+        x = self.H0
+        ctxs = []
+        for l in range(w.n_layers):
+            A = self.built.A
+            out, _, ctx = self.fwd(A, x, self.W[l], self.b[l], relu=w.relu[l], Out=self.out[l], ws=self.ws)
+            ctxs.append(ctx)
+            x = out
+        g = self.G
+        for l in reversed(range(w.n_layers)):
+            want_dH = l > 0
+            _, _, dH = self.bwd(ctxs[l], self.built.AT, self.n_l, self.out[l], g, want_dH=want_dH,
+                                dH=self.dH[l] if want_dH else None, ws=self.ws)
+            g = dH[: self.n_l] if want_dH else None
+        return x
+
+
+def cpu_baseline(w, rows_hint: int):
+    """The oracle (float64, as it stands) on a bounded sample: the local row
+    range [0, R) of the workload's graph treated as a partition (its halo
+    columns included), every layer's forward and backward; scaled to the
+    full graph by n_local / R."""
+    import numpy as np
+
+    import gen
+    from oracle import csr as ocsr, layers as olay, native
+
+    src, dst = w.edges
+    n_l = w.hi - w.lo
+    R = rows_hint or max(1024, min(n_l, 16384))
+    g = np.random.default_rng(0)
+    deg = None
+    if w.norm == "gcn":
+        # column degrees of the sample's halo columns: the whole graph's
+        deg = np.bincount(dst, minlength=w.n_global)
+        if w.symmetrize:
+            deg = deg + np.bincount(src, minlength=w.n_global)
+        deg = (deg + (1 if w.self_loops else 0)).astype(np.int32)
+    ob = ocsr.build(src, dst, w.n_global, w.lo, w.lo + R, w.symmetrize, w.self_loops, w.norm, deg_global=deg)
+    n_ext = ob.A.n_cols
+    total = 0.0
+    per_layer = []
+    for l in range(w.n_layers):
+        d_in, d_out = w.dims[l], w.dims[l + 1]
+        H = g.standard_normal((n_ext, d_in))
+        W = olay.as_f64(w.weights_stored(l), w.dtype)
+        b = w.biases[l]
+        G = g.standard_normal((R, d_out))
+        t0 = time.perf_counter()
+        if w.model == "gcn":
+            Z, Y, _ = olay.gcn_forward(ob.A, H, W, b, w.relu[l])
+            olay.gcn_backward(ob.AT, Z, W, Y, w.relu[l], G, want_dH=l > 0)
+        else:
+            M, Y, _ = olay.sage_forward(ob.A, H, R, W, b, w.relu[l])
+            olay.sage_backward(ob.AT, H[:R], M, W, Y, w.relu[l], G, want_dH=l > 0)
+        dt = time.perf_counter() - t0
+        per_layer.append(dt)
+        total += dt
+    scale = n_l / R
+    ms = total * scale * 1e3
+    return {
+        "value": round(ms, 1), "unit": "ms", "cores": native.num_threads(), "kind": "oracle",
+        "sample": (f"local rows [0,{R}) of the {n_l}-row graph as a partition ({n_ext - R} halo columns), "
+                   f"{w.n_layers}-layer fwd+bwd in float64 took {total:.2f} s, scaled by {scale:.1f}"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path here is one "
+              "GPU's share of a graph, with no collectives.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import gen
+    import sparse_aggregation_gemm_amd as sag
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = gen.make_config(args.config, args.scale)
+    log(f"[bench] workload {w.name} (scale {args.scale}): drawing the graph")
+    t0 = time.perf_counter()
+    _ = w.edges
+    log(f"[bench] graph drawn in {time.perf_counter() - t0:.1f} s")
+    m = Model(w, sag, torch, args.seg_len)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        m.step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    sag.trace_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        m.step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    sag.trace_enable(False)
+    recs = sag.trace_records(clear=True)
+    ms_step = elapsed * 1e3 / args.steps
+
+    # per-op statistics from the HIP events of the timed steps
+    ops = {}
+    for r in recs:
+        o = ops.setdefault(r["name"], {"n": 0, "ms": 0.0, "bytes": r["bytes"], "flops": r["flops"]})
+        o["n"] += 1
+        o["ms"] += r["ms"]
+    table = []
+    for name, o in ops.items():
+        avg = o["ms"] / o["n"]
+        table.append({"op": name, "launches_per_step": o["n"] / args.steps, "avg_ms": round(avg, 4),
+                      "ms_per_step": round(o["ms"] / args.steps, 4),
+                      "GBps": round(o["bytes"] / avg / 1e6, 1) if avg > 0 else None,
+                      "TFLOPs": round(o["flops"] / avg / 1e9, 2) if avg > 0 else None})
+    table.sort(key=lambda t: -t["ms_per_step"])
+    spmm = [t for t in table if t["op"].startswith("spmm")]
+    dom = table[0]
+    dom_o = ops[dom["op"]]
+    avg_s = dom["avg_ms"] / 1e3
+    ai = dom_o["flops"] / max(dom_o["bytes"], 1)
+    dtn = "bf16" if w.dtype == "bf16" else "f32"
+    ridge = MFMA_PEAK_TFLOPS[dtn] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if dom["op"].startswith("gemm") and ai > ridge:
+        roof = {"bound": "mfma", "achieved": round(dom_o["flops"] / avg_s / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS[dtn], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dom_o["bytes"] / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = dom["op"]
+    roof["alg_bytes_per_launch"] = dom_o["bytes"]
+    roof["avg_launch_ms"] = dom["avg_ms"]
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle on a row sample)")
+        cpu = cpu_baseline(w, args.cpu_rows)
+
+    A = m.built.A
+    out = {
+        "metric": METRIC, "value": round(ms_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
+                   "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "model": w.model,
+                   "seg_len": args.seg_len, "schedule": sag.csr_info(A)},
+        "build_ms": round(m.build_ms, 1),
+        "spmm": spmm,
+        "ops": table,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,349 @@
+/*
+ * sag.h -- C ABI of the MI355X (gfx950) GNN-layer hot path.
+ *
+ * One GNN layer's work on one GPU's share of a graph: pull halo rows from a
+ * stale-representation buffer, aggregate with a normalised sparse matrix
+ * (CSR SpMM), transform with a dense matrix (MFMA GEMM, bias and ReLU fused),
+ * and the backward pass (weight-gradient GEMM and the transposed SpMM).
+ *
+ * Sources (the four pages this library follows):
+ *  - "Reducing Communication in Graph Neural Network Training" (CAGNET
+ *    page), background section on GNN training: A gets self connections and
+ *    is normalised as D^-1/2 (A+I) D^-1/2 with D the modified degrees; a
+ *    layer computes sigma(A^T H W); SpMM and the dense product dominate and
+ *    backpropagation uses the same primitives.  Its 1D block-row section: one
+ *    process owns n/P consecutive rows.
+ *  - Sylvie (1-bit quantised halo communication): "Graph Engine" builds the
+ *    HALO node set of each partition; "Forward Propagation" multiplies the
+ *    normalised adjacency with the concatenation of local and recovered halo
+ *    rows; "Backward Propagation" sends the halo rows of the feature
+ *    gradient back to their owners.
+ *  - DIGEST (periodic stale representation synchronisation): the forward
+ *    pass on a subgraph is P_in H_in + P_out H~_out with P_m = P_in + P_out;
+ *    the "pull" operation copies H~_out from the stale store.
+ *  - A DistDGL review: partitioning is done once and amortised over training.
+ *
+ * Conventions
+ * -----------
+ *  - Edge u -> v means node v aggregates u: CSR row v lists its sources u
+ *    (the CAGNET page's A^T H).
+ *  - Dense matrices are row-major with a leading dimension `ld` counted in
+ *    elements.  Every dense pointer must be 16-byte aligned and ld times the
+ *    element size a multiple of 16 bytes (SAG_E_ALIGN otherwise).  Padding
+ *    elements (columns d .. ld-1) may hold anything: they are read only to
+ *    fill 16-byte vectors and never enter a result, and they are never
+ *    written.
+ *  - bf16 data is passed as uint16_t bit patterns.  Every conversion from
+ *    fp32 to bf16 rounds to nearest, ties to even.
+ *  - Pointers are DEVICE pointers unless the comment says "host".  `stream`
+ *    is a hipStream_t passed as void* (NULL = the null stream).
+ *  - Ownership: the caller allocates every buffer, including the workspace
+ *    `ws` whose size the matching *_workspace_bytes function returns (those
+ *    functions run on the host only).  The library allocates no device
+ *    memory, keeps no per-call state and may be called from several host
+ *    threads on different streams.
+ *  - Errors: arguments are validated on the host before anything is
+ *    launched; a failure returns a negative sag_status and launches nothing.
+ *    A HIP error returns SAG_E_HIP.  sag_last_error() gives a detail string
+ *    for the calling thread.  CSR contents (ordering, index ranges) are not
+ *    re-validated by compute calls: a CSR that did not come from
+ *    sag_csr_build_normalize (or equal one) gives undefined results.
+ *  - Every call is asynchronous on `stream` except the two documented as
+ *    synchronising (sag_csr_build_normalize and sag_csr_schedule).
+ *  - Results are deterministic: the same inputs, sizes and schedule give
+ *    the same bits on every run (no floating-point atomics).
+ */
+#ifndef SAG_H
+#define SAG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SAG_OK = 0,
+    SAG_E_INVALID = -1,      /* null pointer, bad size or range, bad enum     */
+    SAG_E_ALIGN = -2,        /* pointer or leading dimension not 16-B aligned */
+    SAG_E_WORKSPACE = -3,    /* workspace or output capacity too small        */
+    SAG_E_RANGE = -4,        /* an edge id outside [0, n_global)              */
+    SAG_E_HIP = -5,          /* a HIP runtime error                           */
+    SAG_E_UNSUPPORTED = -6   /* a size or dtype combination not implemented  */
+} sag_status;
+
+typedef enum { SAG_F32 = 0, SAG_BF16 = 1 } sag_dtype;
+
+/* Normalisation of the adjacency (the values stored in the CSR).
+ * SAG_NORM_GCN : entry (r, c) = 1 / sqrt(d_r * d_c), d = degrees of A + I
+ *                (CAGNET page, background; Sylvie, "Forward Propagation").
+ * SAG_NORM_MEAN: entry (r, c) = 1 / d_r (GraphSAGE mean aggregator).
+ * SAG_NORM_NONE: entry = 1.
+ * Values are computed in fp64 with correctly rounded sqrt and divide and
+ * rounded once to fp32; degrees below 1 are taken as 1. */
+typedef enum { SAG_NORM_GCN = 0, SAG_NORM_MEAN = 1, SAG_NORM_NONE = 2 } sag_norm;
+
+/* Build flags. */
+enum {
+    SAG_SYMMETRIZE = 1,   /* also use the reverse of every edge              */
+    SAG_SELF_LOOPS = 2    /* add one self connection per local row (A + I)  */
+};
+
+/* A CSR matrix in device memory (host struct of device pointers), with an
+ * optional degree-binned schedule.
+ *
+ * indptr[n_rows + 1] (int64), indices[nnz] (int32, column ids in
+ * [0, n_cols), ascending within a row), values[nnz] (fp32; NULL = all 1).
+ *
+ * Schedule (sag_csr_schedule fills it; sched == NULL means none): the rows
+ * are ordered by length class (floor(log2(len))), ascending row id within a
+ * class, and split in three bins: short rows (len <= 32) are summed by a
+ * group of lanes each, several rows per wavefront; medium rows (32 < len <=
+ * seg_len) by one wavefront each; long rows (len > seg_len) are cut into
+ * segments of seg_len entries, each summed by its own wavefront, and the
+ * segment sums of a row are then added in segment order.  `sched` points to
+ * 4 * n_rows int32 row records {row, len, start_lo, start_hi} in bin order,
+ * then 4 * n_seg segment records {long row index, start_lo, start_hi, len},
+ * then n_long + 1 int32 prefix counts of segments per long row.  Without a
+ * schedule every row is treated as a medium row in natural order (correct,
+ * slow on power-law degree laws). */
+typedef struct {
+    int64_t n_rows;
+    int64_t n_cols;
+    int64_t nnz;
+    const int64_t* indptr;
+    const int32_t* indices;
+    const float* values;
+    const int32_t* sched;
+    int64_t n_short;
+    int64_t n_medium;
+    int64_t n_long;
+    int64_t n_seg;
+    int32_t seg_len;
+    int32_t reserved;
+} sag_csr;
+
+/* ---------------------------------------------------------------------------
+ * CSR build (setup, once per graph partition; synchronises `stream`).
+ *
+ * Builds, for the local row range [lo, hi) of an edge list over node ids
+ * [0, n_global), the normalised adjacency A (n_local x (n_local + n_halo)),
+ * optionally its transpose AT ((n_local + n_halo) x n_local), the degrees
+ * and the HALO node list (Sylvie, "Graph Engine": the halo set of a
+ * partition; DIGEST: the out-of-subgraph neighbours pulled from the stale
+ * store).
+ *
+ * Steps: optional symmetrisation; input self-loops dropped; edges whose
+ * destination lies outside [lo, hi) dropped; duplicates collapsed (A is
+ * 0/1); optional self connections; halo_gid = ascending list of distinct
+ * source ids outside [lo, hi); a local column c becomes c - lo, a halo
+ * column n_local + its rank in halo_gid; each row sorted by column;
+ * deg[r] = entries of local row r; deg[n_local + k] = deg_global[halo_gid[k]]
+ * when deg_global is given, else 1 + (entries in halo column k); values per
+ * `norm`; AT row c lists the rows r holding column c, ascending, with the
+ * same values.
+ *
+ * src, dst : device int32[n_edges], edge src -> dst.
+ * deg_global: nullable device int32[n_global].
+ * Outputs (device, capacities in entries): indptr[n_local + 1];
+ *   indices, values: cap_nnz entries; indptr_t[cap_halo + n_local + 1],
+ *   indices_t, values_t: cap_nnz entries (all three NULL: no transpose);
+ *   deg[n_local + cap_halo] (nullable); halo_gid[cap_halo] (nullable when
+ *   no halo node appears).
+ * *nnz and *n_halo (host) receive the true sizes.  If an id lies outside
+ * [0, n_global) the call returns SAG_E_RANGE; if nnz > cap_nnz or n_halo >
+ * cap_halo it returns SAG_E_WORKSPACE with the sizes set and outputs
+ * unspecified.  Upper bounds: nnz <= (symmetrize ? 2 : 1) * n_edges +
+ * n_local, n_halo <= n_global - n_local.
+ */
+size_t sag_csr_build_workspace_bytes(int64_t n_edges, int64_t n_global,
+                                     int64_t lo, int64_t hi, unsigned flags);
+
+sag_status sag_csr_build_normalize(const int32_t* src, const int32_t* dst, int64_t n_edges,
+                                   int64_t n_global, int64_t lo, int64_t hi, unsigned flags,
+                                   sag_norm norm, const int32_t* deg_global,
+                                   int64_t cap_nnz, int64_t cap_halo,
+                                   int64_t* indptr, int32_t* indices, float* values,
+                                   int64_t* indptr_t, int32_t* indices_t, float* values_t,
+                                   int32_t* deg, int32_t* halo_gid,
+                                   int64_t* nnz /* host */, int64_t* n_halo /* host */,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Degree-binned schedule of a CSR (see sag_csr); synchronises `stream`.
+ * seg_len: long-row segment length, a multiple of 64 in [64, 65536].
+ * buf: device memory of sag_csr_schedule_bytes(A, seg_len) bytes, owned by
+ * the caller and referenced by *A afterwards.  Fills the schedule fields of
+ * *A (host struct). */
+size_t sag_csr_schedule_bytes(int64_t n_rows, int64_t nnz, int32_t seg_len);
+size_t sag_csr_schedule_workspace_bytes(int64_t n_rows);
+sag_status sag_csr_schedule(sag_csr* A, int32_t seg_len, void* buf, size_t buf_bytes,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Halo gather -- the DIGEST "pull": dst[k, :] = src[rows[k] - row_base, :]
+ * for k < n, a bitwise row copy of d elements of type dt.  rows: device
+ * int32[n] (typically the halo list of sag_csr_build_normalize, whose global
+ * ids map to stale-buffer rows by subtracting row_base); rows[k] - row_base
+ * must lie in [0, rows of src) (not checked).  src and dst must not overlap.
+ */
+sag_status sag_halo_gather(const void* src, int64_t ld_src, const int32_t* rows, int64_t row_base,
+                           int64_t n, int64_t d, sag_dtype dt, void* dst, int64_t ld_dst,
+                           void* stream);
+
+/* ---------------------------------------------------------------------------
+ * SpMM: Y = A X (CAGNET page: the aggregation A^T H of a layer, one output
+ * row per CSR row; DIGEST: P_in H_in + P_out H~_out when X = [H_in ; H~_out]).
+ * X: [A->n_cols, d] of type xt; Y: [A->n_rows, d] of type yt.  Supported
+ * (xt, yt): (F32, F32), (BF16, BF16), (BF16, F32).  Accumulation is fp32;
+ * d <= 1024 (fp32) or 2048 (bf16).
+ * addend (nullable, type yt, ld ld_add): Y[r] += addend[r] for r < n_add,
+ * added in fp32 before the single rounding to yt.
+ * ws: sag_spmm_workspace_bytes(A, d) bytes (0 unless A has long rows).
+ * sag_spmm_csr_t is the same operation, named for its use on the
+ * transposed matrix in the backward pass (dH_ext = A_norm^T dZ).
+ */
+size_t sag_spmm_workspace_bytes(const sag_csr* A, int64_t d);
+sag_status sag_spmm_csr(const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
+                        void* Y, int64_t ldy, sag_dtype yt,
+                        const void* addend, int64_t ld_add, int64_t n_add,
+                        void* ws, size_t ws_bytes, void* stream);
+sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
+                          void* Y, int64_t ldy, sag_dtype yt,
+                          const void* addend, int64_t ld_add, int64_t n_add,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Layers.  In all four calls: dt is the storage type of activations,
+ * activation gradients and W (F32 or BF16); accumulation is fp32; b, dW and
+ * db are fp32.  W is row-major [w_rows, d_out] with ld = d_out (no
+ * alignment needed).  n_local = A->n_rows; n_ext = A->n_cols = n_local +
+ * n_halo; H_ext is [n_ext, d_in] (ld ldh): local rows first, then the halo
+ * rows (e.g. from sag_halo_gather).  Y_pre (nullable) and Out are
+ * [n_local, d_out] with ld ldo.
+ *
+ * Association order.  (A H) W = A (H W): the layer aggregates first when
+ * d_in <= d_out and transforms first otherwise, so that the SpMM always
+ * runs at the narrower width.  `save` holds what the backward pass needs
+ * (the aggregate when aggregating first, nothing otherwise); its size is
+ * sag_*_save_bytes and its content is private to the library.  The
+ * backward call must get the same A^T, H_ext, W, save and sizes.
+ */
+
+/* GCN layer (CAGNET page, forward-propagation equation; Sylvie, "Forward
+ * Propagation"):  Y = A H_ext W + b;  Out = relu ? max(Y, 0) : Y. */
+size_t sag_gcn_save_bytes(int64_t n_local, int64_t d_in, int64_t d_out, sag_dtype dt);
+size_t sag_gcn_forward_workspace_bytes(const sag_csr* A, int64_t d_in, int64_t d_out, sag_dtype dt);
+sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
+                                 const void* W, const float* b, int64_t d_out, int relu,
+                                 sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                 void* save, size_t save_bytes,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* GCN backward (CAGNET page: backpropagation uses the same SpMM and dense
+ * products; Sylvie, "Backward Propagation": the halo rows of the input
+ * gradient are what a partition sends back; DIGEST: the weight gradient
+ * depends on the stale rows):
+ *   G_Y = relu ? G_out * 1[Y > 0] : G_out   (ReLU'(0) = 0)
+ *   dW = (A H_ext)^T G_Y  (fp32 [d_in, d_out], ld d_out)
+ *   db = column sums of G_Y (fp32 [d_out], nullable)
+ *   dH_ext = A^T G_Y W^T over AT ([n_ext, d_in], ld ldd, type dt;
+ *            NULL skips it).
+ * Y is the forward's Y_pre or its Out (same sign pattern; ld ldg, as G_out).
+ * AT may be NULL only when dH_ext is NULL and the layer aggregates first. */
+size_t sag_gcn_backward_workspace_bytes(const sag_csr* AT, int64_t n_local, int64_t d_in,
+                                        int64_t d_out, sag_dtype dt);
+sag_status sag_gcn_layer_backward(const sag_csr* AT, int64_t n_local,
+                                  const void* H_ext, int64_t ldh, int64_t d_in,
+                                  const void* W, int64_t d_out, int relu,
+                                  const void* Y, const void* G_out, int64_t ldg,
+                                  float* dW, float* db, void* dH_ext, int64_t ldd,
+                                  sag_dtype dt, const void* save, size_t save_bytes,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* GraphSAGE-mean layer (Sylvie, first section: the aggregate of the
+ * neighbours' rows enters the update together with the node's own row;
+ * mean aggregator, self first in the concatenation):
+ *   M = A_mean H_ext;  Y = [H_local | M] W + b;  Out = relu ? max(Y,0) : Y.
+ * W: [2 * d_in, d_out]; rows 0 .. d_in-1 act on the node's own row, the rest
+ * on M. */
+size_t sag_sage_save_bytes(int64_t n_local, int64_t d_in, int64_t d_out, sag_dtype dt);
+size_t sag_sage_forward_workspace_bytes(const sag_csr* A_mean, int64_t d_in, int64_t d_out,
+                                        sag_dtype dt);
+sag_status sag_sage_layer_forward(const sag_csr* A_mean, const void* H_ext, int64_t ldh,
+                                  int64_t d_in, const void* W, const float* b, int64_t d_out,
+                                  int relu, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                  void* save, size_t save_bytes,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* GraphSAGE-mean backward:
+ *   G_Y as for GCN;  dW = [H_local | M]^T G_Y (fp32 [2 * d_in, d_out]);
+ *   db = column sums of G_Y (nullable);  [dH_self | dM] = G_Y W^T;
+ *   dH_ext = A_mean^T dM over AT_mean, plus dH_self on the local rows
+ *   ([n_ext, d_in], ld ldd; NULL skips it). */
+size_t sag_sage_backward_workspace_bytes(const sag_csr* AT_mean, int64_t n_local, int64_t d_in,
+                                         int64_t d_out, sag_dtype dt);
+sag_status sag_sage_layer_backward(const sag_csr* AT_mean, int64_t n_local,
+                                   const void* H_ext, int64_t ldh, int64_t d_in,
+                                   const void* W, int64_t d_out, int relu,
+                                   const void* Y, const void* G_out, int64_t ldg,
+                                   float* dW, float* db, void* dH_ext, int64_t ldd,
+                                   sag_dtype dt, const void* save, size_t save_bytes,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Dense building blocks of the layers, exported for tests and for callers
+ * that compose their own layers.
+ *
+ * sag_gemm: C = [A1 | A2] B (+ bias) (+ addend), optionally ReLU, where A1
+ * is [M, K1] (ld lda1), A2 is [M, K2] (ld lda2; K2 = 0 and A2 = NULL for a
+ * single operand), B is [K1 + K2, N] row-major with ld ldb (trans_b = 0) or
+ * given as its transpose [N, K1 + K2] with ld ldb (trans_b = 1); A1, A2, B,
+ * addend and C have type dt; bias fp32[N]; C_pre (nullable) receives the
+ * value before ReLU.  mask (nullable, [M, K1], ld ldmask, type dt)
+ * multiplies A1 by 1[mask > 0] on load.
+ * sag_gemm_tn: C = [A1 | A2]^T Bm (fp32 [K1 + K2, N], ld ldc) and
+ * colsum = column sums of Bm (fp32[N], nullable), where Bm = B masked by
+ * 1[mask > 0] when mask is given; A1, A2 have M rows; B, mask: [M, N].
+ */
+size_t sag_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, sag_dtype dt);
+sag_status sag_gemm(int64_t M, int64_t N, const void* A1, int64_t lda1, int64_t K1,
+                    const void* A2, int64_t lda2, int64_t K2,
+                    const void* mask, int64_t ldmask,
+                    const void* B, int64_t ldb, int trans_b, const float* bias,
+                    const void* addend, int64_t ld_add, int relu,
+                    void* C, void* C_pre, int64_t ldc, sag_dtype dt,
+                    void* ws, size_t ws_bytes, void* stream);
+size_t sag_gemm_tn_workspace_bytes(int64_t M, int64_t K, int64_t N, sag_dtype dt);
+sag_status sag_gemm_tn(int64_t M, int64_t N, const void* A1, int64_t lda1, int64_t K1,
+                       const void* A2, int64_t lda2, int64_t K2,
+                       const void* B, int64_t ldb, const void* mask, int64_t ldmask,
+                       float* C, int64_t ldc, float* colsum, sag_dtype dt,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Measurement (opt-in; process-wide state, for benchmarks and profiling).
+ * While enabled, every internal operation (SpMM, dense product, mask,
+ * packing of B, halo gather) records a pair of HIP events on its stream,
+ * with its name and shape ("spmm[bf16,rows,nnz,d]", "gemm_nn[bf16,M,K,N]",
+ * ...), its algorithmic bytes (each operand read once, each output written
+ * once: for the SpMM 8 (rows + 1) + 8 nnz + elt d (cols + rows)) and flops.
+ * sag_trace_get synchronises on the record's stop event and returns its
+ * elapsed milliseconds; name receives at most name_cap bytes including the
+ * terminating NUL.  sag_trace_clear destroys the records. */
+sag_status sag_trace_enable(int on);
+int64_t sag_trace_count(void);
+sag_status sag_trace_get(int64_t i, char* name, size_t name_cap, float* ms, int64_t* bytes,
+                         int64_t* flops);
+sag_status sag_trace_clear(void);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics. */
+const char* sag_status_string(sag_status s);
+const char* sag_last_error(void);   /* detail of the calling thread's last error */
+const char* sag_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAG_H */

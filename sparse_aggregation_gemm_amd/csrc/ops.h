@@ -1,0 +1,77 @@
+// Internal launchers shared by the public entry points and the layers.
+#pragma once
+
+#include "common.h"
+
+namespace sag {
+
+// Epilogue applied to every output row of an SpMM or GEMM, in fp32 before
+// the single rounding to the output type:
+//   y = acc (+ addend[row] if row < n_add) (+ bias);  pre = y;
+//   out = relu ? max(y, 0) : y.
+struct Epilogue {
+    const void* addend = nullptr;   // output type, ld ld_add
+    int64_t ld_add = 0;
+    int64_t n_add = 0;
+    const float* bias = nullptr;    // [d]
+    int relu = 0;
+    void* pre = nullptr;            // output type, same ld as the output; nullable
+};
+
+// ---- SpMM ----------------------------------------------------------------------
+// Y[r, :d] = sum_p val[p] X[idx[p], :d]  for every row of A, with the epilogue.
+size_t spmm_ws_bytes(const sag_csr& A, int64_t d);
+sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
+                    int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, size_t ws_bytes,
+                    hipStream_t s);
+sag_status check_csr(const char* name, const sag_csr* A);
+
+// ---- dense products (MFMA) -------------------------------------------------------
+// Operand A of a GEMM: up to two column blocks along K, each [rows, K_i].
+// Rows >= m1 of block 1 read as zero (m1 < M lets block 1 cover only the
+// first rows).  mask (nullable) multiplies block 1 by 1[mask > 0].
+struct GemmA {
+    const void* a1 = nullptr;
+    int64_t lda1 = 0, k1 = 0, m1 = 0;
+    const void* a2 = nullptr;
+    int64_t lda2 = 0, k2 = 0;
+    const void* mask = nullptr;
+    int64_t ldmask = 0;
+};
+
+// Source of a packed B operand: element (k, n) of K-block s and N-block t is
+// p[s][t][kk * sk + nn * sn] (kk, nn local indices); a null pointer reads 0.
+struct PackSrc {
+    const void* p[2][2] = {{nullptr, nullptr}, {nullptr, nullptr}};
+    int64_t sk[2][2] = {{0, 0}, {0, 0}};
+    int64_t sn[2][2] = {{0, 0}, {0, 0}};
+};
+
+// Logical N layout of a packed B: columns [0, n0) come from N-block 0,
+// [nsplit, nsplit + n1) from N-block 1, the rest are zero.  Total width
+// n_total = nsplit + n1 (or n0 when n1 == 0).
+struct NLayout {
+    int64_t n0 = 0, nsplit = 0, n1 = 0;
+    int64_t total() const { return n1 ? nsplit + n1 : n0; }
+};
+
+size_t packed_b_bytes(int64_t k1, int64_t k2, int64_t n_total, sag_dtype dt);
+sag_status pack_b(const PackSrc& src, int64_t k1, int64_t k2, const NLayout& nl, sag_dtype dt,
+                  void* Bp, hipStream_t s);
+
+// C[M, N] = A Bp with the epilogue (C, pre and addend of type dt, ld ldc).
+sag_status gemm_run(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dtype dt,
+                    void* C, int64_t ldc, const Epilogue& epi, hipStream_t s);
+
+// C[K1 + K2, N] (fp32, ld ldc) = A^T Bm, colsum[N] (nullable) = column sums
+// of Bm; Bm = B [M, N] (ld ldb) masked by 1[mask > 0] when mask is given.
+size_t gemm_tn_ws_bytes(int64_t M, int64_t K, int64_t N, sag_dtype dt);
+sag_status gemm_tn_run(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t ldb,
+                       const void* mask, int64_t ldmask, float* C, int64_t ldc, float* colsum,
+                       sag_dtype dt, void* ws, size_t ws_bytes, hipStream_t s);
+
+// out[M, N] = G * 1[Y > 0] (all of type dt).
+sag_status relu_mask_run(int64_t M, int64_t N, const void* G, int64_t ldg, const void* Y,
+                         int64_t ldy, void* out, int64_t ldo, sag_dtype dt, hipStream_t s);
+
+}  // namespace sag

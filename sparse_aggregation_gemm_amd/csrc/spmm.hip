@@ -1,0 +1,509 @@
+// CSR SpMM Y = A X for the aggregation step of a GNN layer (CAGNET page:
+// the A^T H product, one output row per CSR row; DIGEST: P_in H_in +
+// P_out H~_out is one product over the columns [local | halo]).
+//
+// The product is bound by HBM bandwidth, so the kernels are built around
+// 16-byte feature loads: a row of X is split into C = ceil(d / V) vectors of
+// V elements (V = 4 fp32 or 8 bf16), and a group of G lanes (G = the power
+// of two >= C, at most 64; wider rows give each lane NV vectors) covers one
+// row of X.  A wavefront therefore holds P = 64 / G groups:
+//   short rows  -- each group sums its own row (P rows per wavefront);
+//   medium rows -- the wavefront sums one row, group g taking entries
+//                  g, g + P, ...; the P partial sums are then added by a
+//                  fixed butterfly;
+//   long rows   -- one wavefront per segment of seg_len entries writes an
+//                  fp32 partial row; a second kernel adds the partials of
+//                  each row in segment order.
+// Column indices and values are loaded cooperatively (one per lane) and
+// handed to the group that needs them with lane shuffles, so each lane keeps
+// several independent 16-byte loads in flight.  Accumulation is fp32 in a
+// fixed order, so results are bitwise reproducible.
+#include "ops.h"
+#include "trace.h"
+
+namespace sag {
+namespace {
+
+constexpr int kWaves = 4;
+
+template <class YT>
+struct EpiArgs {
+    YT* y;
+    int64_t ldy;
+    YT* pre;
+    const YT* add;
+    int64_t ld_add;
+    int64_t n_add;
+    const float* bias;
+    int relu;
+    int d;
+};
+
+template <class XT, class YT>
+struct SpArgs {
+    const XT* X;
+    int64_t ldx;
+    int C;                    // 16-B vectors per row of X
+    const int64_t* indptr;
+    const int32_t* idx;
+    const float* val;
+    const int4* rec_short;    // row records of each bin
+    const int4* rec_medium;   // (null: every row is medium, natural order)
+    const int4* rec_long;
+    int64_t n_short, n_medium, n_long, n_seg;
+    int64_t nb_seg, nb_medium;  // workgroups of the segment and medium bins
+    const int4* seg;          // segment records (long bin)
+    const int32_t* seg0;      // segments per long row, prefix
+    float* part;              // fp32 partial rows, ld = C * V
+    EpiArgs<YT> e;
+};
+
+template <class T>
+__device__ __forceinline__ void load_vals(const T* p, float* f, int n) {
+    constexpr int V = Vec<T>::N;
+    if (n == V) {
+        uint4 v = *reinterpret_cast<const uint4*>(p);
+        unpack<T>(v, f);
+    } else {
+        for (int e = 0; e < n; ++e) f[e] = to_f32(p[e]);
+    }
+}
+
+// Epilogue and store of V consecutive outputs starting at column ch * V.
+template <class YT, int V>
+__device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int ch, float* a) {
+    const int col0 = ch * V;
+    if (col0 >= e.d) return;
+    const int n = min(V, e.d - col0);
+    constexpr int VY = Vec<YT>::N;
+    if (e.add && row < e.n_add) {
+        float t[V];
+        const YT* ap = e.add + row * e.ld_add + col0;
+#pragma unroll
+        for (int q = 0; q < V; q += VY) {
+            const int nq = min(VY, n - q);
+            if (nq > 0) load_vals<YT>(ap + q, t + q, nq);
+        }
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            if (k < n) a[k] += t[k];
+    }
+    if (e.bias) {
+#pragma unroll
+        for (int k = 0; k < V; ++k)
+            if (k < n) a[k] += e.bias[col0 + k];
+    }
+    if (e.pre) {
+#pragma unroll
+        for (int q = 0; q < V; q += VY) {
+            const int nq = min(VY, n - q);
+            if (nq > 0) store_vals<YT>(e.pre + row * e.ldy + col0 + q, a + q, nq);
+        }
+    }
+    if (e.relu) {
+#pragma unroll
+        for (int k = 0; k < V; ++k) a[k] = a[k] < 0.f ? 0.f : a[k];
+    }
+#pragma unroll
+    for (int q = 0; q < V; q += VY) {
+        const int nq = min(VY, n - q);
+        if (nq > 0) store_vals<YT>(e.y + row * e.ldy + col0 + q, a + q, nq);
+    }
+}
+
+template <class XT>
+__device__ __forceinline__ uint4 load_x(const XT* X, int64_t ldx, int32_t c, int ch) {
+    return *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(c) * ldx + ch * Vec<XT>::N);
+}
+
+template <class XT, int NV, int U>
+__device__ __forceinline__ void accumulate(const XT* X, int64_t ldx, const int (&ch)[NV],
+                                           const int32_t (&c)[U], const float (&w)[U],
+                                           const bool (&ok)[U], float (&acc)[NV][Vec<XT>::N]) {
+    constexpr int V = Vec<XT>::N;
+    uint4 x[U][NV];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) x[u][v] = load_x(X, ldx, c[u], ch[v]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float f[V];
+            unpack<XT>(x[u][v], f);
+#pragma unroll
+            for (int k = 0; k < V; ++k) {
+                const float t = fmaf(w[u], f[k], acc[v][k]);
+                acc[v][k] = ok[u] ? t : acc[v][k];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ int64_t rec_start(const int4& r) {
+    return static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(r.z)) |
+                                (static_cast<uint64_t>(static_cast<uint32_t>(r.w)) << 32));
+}
+
+// ---- short rows: one group of G lanes per row -------------------------------
+template <class XT, class YT, int G, int NV>
+__device__ __forceinline__ void short_rows(const SpArgs<XT, YT>& p, int64_t block) {
+    constexpr int V = Vec<XT>::N;
+    constexpr int P = 64 / G;
+    constexpr int U = NV >= 4 ? 2 : (NV >= 2 ? 4 : 8);
+    const int lane = threadIdx.x & 63;
+    const int gl = lane % G, grp = lane / G;
+    const int64_t i = (block * kWaves + (threadIdx.x >> 6)) * P + grp;
+    const bool valid = i < p.n_short;
+    int row = 0, len = 0;
+    int64_t start = 0;
+    if (valid) {
+        const int4 r = p.rec_short[i];
+        row = r.x;
+        len = r.y;
+        start = rec_start(r);
+    }
+    int lmax = len;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) lmax = max(lmax, __shfl_xor(lmax, off, 64));
+    int ch[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) ch[v] = min(v * G + gl, p.C - 1);
+    float acc[NV][V];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int k = 0; k < V; ++k) acc[v][k] = 0.f;
+
+    for (int j0 = 0; j0 < lmax; j0 += G) {
+        const int jj = j0 + gl;
+        const bool mine = jj < len;
+        const int32_t c_my = mine ? p.idx[start + jj] : 0;
+        const float v_my = mine ? (p.val ? p.val[start + jj] : 1.f) : 0.f;
+        const int nh = min(G, lmax - j0);
+        for (int t = 0; t < nh; t += U) {
+            int32_t c[U];
+            float w[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int src = grp * G + min(t + u, G - 1);
+                c[u] = __shfl(c_my, src, 64);
+                w[u] = __shfl(v_my, src, 64);
+                ok[u] = (t + u < nh) && (j0 + t + u < len);
+            }
+            accumulate<XT, NV, U>(p.X, p.ldx, ch, c, w, ok, acc);
+        }
+    }
+    if (!valid) return;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int cv = v * G + gl;
+        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v]);
+    }
+}
+
+// Sums entries [start, start + len) of one row across the whole wavefront:
+// group g takes entries g, g + P, ...; returns the full sum in group 0.
+template <class XT, int G, int NV>
+__device__ __forceinline__ void wave_row_sum(const XT* X, int64_t ldx, int C,
+                                             const int32_t* idx, const float* val, int64_t start, int len,
+                                             float (&acc)[NV][Vec<XT>::N]) {
+    constexpr int V = Vec<XT>::N;
+    constexpr int P = 64 / G;
+    constexpr int U = NV >= 4 ? 2 : (NV >= 2 ? 4 : 8);
+    const int lane = threadIdx.x & 63;
+    const int gl = lane % G, grp = lane / G;
+    int ch[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) ch[v] = min(v * G + gl, C - 1);
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int k = 0; k < V; ++k) acc[v][k] = 0.f;
+    for (int j0 = 0; j0 < len; j0 += 64) {
+        const int jj = j0 + lane;
+        const bool mine = jj < len;
+        const int32_t c_my = mine ? idx[start + jj] : 0;
+        const float v_my = mine ? (val ? val[start + jj] : 1.f) : 0.f;
+        const int nh = min(64, len - j0);
+        for (int t = 0; t < nh; t += U * P) {
+            int32_t c[U];
+            float w[U];
+            bool ok[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int src = t + u * P + grp;
+                const int s2 = min(src, 63);
+                c[u] = __shfl(c_my, s2, 64);
+                w[u] = __shfl(v_my, s2, 64);
+                ok[u] = src < nh;
+            }
+            accumulate<XT, NV, U>(X, ldx, ch, c, w, ok, acc);
+        }
+    }
+    // add the P group sums with a fixed butterfly
+#pragma unroll
+    for (int off = G; off < 64; off <<= 1)
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int k = 0; k < V; ++k) acc[v][k] += __shfl_xor(acc[v][k], off, 64);
+}
+
+// ---- medium rows: one wavefront per row ----------------------------------------
+template <class XT, class YT, int G, int NV>
+__device__ __forceinline__ void medium_rows(const SpArgs<XT, YT>& p, int64_t block) {
+    constexpr int V = Vec<XT>::N;
+    const int64_t w = block * kWaves + (threadIdx.x >> 6);
+    if (w >= p.n_medium) return;
+    int64_t row, start;
+    int len;
+    if (p.rec_medium) {
+        const int4 r = p.rec_medium[w];
+        row = r.x;
+        len = r.y;
+        start = rec_start(r);
+    } else {
+        row = w;
+        start = p.indptr[w];
+        len = static_cast<int>(p.indptr[w + 1] - start);
+    }
+    float acc[NV][V];
+    wave_row_sum<XT, G, NV>(p.X, p.ldx, p.C, p.idx, p.val, start, len, acc);
+    const int lane = threadIdx.x & 63;
+    if (lane >= G) return;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int cv = v * G + lane;
+        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v]);
+    }
+}
+
+// ---- long rows: one wavefront per segment, fp32 partials -----------------------
+template <class XT, class YT, int G, int NV>
+__device__ __forceinline__ void segments(const SpArgs<XT, YT>& p, int64_t block) {
+    constexpr int V = Vec<XT>::N;
+    const int64_t sidx = block * kWaves + (threadIdx.x >> 6);
+    if (sidx >= p.n_seg) return;
+    const int4 sr = p.seg[sidx];
+    const int64_t start = static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(sr.y)) |
+                                               (static_cast<uint64_t>(static_cast<uint32_t>(sr.z)) << 32));
+    float acc[NV][V];
+    wave_row_sum<XT, G, NV>(p.X, p.ldx, p.C, p.idx, p.val, start, sr.w, acc);
+    const int lane = threadIdx.x & 63;
+    if (lane >= G) return;
+    float* out = p.part + sidx * static_cast<int64_t>(p.C) * V;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        const int cv = v * G + lane;
+        if (cv < p.C) {
+#pragma unroll
+            for (int q = 0; q < V; q += 4)
+                *reinterpret_cast<float4*>(out + cv * V + q) =
+                    make_float4(acc[v][q], acc[v][q + 1], acc[v][q + 2], acc[v][q + 3]);
+        }
+    }
+}
+
+// All three bins in one launch: the workgroups of long-row segments come
+// first (the longest work starts first), then medium rows, then short rows.
+template <class XT, class YT, int G, int NV>
+__global__ __launch_bounds__(256) void spmm_bins(SpArgs<XT, YT> p) {
+    int64_t b = blockIdx.x;
+    if (b < p.nb_seg) {
+        segments<XT, YT, G, NV>(p, b);
+        return;
+    }
+    b -= p.nb_seg;
+    if (b < p.nb_medium) {
+        medium_rows<XT, YT, G, NV>(p, b);
+        return;
+    }
+    short_rows<XT, YT, G, NV>(p, b - p.nb_medium);
+}
+
+// Adds the partial rows of each long row in segment order, then the epilogue.
+template <class XT, class YT>
+__global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
+    constexpr int V = Vec<XT>::N;
+    const int64_t j = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
+    if (j >= p.n_long) return;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = p.rec_long[j].x;
+    const int32_t s0 = p.seg0[j], s1 = p.seg0[j + 1];
+    const int64_t ldp = static_cast<int64_t>(p.C) * V;
+    for (int ch = lane; ch < p.C; ch += 64) {
+        float a[V];
+#pragma unroll
+        for (int k = 0; k < V; ++k) a[k] = 0.f;
+        for (int32_t s = s0; s < s1; ++s) {
+            const float* src = p.part + s * ldp + ch * V;
+#pragma unroll
+            for (int q = 0; q < V; q += 4) {
+                const float4 t = *reinterpret_cast<const float4*>(src + q);
+                a[q] += t.x;
+                a[q + 1] += t.y;
+                a[q + 2] += t.z;
+                a[q + 3] += t.w;
+            }
+        }
+        epi_store<YT, V>(p.e, row, ch, a);
+    }
+}
+
+template <class XT, class YT, int G, int NV>
+sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s) {
+    constexpr int P = 64 / G;
+    const int4* rec = reinterpret_cast<const int4*>(A.sched);
+    if (!rec) {
+        p.rec_medium = nullptr;
+        p.n_medium = A.n_rows;
+    } else {
+        p.rec_short = rec;
+        p.n_short = A.n_short;
+        p.rec_medium = rec + A.n_short;
+        p.n_medium = A.n_medium;
+        p.rec_long = rec + A.n_short + A.n_medium;
+        p.n_long = A.n_long;
+        p.seg = rec + A.n_rows;
+        p.seg0 = reinterpret_cast<const int32_t*>(rec + A.n_rows + A.n_seg);
+        p.n_seg = A.n_long > 0 ? A.n_seg : 0;
+    }
+    p.nb_seg = cdiv(p.n_seg, kWaves);
+    p.nb_medium = cdiv(p.n_medium, kWaves);
+    const int64_t nb_short = cdiv(p.n_short, kWaves * P);
+    const int64_t blocks = p.nb_seg + p.nb_medium + nb_short;
+    if (blocks > 0) {
+        spmm_bins<XT, YT, G, NV><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(p);
+        SAG_LAUNCH_CHECK();
+    }
+    if (p.n_long > 0) {
+        spmm_long_reduce<XT, YT><<<dim3(static_cast<unsigned>(cdiv(p.n_long, kWaves))), 256, 0, s>>>(p);
+        SAG_LAUNCH_CHECK();
+    }
+    return SAG_OK;
+}
+
+template <class XT, class YT>
+sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, void* Y, int64_t ldy,
+                     const Epilogue& epi, void* ws, hipStream_t s) {
+    constexpr int V = Vec<XT>::N;
+    SpArgs<XT, YT> p{};
+    p.X = static_cast<const XT*>(X);
+    p.ldx = ldx;
+    p.C = static_cast<int>(cdiv(d, V));
+    p.indptr = A.indptr;
+    p.idx = A.indices;
+    p.val = A.values;
+    p.part = static_cast<float*>(ws);
+    p.e.y = static_cast<YT*>(Y);
+    p.e.ldy = ldy;
+    p.e.pre = static_cast<YT*>(epi.pre);
+    p.e.add = static_cast<const YT*>(epi.addend);
+    p.e.ld_add = epi.ld_add;
+    p.e.n_add = epi.n_add;
+    p.e.bias = epi.bias;
+    p.e.relu = epi.relu;
+    p.e.d = static_cast<int>(d);
+    const int C = p.C;
+    if (C <= 4) return launch_bins<XT, YT, 4, 1>(A, p, s);
+    if (C <= 8) return launch_bins<XT, YT, 8, 1>(A, p, s);
+    if (C <= 16) return launch_bins<XT, YT, 16, 1>(A, p, s);
+    if (C <= 32) return launch_bins<XT, YT, 32, 1>(A, p, s);
+    if (C <= 64) return launch_bins<XT, YT, 64, 1>(A, p, s);
+    if (C <= 128) return launch_bins<XT, YT, 64, 2>(A, p, s);
+    if (C <= 192) return launch_bins<XT, YT, 64, 3>(A, p, s);
+    if (C <= 256) return launch_bins<XT, YT, 64, 4>(A, p, s);
+    return fail(SAG_E_UNSUPPORTED, "spmm: row width above 256 vectors of 16 bytes");
+}
+
+}  // namespace
+
+sag_status check_csr(const char* name, const sag_csr* A) {
+    const std::string n(name);
+    if (!A) return fail(SAG_E_INVALID, n + ": null CSR");
+    if (A->n_rows < 0 || A->n_cols < 0 || A->nnz < 0) return fail(SAG_E_INVALID, n + ": negative CSR size");
+    if (A->n_rows > INT32_MAX || A->n_cols > INT32_MAX) return fail(SAG_E_INVALID, n + ": CSR too large for int32 ids");
+    if (A->n_rows > 0 && !A->indptr) return fail(SAG_E_INVALID, n + ": null indptr");
+    if (A->nnz > 0 && !A->indices) return fail(SAG_E_INVALID, n + ": null indices");
+    if (A->nnz > 0 && A->n_cols == 0) return fail(SAG_E_INVALID, n + ": entries but no columns");
+    if (A->sched) {
+        if (A->n_short < 0 || A->n_medium < 0 || A->n_long < 0 || A->n_seg < 0 ||
+            A->n_short + A->n_medium + A->n_long != A->n_rows)
+            return fail(SAG_E_INVALID, n + ": inconsistent schedule counts");
+        if (A->n_long > 0 && (A->n_seg < A->n_long || A->seg_len < 64))
+            return fail(SAG_E_INVALID, n + ": inconsistent long-row schedule");
+        if (!aligned16(A->sched)) return fail(SAG_E_ALIGN, n + ": schedule not 16-B aligned");
+    }
+    return SAG_OK;
+}
+
+size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
+    if (!A.sched || A.n_long == 0) return 0;
+    const int64_t C = cdiv(d, 4);   // fp32 partials: C4 = ceil(d / 4) float4 vectors at most
+    return static_cast<size_t>(A.n_seg) * static_cast<size_t>(round_up(C * 4, 8)) * sizeof(float);
+}
+
+sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
+                    int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, size_t ws_bytes,
+                    hipStream_t s) {
+    if (A.n_rows == 0 || d == 0) return SAG_OK;
+    if (ws_bytes < spmm_ws_bytes(A, d) || (spmm_ws_bytes(A, d) > 0 && !ws))
+        return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
+    // algorithmic bytes: CSR arrays once, every X row once, every output once
+    const int64_t ex = elt_size(xt), ey = elt_size(yt);
+    const int64_t bytes = 8 * (A.n_rows + 1) + A.nnz * (A.values ? 8 : 4) + ex * d * A.n_cols +
+                          ey * d * A.n_rows * (epi.pre ? 2 : 1) + (epi.addend ? ey * d * epi.n_add : 0);
+    TraceScope trace(trace_enabled() ? shape_name("spmm", xt == SAG_BF16 ? (yt == SAG_BF16 ? "bf16" : "bf16>f32") : "f32",
+                                                  A.n_rows, A.nnz, d)
+                                     : std::string(),
+                     s, bytes, 2 * A.nnz * d);
+    if (xt == SAG_F32 && yt == SAG_F32) return run_typed<float, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
+    if (xt == SAG_BF16 && yt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, epi, ws, s);
+    if (xt == SAG_BF16 && yt == SAG_F32) return run_typed<uint16_t, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
+    return fail(SAG_E_UNSUPPORTED, "spmm: unsupported (X, Y) dtype pair");
+}
+
+}  // namespace sag
+
+using namespace sag;
+
+extern "C" size_t sag_spmm_workspace_bytes(const sag_csr* A, int64_t d) {
+    if (!A || d < 0) return 0;
+    return spmm_ws_bytes(*A, d);
+}
+
+static sag_status spmm_entry(const char* name, const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt,
+                             int64_t d, void* Y, int64_t ldy, sag_dtype yt, const void* addend,
+                             int64_t ld_add, int64_t n_add, void* ws, size_t ws_bytes, void* stream) {
+    SAG_TRY(check_csr(name, A));
+    if (d < 0) return fail(SAG_E_INVALID, std::string(name) + ": negative width");
+    const int64_t maxd = xt == SAG_BF16 ? 2048 : 1024;
+    if (d > maxd) return fail(SAG_E_UNSUPPORTED, std::string(name) + ": width too large");
+    SAG_TRY(check_dense("spmm X", X, A->nnz > 0 ? A->n_cols : 0, d, ldx, xt));
+    SAG_TRY(check_dense("spmm Y", Y, A->n_rows, d, ldy, yt));
+    if (n_add < 0 || n_add > A->n_rows) return fail(SAG_E_INVALID, std::string(name) + ": n_add out of range");
+    if (addend) SAG_TRY(check_dense("spmm addend", addend, n_add, d, ld_add, yt));
+    if (!(xt == SAG_F32 && yt == SAG_F32) && !(xt == SAG_BF16 && yt == SAG_BF16) &&
+        !(xt == SAG_BF16 && yt == SAG_F32))
+        return fail(SAG_E_UNSUPPORTED, std::string(name) + ": unsupported (X, Y) dtype pair");
+    Epilogue e;
+    e.addend = addend;
+    e.ld_add = ld_add;
+    e.n_add = addend ? n_add : 0;
+    return spmm_run(*A, X, ldx, xt, d, Y, ldy, yt, e, ws, ws_bytes, static_cast<hipStream_t>(stream));
+}
+
+extern "C" sag_status sag_spmm_csr(const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
+                                   void* Y, int64_t ldy, sag_dtype yt, const void* addend, int64_t ld_add,
+                                   int64_t n_add, void* ws, size_t ws_bytes, void* stream) {
+    return spmm_entry("spmm_csr", A, X, ldx, xt, d, Y, ldy, yt, addend, ld_add, n_add, ws, ws_bytes, stream);
+}
+
+extern "C" sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
+                                     void* Y, int64_t ldy, sag_dtype yt, const void* addend, int64_t ld_add,
+                                     int64_t n_add, void* ws, size_t ws_bytes, void* stream) {
+    return spmm_entry("spmm_csr_t", AT, X, ldx, xt, d, Y, ldy, yt, addend, ld_add, n_add, ws, ws_bytes, stream);
+}

@@ -1,0 +1,374 @@
+"""Thin Python binding of the C ABI, with the same names as its entry points.
+
+Argument marshalling only: tensors become device pointers, sizes and leading
+dimensions; PyTorch supplies device memory and the current stream.  Every
+step of the computation runs in libsag.so's HIP kernels.
+
+Dense operands are 2-D tensors with unit column stride whose row stride is
+the leading dimension (a multiple of 16 bytes); ``empty_dense`` allocates
+such a tensor with the row padded.  bf16 tensors are torch.bfloat16.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass, field
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.SAG_F32, torch.bfloat16: L.SAG_BF16}
+_NORM = {"gcn": L.SAG_NORM_GCN, "mean": L.SAG_NORM_MEAN, "none": L.SAG_NORM_NONE}
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def dtype_code(dtype: torch.dtype) -> int:
+    if dtype not in _DT:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return _DT[dtype]
+
+
+def padded_ld(d: int, dtype: torch.dtype) -> int:
+    v = 16 // torch.empty(0, dtype=dtype).element_size()
+    return max(v, (d + v - 1) // v * v)
+
+
+def empty_dense(rows: int, d: int, dtype: torch.dtype, device, fill=None) -> torch.Tensor:
+    """[rows, d] view of a [rows, ld] buffer with ld padded to 16 bytes."""
+    buf = torch.empty((rows, padded_ld(d, dtype)), dtype=dtype, device=device)
+    if fill is not None:
+        buf.fill_(fill)
+    return buf[:, :d]
+
+
+def as_dense(x: torch.Tensor) -> torch.Tensor:
+    """x with a 16-byte row pitch (copied into a padded buffer if needed)."""
+    es = x.element_size()
+    if x.dim() == 2 and x.stride(1) == 1 and (x.stride(0) * es) % 16 == 0 \
+            and x.stride(0) >= x.shape[1] and x.data_ptr() % 16 == 0:
+        return x
+    out = empty_dense(x.shape[0], x.shape[1], x.dtype, x.device)
+    out.copy_(x)
+    return out
+
+
+def _ld(x: torch.Tensor) -> int:
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("dense operands must be 2-D with unit column stride")
+    return max(x.stride(0), x.shape[1]) if x.shape[0] <= 1 else x.stride(0)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+@dataclass
+class Csr:
+    """A CSR matrix in device memory plus its optional schedule."""
+    n_rows: int
+    n_cols: int
+    indptr: torch.Tensor
+    indices: torch.Tensor
+    values: torch.Tensor | None
+    sched: torch.Tensor | None = None
+    raw: L.SagCsr = field(default_factory=L.SagCsr)
+
+    def __post_init__(self):
+        self.raw.n_rows = self.n_rows
+        self.raw.n_cols = self.n_cols
+        self.raw.nnz = self.nnz
+        self.raw.indptr = _ptr(self.indptr)
+        self.raw.indices = _ptr(self.indices)
+        self.raw.values = _ptr(self.values)
+
+    @property
+    def nnz(self) -> int:
+        return int(self.indices.numel())
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.raw)
+
+    @property
+    def device(self):
+        return self.indptr.device
+
+
+@dataclass
+class Built:
+    A: Csr
+    AT: Csr | None
+    deg: torch.Tensor        # int32 [n_local + n_halo]
+    halo_gid: torch.Tensor   # int32 [n_halo]
+
+    @property
+    def n_local(self) -> int:
+        return self.A.n_rows
+
+    @property
+    def n_halo(self) -> int:
+        return int(self.halo_gid.numel())
+
+
+def csr_build_normalize(src: torch.Tensor, dst: torch.Tensor, n_global: int, lo: int, hi: int,
+                        symmetrize: bool, self_loops: bool, norm: str = "gcn",
+                        deg_global: torch.Tensor | None = None, transpose: bool = True,
+                        max_halo: int | None = None) -> Built:
+    """sag_csr_build_normalize: the normalised CSR of rows [lo, hi), its
+    transpose, degrees and HALO list.  Synchronises the current stream."""
+    dev = src.device
+    src = src.to(torch.int32).contiguous()
+    dst = dst.to(torch.int32).contiguous()
+    n_edges = src.numel()
+    flags = (L.SAG_SYMMETRIZE if symmetrize else 0) | (L.SAG_SELF_LOOPS if self_loops else 0)
+    n_local = hi - lo
+    cap_nnz = (2 if symmetrize else 1) * n_edges + (n_local if self_loops else 0)
+    cap_halo = n_global - n_local if max_halo is None else int(max_halo)
+    lib = L.lib()
+    ws = _ws(lib.sag_csr_build_workspace_bytes(n_edges, n_global, lo, hi, flags), dev)
+    indptr = torch.empty(n_local + 1, dtype=torch.int64, device=dev)
+    indices = torch.empty(max(cap_nnz, 1), dtype=torch.int32, device=dev)
+    values = torch.empty(max(cap_nnz, 1), dtype=torch.float32, device=dev)
+    if transpose:
+        indptr_t = torch.empty(n_local + cap_halo + 1, dtype=torch.int64, device=dev)
+        indices_t = torch.empty(max(cap_nnz, 1), dtype=torch.int32, device=dev)
+        values_t = torch.empty(max(cap_nnz, 1), dtype=torch.float32, device=dev)
+    else:
+        indptr_t = indices_t = values_t = None
+    deg = torch.empty(max(n_local + cap_halo, 1), dtype=torch.int32, device=dev)
+    halo = torch.empty(max(cap_halo, 1), dtype=torch.int32, device=dev)
+    if deg_global is not None:
+        deg_global = deg_global.to(device=dev, dtype=torch.int32).contiguous()
+    nnz, n_halo = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib.sag_csr_build_normalize(
+        _ptr(src), _ptr(dst), n_edges, n_global, lo, hi, flags, _NORM[norm], _ptr(deg_global),
+        cap_nnz, cap_halo, _ptr(indptr), _ptr(indices), _ptr(values), _ptr(indptr_t),
+        _ptr(indices_t), _ptr(values_t), _ptr(deg), _ptr(halo), ctypes.byref(nnz),
+        ctypes.byref(n_halo), _ptr(ws), ws.numel(), _stream(dev))
+    L.check("sag_csr_build_normalize", st)
+    nnz, n_halo = nnz.value, n_halo.value
+    n_ext = n_local + n_halo
+    A = Csr(n_local, n_ext, indptr, indices[:nnz], values[:nnz])
+    AT = None
+    if transpose:
+        AT = Csr(n_ext, n_local, indptr_t[:n_ext + 1], indices_t[:nnz], values_t[:nnz])
+    return Built(A, AT, deg[:n_ext], halo[:n_halo])
+
+
+def csr_schedule(A: Csr, seg_len: int = 1024) -> Csr:
+    """sag_csr_schedule: attach the degree-binned schedule to A (in place).
+    Synchronises the current stream."""
+    lib = L.lib()
+    dev = A.device
+    nb = lib.sag_csr_schedule_bytes(A.n_rows, A.nnz, seg_len)
+    buf = torch.empty(max(int(nb), 16), dtype=torch.uint8, device=dev)
+    ws = _ws(lib.sag_csr_schedule_workspace_bytes(A.n_rows), dev)
+    st = lib.sag_csr_schedule(A.ref, seg_len, _ptr(buf), buf.numel(), _ptr(ws), ws.numel(), _stream(dev))
+    L.check("sag_csr_schedule", st)
+    A.sched = buf
+    return A
+
+
+def csr_info(A: Csr) -> dict:
+    r = A.raw
+    return {"n_short": r.n_short, "n_medium": r.n_medium, "n_long": r.n_long,
+            "n_seg": r.n_seg, "seg_len": r.seg_len}
+
+
+def halo_gather(src: torch.Tensor, rows: torch.Tensor, out: torch.Tensor, row_base: int = 0) -> torch.Tensor:
+    """sag_halo_gather: out[k] = src[rows[k] - row_base] (bitwise)."""
+    rows = rows.to(torch.int32).contiguous()
+    st = L.lib().sag_halo_gather(_ptr(src), _ld(src), _ptr(rows), row_base, rows.numel(), src.shape[1],
+                                 dtype_code(src.dtype), _ptr(out), _ld(out) if out.shape[0] else src.shape[1],
+                                 _stream(src.device))
+    L.check("sag_halo_gather", st)
+    return out
+
+
+def _spmm(name, A: Csr, X, out_dtype=None, Y=None, addend=None):
+    lib = L.lib()
+    d = X.shape[1]
+    yt = out_dtype or X.dtype
+    if Y is None:
+        Y = empty_dense(A.n_rows, d, yt, X.device)
+    n_add = addend.shape[0] if addend is not None else 0
+    ws = _ws(lib.sag_spmm_workspace_bytes(A.ref, d), X.device)
+    st = getattr(lib, name)(A.ref, _ptr(X), _ld(X), dtype_code(X.dtype), d, _ptr(Y), _ld(Y),
+                            dtype_code(Y.dtype), _ptr(addend),
+                            _ld(addend) if addend is not None else 0, n_add,
+                            _ptr(ws), ws.numel(), _stream(X.device))
+    L.check(name, st)
+    return Y
+
+
+def spmm_csr(A: Csr, X, out_dtype=None, Y=None, addend=None):
+    """sag_spmm_csr: Y = A X (+ addend on its first rows)."""
+    return _spmm("sag_spmm_csr", A, X, out_dtype, Y, addend)
+
+
+def spmm_csr_t(AT: Csr, X, out_dtype=None, Y=None, addend=None):
+    """sag_spmm_csr_t: the same product over a transposed CSR."""
+    return _spmm("sag_spmm_csr_t", AT, X, out_dtype, Y, addend)
+
+
+# ---- layers ------------------------------------------------------------------------
+
+@dataclass
+class LayerCtx:
+    """What a layer's forward hands to its backward."""
+    kind: str
+    save: torch.Tensor
+    H_ext: torch.Tensor
+    W: torch.Tensor
+    d_in: int
+    d_out: int
+    relu: bool
+
+
+def _layer_forward(kind, A: Csr, H_ext, W, b, relu, want_pre, Out=None, Y_pre=None, ws=None):
+    lib = L.lib()
+    dt = dtype_code(H_ext.dtype)
+    d_in = H_ext.shape[1]
+    d_out = W.shape[1]
+    dev = H_ext.device
+    W = W.contiguous()
+    if Out is None:
+        Out = empty_dense(A.n_rows, d_out, H_ext.dtype, dev)
+    if want_pre and Y_pre is None:
+        Y_pre = empty_dense(A.n_rows, d_out, H_ext.dtype, dev)
+    if want_pre and _ld(Y_pre) != _ld(Out):
+        raise ValueError("Y_pre and Out must share their leading dimension")
+    save_bytes = getattr(lib, f"sag_{kind}_save_bytes")(A.n_rows, d_in, d_out, dt)
+    save = _ws(save_bytes, dev)
+    nws = getattr(lib, f"sag_{kind}_forward_workspace_bytes")(A.ref, d_in, d_out, dt)
+    if ws is None or ws.numel() < nws:
+        ws = _ws(nws, dev)
+    st = getattr(lib, f"sag_{kind}_layer_forward")(
+        A.ref, _ptr(H_ext), _ld(H_ext), d_in, _ptr(W), _ptr(b), d_out, int(relu), dt,
+        _ptr(Y_pre) if want_pre else None, _ptr(Out), _ld(Out), _ptr(save), save.numel(),
+        _ptr(ws), ws.numel(), _stream(dev))
+    L.check(f"sag_{kind}_layer_forward", st)
+    ctx = LayerCtx(kind, save, H_ext, W, d_in, d_out, bool(relu))
+    return Out, Y_pre, ctx
+
+
+def _layer_backward(ctx: LayerCtx, AT: Csr | None, n_local: int, Y, G_out, want_dH=True,
+                    want_db=True, dH=None, ws=None):
+    lib = L.lib()
+    kind = ctx.kind
+    dt = dtype_code(G_out.dtype)
+    dev = G_out.device
+    w_rows = ctx.W.shape[0]
+    dW = torch.empty((w_rows, ctx.d_out), dtype=torch.float32, device=dev)
+    db = torch.empty(ctx.d_out, dtype=torch.float32, device=dev) if want_db else None
+    if want_dH and dH is None:
+        dH = empty_dense(AT.n_rows, ctx.d_in, G_out.dtype, dev)
+    if not want_dH:
+        dH = None
+    if ctx.relu and _ld(Y) != _ld(G_out):
+        raise ValueError("Y and G_out must share their leading dimension")
+    nws = getattr(lib, f"sag_{kind}_backward_workspace_bytes")(
+        AT.ref if AT is not None else None, n_local, ctx.d_in, ctx.d_out, dt)
+    if ws is None or ws.numel() < nws:
+        ws = _ws(nws, dev)
+    st = getattr(lib, f"sag_{kind}_layer_backward")(
+        AT.ref if AT is not None else None, n_local, _ptr(ctx.H_ext), _ld(ctx.H_ext), ctx.d_in,
+        _ptr(ctx.W), ctx.d_out, int(ctx.relu), _ptr(Y) if ctx.relu else None, _ptr(G_out),
+        _ld(G_out), _ptr(dW), _ptr(db), _ptr(dH), _ld(dH) if dH is not None else 0, dt,
+        _ptr(ctx.save), ctx.save.numel(), _ptr(ws), ws.numel(), _stream(dev))
+    L.check(f"sag_{kind}_layer_backward", st)
+    return dW, db, dH
+
+
+def gcn_layer_forward(A: Csr, H_ext, W, b=None, relu=True, want_pre=False, **kw):
+    """sag_gcn_layer_forward: Out = relu(A H_ext W + b).  Returns (Out, Y_pre, ctx)."""
+    return _layer_forward("gcn", A, H_ext, W, b, relu, want_pre, **kw)
+
+
+def gcn_layer_backward(ctx, AT, n_local, Y, G_out, want_dH=True, want_db=True, **kw):
+    """sag_gcn_layer_backward: returns (dW, db, dH_ext)."""
+    return _layer_backward(ctx, AT, n_local, Y, G_out, want_dH, want_db, **kw)
+
+
+def sage_layer_forward(A: Csr, H_ext, W, b=None, relu=True, want_pre=False, **kw):
+    """sag_sage_layer_forward: Out = relu([H_local | A_mean H_ext] W + b)."""
+    return _layer_forward("sage", A, H_ext, W, b, relu, want_pre, **kw)
+
+
+def sage_layer_backward(ctx, AT, n_local, Y, G_out, want_dH=True, want_db=True, **kw):
+    """sag_sage_layer_backward: returns (dW, db, dH_ext)."""
+    return _layer_backward(ctx, AT, n_local, Y, G_out, want_dH, want_db, **kw)
+
+
+# ---- dense building blocks ------------------------------------------------------------
+
+def gemm(A1, B, A2=None, mask=None, trans_b=False, bias=None, addend=None, relu=False,
+         want_pre=False):
+    """sag_gemm: C = [A1 | A2] B (+ bias) (+ addend), optional ReLU."""
+    lib = L.lib()
+    dt = dtype_code(A1.dtype)
+    M = A1.shape[0]
+    K1 = A1.shape[1]
+    K2 = A2.shape[1] if A2 is not None else 0
+    B = B.contiguous()
+    N = B.shape[0] if trans_b else B.shape[1]
+    C = empty_dense(M, N, A1.dtype, A1.device)
+    pre = empty_dense(M, N, A1.dtype, A1.device) if want_pre else None
+    if pre is not None and _ld(pre) != _ld(C):
+        raise AssertionError
+    ws = _ws(lib.sag_gemm_workspace_bytes(M, K1 + K2, N, dt), A1.device)
+    st = lib.sag_gemm(M, N, _ptr(A1), _ld(A1), K1, _ptr(A2), _ld(A2) if A2 is not None else 0, K2,
+                      _ptr(mask), _ld(mask) if mask is not None else 0, _ptr(B), B.stride(0),
+                      int(trans_b), _ptr(bias), _ptr(addend), _ld(addend) if addend is not None else 0,
+                      int(relu), _ptr(C), _ptr(pre), _ld(C), dt, _ptr(ws), ws.numel(),
+                      _stream(A1.device))
+    L.check("sag_gemm", st)
+    return (C, pre) if want_pre else C
+
+
+def gemm_tn(A1, B, A2=None, mask=None, want_colsum=True):
+    """sag_gemm_tn: C = [A1 | A2]^T (B * 1[mask > 0]) in fp32, and column sums."""
+    lib = L.lib()
+    dt = dtype_code(A1.dtype)
+    M, K1 = A1.shape
+    K2 = A2.shape[1] if A2 is not None else 0
+    N = B.shape[1]
+    C = torch.empty((K1 + K2, N), dtype=torch.float32, device=A1.device)
+    cs = torch.empty(N, dtype=torch.float32, device=A1.device) if want_colsum else None
+    ws = _ws(lib.sag_gemm_tn_workspace_bytes(M, K1 + K2, N, dt), A1.device)
+    st = lib.sag_gemm_tn(M, N, _ptr(A1), _ld(A1), K1, _ptr(A2), _ld(A2) if A2 is not None else 0, K2,
+                         _ptr(B), _ld(B), _ptr(mask), _ld(mask) if mask is not None else 0, _ptr(C),
+                         N, _ptr(cs), dt, _ptr(ws), ws.numel(), _stream(A1.device))
+    L.check("sag_gemm_tn", st)
+    return (C, cs) if want_colsum else C
+
+
+def trace_enable(on: bool = True) -> None:
+    """sag_trace_enable: HIP-event timing of every internal operation."""
+    L.check("sag_trace_enable", L.lib().sag_trace_enable(int(on)))
+
+
+def trace_records(clear: bool = True) -> list:
+    """All trace records as dicts {name, ms, bytes, flops} (synchronises)."""
+    lib = L.lib()
+    out = []
+    buf = ctypes.create_string_buffer(256)
+    ms, nb, nf = ctypes.c_float(), ctypes.c_int64(), ctypes.c_int64()
+    for i in range(lib.sag_trace_count()):
+        L.check("sag_trace_get", lib.sag_trace_get(i, buf, 256, ctypes.byref(ms), ctypes.byref(nb),
+                                                   ctypes.byref(nf)))
+        out.append({"name": buf.value.decode(), "ms": ms.value, "bytes": nb.value, "flops": nf.value})
+    if clear:
+        lib.sag_trace_clear()
+    return out
+
+
+def version() -> str:
+    return L.lib().sag_version().decode()

@@ -1,0 +1,102 @@
+"""The C-ABI library loads without a GPU, exports every function that
+include/sag.h declares, and rejects bad arguments on the host before any
+launch (no GPU is touched by these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sag.h")
+
+sag = pytest.importorskip("sparse_aggregation_gemm_amd")
+L = sag._lib
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sag_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["sag_csr_build_normalize", "sag_halo_gather", "sag_spmm_csr", "sag_spmm_csr_t",
+              "sag_gcn_layer_forward", "sag_gcn_layer_backward", "sag_sage_layer_forward",
+              "sag_sage_layer_backward"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_declares_every_export():
+    assert set(declared_functions()) == set(L.SIGNATURES)
+
+
+def test_status_strings():
+    lib = L.lib()
+    assert lib.sag_status_string(0) == b"ok"
+    assert lib.sag_status_string(-4) == b"edge id out of range"
+    assert b"gfx950" in lib.sag_version()
+
+
+def test_host_side_validation():
+    lib = L.lib()
+    # bad dtype, negative sizes, null pointers: rejected before any launch
+    assert lib.sag_halo_gather(None, 8, None, 0, 4, 8, 7, None, 8, None) == L.SAG_E_INVALID
+    assert lib.sag_halo_gather(None, 8, None, 0, -1, 8, 0, None, 8, None) == L.SAG_E_INVALID
+    assert lib.sag_halo_gather(None, 8, None, 0, 4, 8, 0, None, 8, None) == L.SAG_E_INVALID
+    # misaligned leading dimension (fp32, ld 6 -> 24 bytes)
+    fake = ctypes.c_void_p(4096)
+    rows = ctypes.c_void_p(8192)
+    assert lib.sag_halo_gather(fake, 6, rows, 0, 4, 5, 0, fake, 8, None) == L.SAG_E_ALIGN
+    assert lib.sag_halo_gather(fake, 4, rows, 0, 4, 5, 0, fake, 8, None) == L.SAG_E_INVALID  # ld < d
+    assert b"ld" in lib.sag_last_error()
+    assert lib.sag_spmm_csr(None, None, 0, 0, 4, None, 4, 0, None, 0, 0, None, 0, None) == L.SAG_E_INVALID
+    A = L.SagCsr()
+    A.n_rows, A.n_cols, A.nnz = 10, 10, 5
+    assert lib.sag_spmm_csr(ctypes.byref(A), fake, 4, 0, 4, fake, 4, 0, None, 0, 0, None, 0, None) == L.SAG_E_INVALID
+    nnz, nh = ctypes.c_int64(), ctypes.c_int64()
+    # lo > hi
+    st = lib.sag_csr_build_normalize(None, None, 0, 10, 5, 3, 0, 0, None, 0, 0, fake, None, None,
+                                     None, None, None, None, None, ctypes.byref(nnz), ctypes.byref(nh),
+                                     None, 0, None)
+    assert st == L.SAG_E_INVALID
+    # unknown flag
+    st = lib.sag_csr_build_normalize(None, None, 0, 10, 0, 10, 8, 0, None, 0, 0, fake, None, None,
+                                     None, None, None, None, None, ctypes.byref(nnz), ctypes.byref(nh),
+                                     None, 0, None)
+    assert st == L.SAG_E_INVALID
+    # workspace too small
+    st = lib.sag_csr_build_normalize(None, None, 0, 10, 0, 10, 2, 0, None, 10, 0, fake, fake, fake,
+                                     None, None, None, None, None, ctypes.byref(nnz), ctypes.byref(nh),
+                                     fake, 16, None)
+    assert st == L.SAG_E_WORKSPACE
+    # bad seg_len for the schedule
+    assert lib.sag_csr_schedule(ctypes.byref(A), 100, fake, 1 << 20, fake, 1 << 20, None) == L.SAG_E_INVALID
+    # layers: width zero, bad dtype
+    assert lib.sag_gcn_layer_forward(ctypes.byref(A), fake, 4, 0, fake, None, 4, 1, 0, None, fake, 4,
+                                     None, 0, fake, 1 << 20, None) == L.SAG_E_INVALID
+    assert lib.sag_sage_layer_forward(ctypes.byref(A), fake, 4, 4, fake, None, 4, 1, 9, None, fake, 4,
+                                      None, 0, fake, 1 << 20, None) == L.SAG_E_INVALID
+    assert lib.sag_gemm(4, 4, fake, 4, 4, None, 0, 0, None, 0, fake, 4, 0, None, None, 0, 0, fake, None,
+                        4, 3, fake, 1 << 20, None) == L.SAG_E_INVALID
+
+
+def test_workspace_queries_are_host_only():
+    lib = L.lib()
+    assert lib.sag_csr_build_workspace_bytes(1000, 100, 0, 100, 3) > 16 * 1000
+    assert lib.sag_csr_build_workspace_bytes(10, 5, 3, 2, 0) == 0
+    assert lib.sag_csr_schedule_bytes(100, 1000, 64) >= 1600
+    A = L.SagCsr()
+    A.n_rows, A.n_cols, A.nnz = 100, 100, 1000
+    assert lib.sag_spmm_workspace_bytes(ctypes.byref(A), 64) == 0   # no long rows without a schedule
+    assert lib.sag_gcn_save_bytes(100, 16, 64, 0) == 100 * 16 * 4   # aggregate first: Z is saved
+    assert lib.sag_gcn_save_bytes(100, 64, 16, 0) == 0              # transform first: nothing
+    assert lib.sag_sage_save_bytes(100, 100, 256, 1) == 100 * 104 * 2
+    assert lib.sag_gemm_tn_workspace_bytes(10000, 512, 256, 1) > 0

@@ -1,0 +1,108 @@
+"""GPU MFMA products against float64 matrix products on the same stored
+inputs (the oracle's dense step is a library matmul in float64)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+
+pytestmark = pytest.mark.gpu
+
+sag = pytest.importorskip("sparse_aggregation_gemm_amd")
+from gpu_util import DEV, f64, say, to_dev, to_dev_dense, tol  # noqa: E402
+
+
+def _mat(g, shape, dt, integers=False):
+    x = g.integers(-4, 5, shape).astype(np.float32) if integers else g.standard_normal(shape).astype(np.float32)
+    stored = gen.f32_to_bf16_bits(x) if dt == "bf16" else x
+    return stored, to_dev_dense(stored, dt)
+
+
+def _err(got, ref, den):
+    return float(np.max(np.abs(got - ref) / (den + 1e-30))) if ref.size else 0.0
+
+
+SHAPES = [(1, 1, 1), (5, 3, 7), (130, 64, 16), (257, 100, 256), (1000, 200, 47), (333, 512, 48),
+          (700, 128, 602), (4099, 602, 128), (129, 41, 300)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,K,N", SHAPES)
+def test_gemm_nn(dt, M, K, N):
+    g = np.random.default_rng(M * 7 + K * 3 + N)
+    As, A = _mat(g, (M, K), dt)
+    Ws, W = _mat(g, (K, N), dt)
+    W = W.contiguous()
+    b = g.uniform(-0.1, 0.1, N).astype(np.float32)
+    say(f"gemm nn dt={dt} M={M} K={K} N={N}")
+    C, pre = sag.gemm(A, W, bias=to_dev(b), relu=True, want_pre=True)
+    A64, W64 = f64(A), f64(W)
+    ref = A64 @ W64 + b
+    den = np.abs(A64) @ np.abs(W64) + np.abs(b)
+    assert _err(f64(pre), ref, den) <= tol(dt)
+    assert _err(f64(C), np.maximum(ref, 0), den) <= tol(dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_two_blocks_mask_addend_transposed(dt):
+    g = np.random.default_rng(3)
+    M, K1, K2, N = 517, 100, 100, 256
+    _, A1 = _mat(g, (M, K1), dt)
+    _, A2 = _mat(g, (M, K2), dt)
+    _, Mk = _mat(g, (M, K1), dt)
+    _, Bt = _mat(g, (N, K1 + K2), dt)          # B given transposed
+    Bt = Bt.contiguous()
+    _, add = _mat(g, (M, N), dt)
+    say(f"gemm two blocks dt={dt}")
+    C = sag.gemm(A1, Bt, A2=A2, mask=Mk, trans_b=True, addend=add)
+    A64 = np.concatenate([f64(A1) * (f64(Mk) > 0), f64(A2)], 1)
+    B64 = f64(Bt).T
+    ref = A64 @ B64 + f64(add)
+    den = np.abs(A64) @ np.abs(B64) + np.abs(f64(add))
+    assert _err(f64(C), ref, den) <= tol(dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_gemm_exact_integers(dt):
+    g = np.random.default_rng(4)
+    _, A = _mat(g, (300, 96), dt, integers=True)
+    _, W = _mat(g, (96, 80), dt, integers=True)
+    W = W.contiguous()
+    say(f"gemm exact dt={dt}")
+    C = sag.gemm(A, W)
+    assert np.array_equal(f64(C), f64(A) @ f64(W))
+
+
+TN_SHAPES = [(1, 1, 1), (33, 17, 5), (1000, 100, 256), (5000, 256, 47), (20000, 128, 128),
+             (70000, 512, 48), (3, 602, 128)]
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M,K,N", TN_SHAPES)
+def test_gemm_tn(dt, M, K, N):
+    g = np.random.default_rng(M + K + N)
+    _, A = _mat(g, (M, K), dt)
+    _, B = _mat(g, (M, N), dt)
+    _, Mk = _mat(g, (M, N), dt)
+    say(f"gemm tn dt={dt} M={M} K={K} N={N}")
+    C, cs = sag.gemm_tn(A, B, mask=Mk)
+    Bm = f64(B) * (f64(Mk) > 0)
+    A64 = f64(A)
+    ref = A64.T @ Bm
+    den = np.abs(A64).T @ np.abs(Bm)
+    assert _err(f64(C), ref, den) <= 1e-5   # inputs are exact values; only fp32 sums round
+    assert _err(f64(cs), Bm.sum(0), np.abs(Bm).sum(0)) <= 1e-5
+
+
+def test_gemm_tn_two_blocks():
+    g = np.random.default_rng(8)
+    M, K1, K2, N = 3001, 100, 100, 256
+    _, A1 = _mat(g, (M, K1), "bf16")
+    _, A2 = _mat(g, (M, K2), "bf16")
+    _, B = _mat(g, (M, N), "bf16")
+    say("gemm tn two blocks")
+    C, cs = sag.gemm_tn(A1, B, A2=A2)
+    A64 = np.concatenate([f64(A1), f64(A2)], 1)
+    ref = A64.T @ f64(B)
+    den = np.abs(A64).T @ np.abs(f64(B))
+    assert _err(f64(C), ref, den) <= 1e-5

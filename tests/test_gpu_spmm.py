@@ -1,0 +1,208 @@
+"""GPU SpMM and halo gather against the oracle.
+
+Gather: bit-exact.  SpMM: error relative to the magnitude of the summed
+terms (the same product on absolute values) within 1e-5 for fp32 and 2e-2
+for bf16 inputs; bit-exact where every partial sum is exactly representable
+(small-integer features on an 8-regular graph)."""
+import numpy as np
+import pytest
+import torch
+
+import gen
+from oracle import csr as ocsr, layers as olay, native
+
+pytestmark = pytest.mark.gpu
+
+sag = pytest.importorskip("sparse_aggregation_gemm_amd")
+from gpu_util import DEV, bits16, f64, say, to_dev, to_dev_dense, tol  # noqa: E402
+
+
+# ---- halo gather -------------------------------------------------------------
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [1, 3, 8, 41, 100, 128, 602])
+def test_gather_bit_exact(dt, d):
+    g = np.random.default_rng(d)
+    n_src, n = 3000, 1777
+    x = gen.normal_f32((n_src, d), g)
+    xs = gen.f32_to_bf16_bits(x) if dt == "bf16" else x
+    rows = g.integers(0, n_src, n).astype(np.int32)
+    say(f"gather dt={dt} d={d}")
+    src = to_dev_dense(xs, dt)
+    out = sag.empty_dense(n, d, src.dtype, DEV, fill=0)
+    sag.halo_gather(src, to_dev(rows), out)
+    ref = ocsr.gather(xs, rows)
+    if dt == "bf16":
+        assert np.array_equal(bits16(out), ref)
+    else:
+        assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+def test_gather_into_layer_input_keeps_padding():
+    """Rows land after the local rows of H_ext; padding columns untouched."""
+    d = 100
+    g = np.random.default_rng(1)
+    stale = gen.f32_to_bf16_bits(gen.normal_f32((500, d), g))
+    rows = g.integers(0, 500, 64).astype(np.int32)
+    src = to_dev_dense(stale, "bf16")
+    H = torch.full((128, sag.padded_ld(d, torch.bfloat16)), 7.0, dtype=torch.bfloat16, device=DEV)
+    say("gather into H_ext tail")
+    sag.halo_gather(src, to_dev(rows), H[64:, :d])
+    Hh = H.float().cpu().numpy()
+    assert np.all(Hh[:64] == 7.0) and np.all(Hh[64:, d:] == 7.0)
+    assert np.array_equal(bits16(H[64:, :d]), stale[rows])
+
+
+# ---- SpMM --------------------------------------------------------------------------
+
+def _graph(cfg, scale):
+    w = gen.make_config(cfg, scale)
+    src, dst = w.edges
+    return w, src, dst
+
+
+def _check_spmm(A_gpu, A_or, X, dt, out_dt=None, label="", seg_len=None):
+    out_dt = out_dt or dt
+    Xd = to_dev_dense(X if dt == "f32" else gen.f32_to_bf16_bits(X), dt)
+    X64 = f64(Xd)
+    tdt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    say(f"spmm {label} dt={dt}->{out_dt} d={X.shape[1]} seg={seg_len}")
+    Y = sag.spmm_csr(A_gpu, Xd, out_dtype=tdt)
+    ref = native.spmm(A_or.indptr, A_or.indices, A_or.values, X64)
+    den = native.spmm(A_or.indptr, A_or.indices, A_or.values, np.abs(X64), abs_mode=True)
+    err = np.max(np.abs(f64(Y) - ref) / (den + 1e-30)) if ref.size else 0.0
+    bound = tol(dt) if out_dt == "f32" or dt == "f32" else tol("bf16")
+    if dt == "bf16" and out_dt == "f32":
+        bound = 1e-5   # bf16 inputs are exact; only fp32 accumulation rounds
+    assert err <= bound, f"{label}: err {err:.3e} > {bound}"
+    return Y
+
+
+@pytest.mark.parametrize("sched", [None, 64, 1024])
+@pytest.mark.parametrize("dt,out_dt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
+@pytest.mark.parametrize("d", [1, 5, 16, 41, 100, 128, 256, 602])
+def test_spmm_power_law(sched, dt, out_dt, d):
+    if dt == "bf16" and d == 602:
+        d = 1000   # the widest bf16 rows: four vectors per lane
+    w, src, dst = _graph(2, 0.004)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, 0, w.n_global, True, True, "gcn")
+    if sched:
+        sag.csr_schedule(gb.A, sched)
+    ob = ocsr.build(src, dst, w.n_global, 0, w.n_global, True, True, "gcn")
+    X = gen.normal_f32((ob.A.n_cols, d), np.random.default_rng(d))
+    _check_spmm(gb.A, ob.A, X, dt, out_dt, "power-law", sched)
+
+
+@pytest.mark.parametrize("sched", [None, 64])
+def test_spmm_partition_with_halo(sched):
+    """DIGEST split: rows of one range, columns [local | halo]."""
+    w, src, dst = _graph(3, 1 / 64)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, w.lo, w.hi, True, False, "mean")
+    ob = ocsr.build(src, dst, w.n_global, w.lo, w.hi, True, False, "mean")
+    assert ob.n_halo > 0
+    if sched:
+        sag.csr_schedule(gb.A, sched)
+        sag.csr_schedule(gb.AT, sched)
+    X = gen.normal_f32((ob.A.n_cols, 128), np.random.default_rng(3))
+    _check_spmm(gb.A, ob.A, X, "f32", label="partition A")
+    X2 = gen.normal_f32((ob.AT.n_cols, 128), np.random.default_rng(4))
+    _check_spmm(gb.AT, ob.AT, X2, "f32", label="partition AT")
+
+
+@pytest.mark.parametrize("seg_len", [64, 128])
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_spmm_exact_small_integers(seg_len, dt):
+    """8-regular graph + I would need 7 neighbours; a random 7-regular graph
+    plus self-loops has entries 1/8 (exact), and integer features in
+    [-8, 8] keep every partial sum exact: bit-exact in any order."""
+    n, k = 4096, 7
+    src, dst = gen.random_regular_pairs(n, k, np.random.default_rng(11), swaps=2)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 0, n, True, True, "gcn")
+    sag.csr_schedule(gb.A, seg_len)
+    ob = ocsr.build(src, dst, n, 0, n, True, True, "gcn")
+    assert np.all(ob.A.values == np.float32(0.125))
+    g = np.random.default_rng(12)
+    X = g.integers(-8, 9, (n, 72)).astype(np.float32)
+    Xd = to_dev_dense(X if dt == "f32" else gen.f32_to_bf16_bits(X), dt)
+    say(f"spmm exact dt={dt}")
+    Y = sag.spmm_csr(gb.A, Xd, out_dtype=torch.float32)
+    ref = native.spmm(ob.A.indptr, ob.A.indices, ob.A.values, X.astype(np.float64))
+    assert np.array_equal(f64(Y), ref)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_spmm_long_rows_exact(dt):
+    """Rows far longer than a segment (three star centres, values 1) with
+    integer features: bit-exact after the segment sums are added."""
+    n = 20000
+    hubs = [0, 1, 2]
+    src = np.concatenate([np.arange(3, n, dtype=np.int32)] * 3)
+    dst = np.repeat(np.array(hubs, np.int32), n - 3)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 0, n, False, True, "none")
+    sag.csr_schedule(gb.A, 128)
+    info = sag.csr_info(gb.A)
+    assert info["n_long"] == 3
+    ob = ocsr.build(src, dst, n, 0, n, False, True, "none")
+    X = np.random.default_rng(5).integers(-4, 5, (n, 40)).astype(np.float32)
+    Xd = to_dev_dense(X if dt == "f32" else gen.f32_to_bf16_bits(X), dt)
+    say(f"spmm long rows dt={dt}")
+    Y = sag.spmm_csr(gb.A, Xd, out_dtype=torch.float32)
+    ref = native.spmm(ob.A.indptr, ob.A.indices, ob.A.values, X.astype(np.float64))
+    assert np.array_equal(f64(Y), ref)
+
+
+def test_spmm_ring_closed_form():
+    """Cycle + I: Fourier modes are eigenvectors with eigenvalue
+    (1 + 2 cos(2 pi f / n)) / 3."""
+    n = 1000
+    src, dst = gen.ring_pairs(n)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 0, n, True, True, "gcn")
+    i = np.arange(n)
+    fs = [0, 1, 7, 250, 499]
+    X = np.stack([np.cos(2 * np.pi * f * i / n) for f in fs], 1).astype(np.float32)
+    say("spmm ring")
+    Y = f64(sag.spmm_csr(gb.A, to_dev_dense(X)))
+    lam = (1 + 2 * np.cos(2 * np.pi * np.array(fs) / n)) / 3
+    assert np.max(np.abs(Y - X.astype(np.float64) * lam)) < 1e-6
+
+
+def test_spmm_addend_and_transpose_adjoint():
+    """<Y, A X> = <A^T Y, X>, and the addend lands on the first rows."""
+    w, src, dst = _graph(4, 0.003)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, 0, w.n_global, True, True, "mean")
+    sag.csr_schedule(gb.A, 256)
+    sag.csr_schedule(gb.AT, 256)
+    g = np.random.default_rng(9)
+    n = gb.A.n_rows
+    X = g.standard_normal((n, 48)).astype(np.float32)
+    Yv = g.standard_normal((n, 48)).astype(np.float32)
+    say("spmm adjoint")
+    AX = f64(sag.spmm_csr(gb.A, to_dev_dense(X)))
+    ATY = f64(sag.spmm_csr_t(gb.AT, to_dev_dense(Yv)))
+    lhs = np.sum(Yv.astype(np.float64) * AX)
+    rhs = np.sum(ATY * X.astype(np.float64))
+    assert abs(lhs - rhs) <= 1e-5 * np.sum(np.abs(Yv) @ np.ones(48))
+    add = g.standard_normal((n // 2, 48)).astype(np.float32)
+    Z = f64(sag.spmm_csr(gb.A, to_dev_dense(X), addend=to_dev_dense(add)))
+    assert np.allclose(Z[: n // 2], AX[: n // 2] + add, rtol=0, atol=1e-5)
+    assert np.array_equal(Z[n // 2:], AX[n // 2:])
+
+
+def test_spmm_deterministic():
+    w, src, dst = _graph(2, 0.004)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, 0, w.n_global, True, True, "gcn")
+    sag.csr_schedule(gb.A, 64)
+    X = to_dev_dense(gen.normal_f32((gb.A.n_cols, 100), np.random.default_rng(0)))
+    say("spmm determinism")
+    a = sag.spmm_csr(gb.A, X)
+    b = sag.spmm_csr(gb.A, X)
+    assert torch.equal(a, b)
+
+
+def test_spmm_empty():
+    e = np.zeros(0, np.int32)
+    gb = sag.csr_build_normalize(to_dev(e), to_dev(e), 10, 0, 10, True, False, "gcn")
+    X = to_dev_dense(np.ones((10, 8), np.float32))
+    say("spmm empty rows")
+    Y = sag.spmm_csr(gb.A, X)
+    assert np.all(f64(Y) == 0.0)
