@@ -480,8 +480,15 @@ __global__ void relu_mask_kernel(int64_t M, int64_t C, int64_t N, const T* __res
     if (n == V) {
         *reinterpret_cast<uint4*>(out + r * ldo + c0) = g;
     } else {
-        const T* gp = reinterpret_cast<const T*>(&g);
-        for (int e = 0; e < n; ++e) out[r * ldo + c0 + e] = gp[e];
+        const uint32_t w[4] = {g.x, g.y, g.z, g.w};
+        for (int e = 0; e < n; ++e) {
+            if constexpr (V == 4) {
+                reinterpret_cast<uint32_t*>(out + r * ldo + c0)[e] = w[e];
+            } else {
+                reinterpret_cast<uint16_t*>(out + r * ldo + c0)[e] =
+                    static_cast<uint16_t>((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
+            }
+        }
     }
 }
 
@@ -513,20 +520,20 @@ struct TnPlan {
     int64_t n_ktile, n_ntile, n_chunks, rows_per_chunk, ldp_k, ldp_n;
 };
 
+// The chunk count depends on M only (so workspace sizes grow with K and N):
+// chunks of at least 256 rows, at most 512 chunks.
 TnPlan tn_plan(int64_t M, int64_t Kv, int64_t N, sag_dtype dt) {
     TnPlan p;
     p.bnt = N <= 64 ? 64 : 128;
     p.n_ktile = cdiv(Kv > 0 ? Kv : 1, kBKT);
     p.n_ntile = cdiv(N > 0 ? N : 1, p.bnt);
     const int64_t ms = dt == SAG_BF16 ? 32 : 16;
-    const int64_t tiles = p.n_ktile * p.n_ntile;
-    int64_t want = cdiv(2048, tiles);
-    // bounded chunk length keeps the fp32 sequential sums short
-    const int64_t max_rows = 4096;
-    if (cdiv(M, want) > max_rows) want = cdiv(M, max_rows);
-    int64_t rpc = round_up(cdiv(M > 0 ? M : 1, want), ms);
+    const int64_t m = M > 0 ? M : 1;
+    int64_t want = cdiv(m, 256);
+    if (want > 512) want = 512;
+    const int64_t rpc = round_up(cdiv(m, want), ms);
     p.rows_per_chunk = rpc;
-    p.n_chunks = cdiv(M > 0 ? M : 1, rpc);
+    p.n_chunks = cdiv(m, rpc);
     p.ldp_k = p.n_ktile * kBKT;
     p.ldp_n = p.n_ntile * p.bnt;
     return p;

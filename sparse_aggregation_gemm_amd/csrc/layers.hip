@@ -19,6 +19,8 @@
 // [P | T] = H [W_self | W_neigh] in one product and adds P in the SpMM's
 // epilogue; the backward takes dW_self = H_local^T G_Y, dW_neigh = H^T S and
 // dH = [G_Y | S] [W_self ; W_neigh]^T.
+#include <algorithm>
+
 #include "ops.h"
 
 namespace sag {
@@ -62,7 +64,8 @@ sag_status check_layer_common(const char* who, const sag_csr* A, const void* H, 
     const std::string w(who);
     if (dt != SAG_F32 && dt != SAG_BF16) return fail(SAG_E_INVALID, w + ": bad dtype");
     if (d_in <= 0 || d_out <= 0) return fail(SAG_E_INVALID, w + ": widths must be positive");
-    if (d_in > (dt == SAG_BF16 ? 1024 : 512) || d_out > (dt == SAG_BF16 ? 1024 : 512))
+    // the SpMM runs at min(d_in, d_out) and supports 256 vectors of 16 bytes
+    if (std::min(d_in, d_out) > (dt == SAG_BF16 ? 2048 : 1024))
         return fail(SAG_E_UNSUPPORTED, w + ": width too large");
     SAG_TRY(check_csr(who, A));
     SAG_TRY(check_dense("layer H_ext", H, A->n_cols, d_in, ldh, dt));
@@ -74,7 +77,7 @@ sag_status check_layer_common(const char* who, const sag_csr* A, const void* H, 
 
 LayerWs gcn_fwd_ws(const sag_csr& A, int64_t d_in, int64_t d_out, sag_dtype dt, void* ws, size_t bytes) {
     const size_t bp = packed_b_bytes(d_in, 0, d_out, dt);
-    if (aggregate_first(d_in, d_out)) return carve(ws, bytes, bp, 0, 0, 0, 0);
+    if (aggregate_first(d_in, d_out)) return carve(ws, bytes, bp, 0, 0, spmm_ws_bytes(A, d_in), 0);
     return carve(ws, bytes, bp, dense_bytes(A.n_cols, d_out, dt), 0, spmm_ws_bytes(A, d_out), 0);
 }
 
@@ -98,7 +101,8 @@ LayerWs gcn_bwd_ws(const sag_csr* AT, int64_t n_local, int64_t d_in, int64_t d_o
 // ---- SAGE ---------------------------------------------------------------------------
 
 LayerWs sage_fwd_ws(const sag_csr& A, int64_t d_in, int64_t d_out, sag_dtype dt, void* ws, size_t bytes) {
-    if (aggregate_first(d_in, d_out)) return carve(ws, bytes, packed_b_bytes(d_in, d_in, d_out, dt), 0, 0, 0, 0);
+    if (aggregate_first(d_in, d_out))
+        return carve(ws, bytes, packed_b_bytes(d_in, d_in, d_out, dt), 0, 0, spmm_ws_bytes(A, d_in), 0);
     const int64_t np = ldv(d_out, dt);
     // t1 = [P | T], [n_ext, np + d_out]
     return carve(ws, bytes, packed_b_bytes(d_in, 0, np + d_out, dt), dense_bytes(A.n_cols, np + d_out, dt), 0,
@@ -168,7 +172,7 @@ extern "C" sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext,
     e.pre = Y_pre;
     if (aggregate_first(d_in, d_out)) {
         const int64_t ldz = ldv(d_in, dt);
-        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldz, dt, Epilogue{}, nullptr, 0, s));
+        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldz, dt, Epilogue{}, w.spmm, w.spmm_bytes, s));
         GemmA a;
         a.a1 = save; a.lda1 = ldz; a.k1 = d_in; a.m1 = n_l;
         return gemm_run(n_l, d_out, a, w.Bp, dt, Out, ldo, e, s);
@@ -312,7 +316,7 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
         nl.n0 = nl.nsplit = d_out;
         SAG_TRY(pack_b(src, d_in, d_in, nl, dt, w.Bp, s));
         const int64_t ldm = ldv(d_in, dt);
-        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldm, dt, Epilogue{}, nullptr, 0, s));
+        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldm, dt, Epilogue{}, w.spmm, w.spmm_bytes, s));
         GemmA a;
         a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = n_l;
         a.a2 = save; a.lda2 = ldm; a.k2 = d_in;
