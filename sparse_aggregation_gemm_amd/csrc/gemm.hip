@@ -15,6 +15,8 @@
 // k-contiguous array, so the main loops need no bounds checks on it.
 // Workgroups are renumbered so that the tiles sharing rows of A run on the
 // same XCD (one L2 each on MI355X).
+#include <type_traits>
+
 #include "ops.h"
 #include "trace.h"
 
@@ -22,15 +24,34 @@ namespace sag {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+// Calls f(std::integral_constant<int, I>) for I in [B, E): register arrays
+// indexed by I stay in registers however large the body is.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kKPad = 32;    // K of a packed B is padded to this
+// K of a packed B is padded to a multiple of 8 MFMA k-steps (the prefetch
+// depth of the NN kernel): 128 for bf16, 64 for fp32.
 constexpr int kNPad = 256;   // N of a packed B is padded to this
 
 inline int64_t kp(int64_t k, sag_dtype dt) { return round_up(k, vec_elems(dt)); }
-inline int64_t k_total(int64_t k1, int64_t k2, sag_dtype dt) { return round_up(kp(k1, dt) + kp(k2, dt), kKPad); }
+inline int64_t k_total(int64_t k1, int64_t k2, sag_dtype dt) {
+    return round_up(kp(k1, dt) + kp(k2, dt), dt == SAG_BF16 ? 128 : 64);
+}
 
 // ---- element tricks on 16-byte vectors ---------------------------------------------
+
+// Element-wise select of 16-byte vectors (a ?: on the vector class can be
+// lowered through private memory).
+__device__ __forceinline__ uint4 sel(bool c, const uint4& x, const uint4& y) {
+    return make_uint4(c ? x.x : y.x, c ? x.y : y.y, c ? x.z : y.z, c ? x.w : y.w);
+}
 
 // Zeroes elements >= n of a vector of T.
 template <class T>
@@ -71,8 +92,12 @@ __device__ __forceinline__ uint4 apply_mask(uint4 a, uint4 m) {
     return make_uint4(aw[0], aw[1], aw[2], aw[3]);
 }
 
-// Loads the 16-byte vector of virtual column k0 (a multiple of V) of row r
-// of the block operand [A1 | A2]; zero outside the operand.
+// The block operand [A1 | A2] seen through "virtual" columns: A1 occupies
+// columns [0, k1p), A2 [k1p, k1p + k2p) (each padded to whole 16-byte
+// vectors); anything else reads as zero.  Loading is split in two so that
+// loads can be issued far ahead of their use without waiting: addr() gives
+// an address that is always valid (out-of-range requests point at `safe`),
+// and fix() zeroes what lies outside the operand once the data is used.
 template <class T>
 struct AOperand {
     const T* a1;
@@ -82,33 +107,68 @@ struct AOperand {
     const T* mask;
     int64_t ldmask;
     int64_t M;
+    const T* safe;   // any valid 16-byte aligned address
 
-    __device__ __forceinline__ uint4 load(int64_t r, int64_t k0) const {
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (r >= M) return v;
-        if (k0 < k1p) {
-            if (r < m1) {
-                v = *reinterpret_cast<const uint4*>(a1 + r * lda1 + k0);
-                v = keep_first<T>(v, static_cast<int>(k1 - k0));
-                if (mask) v = apply_mask<T>(v, *reinterpret_cast<const uint4*>(mask + r * ldmask + k0));
+    __device__ __forceinline__ const uint4* addr(int64_t r, int64_t k0) const {
+        const T* p = safe;
+        if (r < M) {
+            if (k0 < k1p) {
+                if (r < m1) p = a1 + r * lda1 + k0;
+            } else if (k0 < k1p + k2p) {
+                p = a2 + r * lda2 + (k0 - k1p);
             }
-        } else if (k0 < k1p + k2p) {
-            const int64_t kk = k0 - k1p;
-            v = *reinterpret_cast<const uint4*>(a2 + r * lda2 + kk);
-            v = keep_first<T>(v, static_cast<int>(k2 - kk));
         }
-        return v;
+        return reinterpret_cast<const uint4*>(p);
+    }
+    __device__ __forceinline__ const uint4* mask_addr(int64_t r, int64_t k0) const {
+        const T* p = safe;
+        if (mask && r < M && r < m1 && k0 < k1p) p = mask + r * ldmask + k0;
+        return reinterpret_cast<const uint4*>(p);
+    }
+    __device__ __forceinline__ uint4 fix(uint4 v, int64_t r, int64_t k0) const {
+        const bool in1 = k0 < k1p, in2 = !in1 && k0 < k1p + k2p;
+        const int n = in1 ? static_cast<int>(k1 - k0) : static_cast<int>(k2 - (k0 - k1p));
+        const bool ok = r < M && ((in1 && r < m1) || in2);
+        return sel(ok, keep_first<T>(v, n), make_uint4(0, 0, 0, 0));
+    }
+    __device__ __forceinline__ uint4 fix_masked(uint4 v, uint4 m, int64_t r, int64_t k0) const {
+        v = fix(v, r, k0);
+        return sel(mask && k0 < k1p, apply_mask<T>(v, m), v);
+    }
+    // ---- streaming access used by the NN kernel ----
+    // Row pointers of row r (clamped to a valid row: rows >= M only feed
+    // outputs that are never stored).
+    __device__ __forceinline__ void row_ptrs(int64_t r, const T*& p1, const T*& p2) const {
+        const int64_t rc = r < M ? r : M - 1;
+        p1 = a1 ? a1 + (rc < m1 ? rc : m1 - 1) * lda1 : safe;
+        p2 = a2 ? a2 + rc * lda2 : p1;
+    }
+    // Address of the vector at virtual column k0, clamped into the operand.
+    __device__ __forceinline__ const uint4* stream_addr(const T* p1, const T* p2, int64_t k0) const {
+        const int64_t last = k1p + k2p - Vec<T>::N;
+        const int64_t kc = k0 < last ? k0 : last;
+        return reinterpret_cast<const uint4*>(kc < k1p ? p1 + kc : p2 + (kc - k1p));
+    }
+    // True when the k-range [kb, kb + span) holds a column that must read as
+    // zero: the ragged tail of a block or anything past the operand.
+    __device__ __forceinline__ bool needs_fix(int64_t kb, int64_t span) const {
+        return (kb + span > k1 && kb < k1p) || (kb + span > k1p + k2);
+    }
+    // one-shot load (used where the value is needed at once)
+    __device__ __forceinline__ uint4 load(int64_t r, int64_t k0) const {
+        const uint4 v = *addr(r, k0);
+        return mask ? fix_masked(v, *mask_addr(r, k0), r, k0) : fix(v, r, k0);
     }
 };
 
 template <class T>
-AOperand<T> make_aop(const GemmA& A, int64_t M, sag_dtype dt) {
+AOperand<T> make_aop(const GemmA& A, int64_t M, sag_dtype dt, const void* safe) {
     AOperand<T> o;
     o.a1 = static_cast<const T*>(A.a1);
     o.lda1 = A.lda1;
-    o.k1 = A.k1;
+    o.k1 = A.a1 ? A.k1 : 0;
     o.m1 = A.a1 ? (A.m1 > 0 ? A.m1 : M) : 0;
-    o.k1p = kp(A.k1, dt);
+    o.k1p = A.a1 ? kp(A.k1, dt) : 0;
     o.a2 = static_cast<const T*>(A.a2);
     o.lda2 = A.lda2;
     o.k2 = A.a2 ? A.k2 : 0;
@@ -116,6 +176,7 @@ AOperand<T> make_aop(const GemmA& A, int64_t M, sag_dtype dt) {
     o.mask = static_cast<const T*>(A.mask);
     o.ldmask = A.ldmask;
     o.M = M;
+    o.safe = static_cast<const T*>(safe);
     return o;
 }
 
@@ -163,195 +224,329 @@ struct EpiT {
     int relu;
 };
 
+// Stores n <= 4 consecutive values (4 as one vector: 8 bytes of bf16 or 16
+// bytes of fp32; p is aligned for that when n == 4).
+template <class T>
+__device__ __forceinline__ void store4(T* p, const float* y, int n) {
+    if (n == 4) {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t lo = uint32_t(f32_to_bf16(y[0])) | (uint32_t(f32_to_bf16(y[1])) << 16);
+            const uint32_t hi = uint32_t(f32_to_bf16(y[2])) | (uint32_t(f32_to_bf16(y[3])) << 16);
+            *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+        } else {
+            *reinterpret_cast<float4*>(p) = make_float4(y[0], y[1], y[2], y[3]);
+        }
+    } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            if (t < n) p[t] = from_f32<T>(y[t]);
+    }
+}
+
 // ---- NN ------------------------------------------------------------------------------
-constexpr int kBM = 128;
+// C = A B with M huge and K, N small (the layer's transform and input
+// gradient).  A workgroup keeps its BN columns of the packed B (all of K) in
+// LDS for its whole life; each of its wavefronts streams 32-row blocks of A
+// straight from memory into MFMA operands with kDepth 16-byte fragments in
+// flight, so the only HBM traffic is A once and C once.  Persistent: one
+// workgroup per CU walks the 32-row blocks of its N block.
+constexpr int kNnWaves = 8;
+constexpr int kDepth = 8;
 
-template <class T, int BN>
-__global__ __launch_bounds__(256) void gemm_nn(AOperand<T> A, const T* __restrict__ Bp, int64_t Kt,
-                                               int64_t N, int64_t n_nblk, EpiT<T> e) {
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+template <class T> struct StreamMfma;
+// The MFMAs compute transposed blocks, C^T = B^T A^T: B supplies the first
+// operand and A the second, so lane l accumulates row l%32 of a 32x32 block
+// of C and register r holds column 8*(r/4) + 4*(l/32) + r%4 -- four
+// consecutive columns per register quad, stored as one vector.
+// bf16: one A load holds k0..k0+7 (lanes 0-31) or k0+8..k0+15 (lanes 32-63),
+// exactly the operand of one 32x32x16 MFMA.
+template <> struct StreamMfma<uint16_t> {
+    static constexpr int KSTEP = 16;
+    template <int NB>
+    __device__ static __forceinline__ void step(const uint4& a, const uint16_t* Bs, int64_t LP, int ks, int lane,
+                                                f32x16_t (&acc)[NB]) {
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+        const uint16_t* bp = Bs + (lane % 32) * LP + ks * 16 + (lane / 32) * 8;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(bp + j * 32 * LP);
+            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, acc[j], 0, 0, 0);
+        }
+    }
+};
+// fp32: one A load holds k0..k0+3 (lanes 0-31) or k0+4..k0+7 (lanes 32-63);
+// four 32x32x2 MFMAs pair k0+s with k0+4+s, and B is read with the same
+// pairing, so the products sum over k0..k0+7.
+template <> struct StreamMfma<float> {
+    static constexpr int KSTEP = 8;
+    template <int NB>
+    __device__ static __forceinline__ void step(const uint4& a, const float* Bs, int64_t LP, int ks, int lane,
+                                                f32x16_t (&acc)[NB]) {
+        const f32x4_t av = __builtin_bit_cast(f32x4_t, a);
+        const float* bp = Bs + (lane % 32) * LP + ks * 8 + (lane / 32) * 4;
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bp + j * 32 * LP);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[q], av[q], acc[j], 0, 0, 0);
+        }
+    }
+};
+
+template <class T, int BN, bool MASK>
+__global__ __launch_bounds__(kNnWaves * 64) void gemm_nn(AOperand<T> A, const T* __restrict__ Bp, int64_t Kt,
+                                                         int64_t N, int64_t n_nblk, int64_t n_mgroups,
+                                                         int64_t n_mblk, EpiT<T> e) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    T* Bs = reinterpret_cast<T*>(lds_raw);
     constexpr int V = Vec<T>::N;
-    constexpr int BK = 64 / sizeof(T);          // 64 bytes of k per row and tile
-    constexpr int LP = BK + V;                  // LDS row pitch (elements), +16 B
-    constexpr int NB = BN / 64;                 // 32-column blocks per wave
-    constexpr int KI = Mfma<T>::KI;
-    __shared__ __attribute__((aligned(16))) T As[kBM * LP];
-    __shared__ __attribute__((aligned(16))) T Bs[BN * LP];
-
+    constexpr int NB = BN / 32;
+    constexpr int KSTEP = StreamMfma<T>::KSTEP;
+    const int64_t LP = Kt + V;
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
-    const int64_t mb0 = (tile / n_nblk) * kBM;
-    const int64_t nb0 = (tile % n_nblk) * BN;
-    const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-
-    uint4 ra[2], rb[NB];
-    auto load_tile = [&](int64_t kt) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = t + 256 * i;
-            ra[i] = A.load(mb0 + q / 4, kt * BK + (q % 4) * V);
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int q = t + 256 * i;
-            rb[i] = *reinterpret_cast<const uint4*>(Bp + (nb0 + q / 4) * Kt + kt * BK + (q % 4) * V);
-        }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = t + 256 * i;
-            *reinterpret_cast<uint4*>(&As[(q / 4) * LP + (q % 4) * V]) = ra[i];
-        }
-#pragma unroll
-        for (int i = 0; i < NB; ++i) {
-            const int q = t + 256 * i;
-            *reinterpret_cast<uint4*>(&Bs[(q / 4) * LP + (q % 4) * V]) = rb[i];
-        }
-    };
-
-    f32x16_t acc[2][NB];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
+    const int64_t nb = tile % n_nblk, mg = tile / n_nblk;
+    const int64_t n0 = nb * BN;
+    const int64_t kvec = Kt / V;
+    for (int64_t q = threadIdx.x; q < BN * kvec; q += kNnWaves * 64) {
+        const int64_t r = q / kvec, c = (q % kvec) * V;
+        *reinterpret_cast<uint4*>(Bs + r * LP + c) = *reinterpret_cast<const uint4*>(Bp + (n0 + r) * Kt + c);
+    }
+    // the bias of the block's columns sits after B, so the epilogue never
+    // waits on global memory behind the prefetched fragments
+    float* bias_lds = reinterpret_cast<float*>(lds_raw + static_cast<size_t>(BN) * LP * sizeof(T));
+    for (int q = threadIdx.x; q < BN; q += kNnWaves * 64)
+        bias_lds[q] = (e.bias && n0 + q < N) ? e.bias[n0 + q] : 0.f;
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t stride = n_mgroups * kNnWaves;
+    int64_t mb = mg * kNnWaves + wave;
+    if (mb >= n_mblk) return;
+    const int nks = static_cast<int>(Kt / KSTEP);   // a multiple of kDepth
+    const int64_t koff = (lane / 32) * (KSTEP / 2);
+    const int64_t rl = lane % 32;
+    // kDepth raw fragments (and mask fragments) in flight; fixed up at use
+    uint4 buf[kDepth], mbuf[MASK ? kDepth : 1];
+    const T *p1, *p2, *q1, *q2;           // row pointers of this block and the next
+    A.row_ptrs(mb * 32 + rl, p1, p2);
+    const T* mrow = MASK ? A.mask + (mb * 32 + rl < A.M ? mb * 32 + rl : A.M - 1) * A.ldmask : nullptr;
+    const T* mrow_next = mrow;
+    static_for<0, kDepth>([&](auto dc) {
+        constexpr int d = decltype(dc)::value;
+        buf[d] = *A.stream_addr(p1, p2, d * KSTEP + koff);
+        if constexpr (MASK) mbuf[d] = *reinterpret_cast<const uint4*>(mrow + min<int64_t>(d * KSTEP + koff, A.k1p - V));
+    });
+    for (;;) {
+        f32x16_t acc[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    const int64_t nkt = Kt / BK;
-    load_tile(0);
-    store_tile();
-    __syncthreads();
-    for (int64_t kt = 0; kt < nkt; ++kt) {
-        if (kt + 1 < nkt) load_tile(kt + 1);
-#pragma unroll
-        for (int ks = 0; ks < BK; ks += KI) {
-            typename Mfma<T>::frag fa[2], fb[NB];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) fa[i] = Mfma<T>::ld(&As[(wm * 64 + i * 32 + lane % 32) * LP], ks);
-#pragma unroll
-            for (int j = 0; j < NB; ++j) fb[j] = Mfma<T>::ld(&Bs[(wn * (BN / 2) + j * 32 + lane % 32) * LP], ks);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < NB; ++j) acc[i][j] = Mfma<T>::mma(fa[i], fb[j], acc[i][j]);
+            for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+        const int64_t mb_next = mb + stride;
+        A.row_ptrs(mb_next * 32 + rl, q1, q2);
+        if constexpr (MASK) {
+            const int64_t rn = mb_next * 32 + rl;
+            mrow_next = A.mask + (rn < A.M ? rn : A.M - 1) * A.ldmask;
         }
-        __syncthreads();
-        if (kt + 1 < nkt) {
-            store_tile();
-            __syncthreads();
+        // rows of this block at or past m1 read block 1 as zero
+        const bool zero_rows = A.a1 && (mb * 32 + 31 >= A.m1) && (mb * 32 < A.M);
+        for (int ks0 = 0; ks0 < nks; ks0 += kDepth) {
+            static_for<0, kDepth>([&](auto dc) {
+                constexpr int d = decltype(dc)::value;
+                const int ks = ks0 + d;
+                const int64_t k_use = static_cast<int64_t>(ks) * KSTEP + koff;
+                uint4 a = buf[d];
+                if constexpr (MASK) {
+                    // block 1 only; on the boundary step the upper half-wave is in block 2
+                    if (ks * KSTEP < A.k1p) {
+                        a = sel(k_use < A.k1p, apply_mask<T>(a, mbuf[d]), a);
+                    }
+                }
+                if (zero_rows || A.needs_fix(static_cast<int64_t>(ks) * KSTEP, KSTEP))
+                    a = A.fix(a, mb * 32 + rl, k_use);
+                int kn = ks + kDepth;
+                const T *r1 = p1, *r2 = p2, *mr = mrow;
+                if (kn >= nks) {
+                    kn -= nks;
+                    r1 = q1;
+                    r2 = q2;
+                    mr = mrow_next;
+                }
+                const int64_t k_next = static_cast<int64_t>(kn) * KSTEP + koff;
+                buf[d] = *A.stream_addr(r1, r2, k_next);
+                if constexpr (MASK) mbuf[d] = *reinterpret_cast<const uint4*>(mr + min<int64_t>(k_next, A.k1p - V));
+                StreamMfma<T>::template step<NB>(a, Bs, LP, ks, lane, acc);
+            });
         }
-    }
-
-    // epilogue: acc register r of lane l holds row 8*(r/4) + 4*(l/32) + r%4,
-    // column l%32 of its 32x32 block
+        // epilogue: lane l holds row l%32 of the block; register quad q of
+        // column block j holds columns j*32 + 8q + 4(l/32) .. +3
+        const int64_t row = mb * 32 + rl;
+        if (row < A.M) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+            for (int j = 0; j < NB; ++j) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const int64_t col = nb0 + wn * (BN / 2) + j * 32 + lane % 32;
-            if (col >= N) continue;
-            const float bias = e.bias ? e.bias[col] : 0.f;
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t cl = j * 32 + 8 * q + 4 * (lane / 32);
+                    const int64_t col = n0 + cl;
+                    if (col >= N) continue;
+                    const int n = static_cast<int>(N - col < 4 ? N - col : 4);
+                    float y[4];
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t row = mb0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-                if (row >= A.M) continue;
-                float y = acc[i][j][r] + bias;
-                if (e.add && row < e.n_add) y += to_f32(e.add[row * e.ld_add + col]);
-                if (e.pre) e.pre[row * e.ldc + col] = from_f32<T>(y);
-                if (e.relu) y = y < 0.f ? 0.f : y;
-                e.c[row * e.ldc + col] = from_f32<T>(y);
+                    for (int t = 0; t < 4; ++t) y[t] = acc[j][4 * q + t] + bias_lds[cl + t];
+                    if (e.add && row < e.n_add) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+                            if (t < n) y[t] += to_f32(e.add[row * e.ld_add + col + t]);
+                    }
+                    if (e.pre) store4<T>(e.pre + row * e.ldc + col, y, n);
+                    if (e.relu) {
+#pragma unroll
+                        for (int t = 0; t < 4; ++t) y[t] = y[t] < 0.f ? 0.f : y[t];
+                    }
+                    store4<T>(e.c + row * e.ldc + col, y, n);
+                }
             }
         }
+        mb = mb_next;
+        if (mb >= n_mblk) break;
+        p1 = q1;
+        p2 = q2;
+        mrow = mrow_next;
     }
 }
 
 // ---- TN (weight gradient) -----------------------------------------------------------
-// Tile: BKT rows of C (the K dimension) x BNT columns, reduction over a
-// chunk of M rows, MS rows per step.
-constexpr int kBKT = 128;
+// C[k, n] = sum over a chunk of rows m of A[m, k] B[m, n].  Tile: KT rows of C
+// (K up to 512 in one tile) by BNT columns; 8 wavefronts, WK along K by WN
+// along N.  Each step stages MS rows of A and B in LDS; for bf16 they are
+// stored transposed (k-major, m contiguous) because the MFMA reduction runs
+// over m, with each thread writing 4 consecutive m values at once.
+constexpr int kTnThreads = 512;
 
-template <class T, int BNT>
-__global__ __launch_bounds__(256) void gemm_tn(AOperand<T> A, const T* __restrict__ B, int64_t ldb,
-                                               const T* __restrict__ mask, int64_t ldmask, int64_t N,
-                                               int64_t n_ktile, int64_t n_ntile, int64_t rows_per_chunk,
-                                               float* __restrict__ part, int64_t ldp_k, int64_t ldp_n,
-                                               float* __restrict__ part_cs) {
+template <class T, int KT, int BNT>
+__global__ __launch_bounds__(kTnThreads) void gemm_tn(AOperand<T> A, const T* __restrict__ B, int64_t ldb,
+                                                      const T* __restrict__ mask, int64_t ldmask, int64_t N,
+                                                      int64_t n_ktile, int64_t n_ntile, int64_t rows_per_chunk,
+                                                      float* __restrict__ part, int64_t ldp_k, int64_t ldp_n,
+                                                      float* __restrict__ part_cs) {
+    constexpr bool kBf16 = sizeof(T) == 2;
     constexpr int V = Vec<T>::N;
     constexpr int KI = Mfma<T>::KI;
-    constexpr bool kBf16 = sizeof(T) == 2;
-    constexpr int MS = kBf16 ? 32 : 16;               // M rows per step
-    constexpr int NBK = kBKT / 64, NBN = BNT / 64;    // 32-blocks per wave
-    // bf16: LDS transposed [k][m] and [n][m]; fp32: natural [m][k] and [m][n]
-    constexpr int LPA = kBf16 ? MS + 8 : kBKT + 4;
+    constexpr int MS = kBf16 ? 32 : 16;               // rows per step
+    constexpr int WK = KT / 64, WN = 8 / WK;
+    constexpr int TK = KT / WK, TNW = BNT / WN;       // wave tile
+    constexpr int NBK = TK / 32, NBN = TNW / 32;
+    static_assert(TNW >= 32 && TNW % 32 == 0, "wave tile too narrow");
+    constexpr int LPA = kBf16 ? MS + 8 : KT + 4;
     constexpr int LPB = kBf16 ? MS + 8 : BNT + 4;
-    constexpr int SA = kBf16 ? kBKT * LPA : MS * LPA;
+    constexpr int SA = kBf16 ? KT * LPA : MS * LPA;
     constexpr int SB = kBf16 ? BNT * LPB : MS * LPB;
     __shared__ __attribute__((aligned(16))) T As[SA];
     __shared__ __attribute__((aligned(16))) T Bs[SB];
-    constexpr int VA = MS * kBKT / V / 256;           // A vectors per thread per step
-    constexpr int VB = MS * BNT / V / 256;
-    static_assert(VA >= 1 && VB >= 1, "tile too small");
+    constexpr int ITEMS_A = (MS / 4) * (KT / V);      // 4 rows x one vector each
+    constexpr int ITEMS_B = (MS / 4) * (BNT / V);
+    static_assert(ITEMS_A <= kTnThreads && ITEMS_B <= kTnThreads, "too many items");
 
     const int64_t tiles = n_ktile * n_ntile;
     const int64_t chunk = blockIdx.x / tiles;
     const int64_t tt = blockIdx.x % tiles;
-    const int64_t k0 = (tt / n_ntile) * kBKT;
+    const int64_t k0 = (tt / n_ntile) * KT;
     const int64_t n0 = (tt % n_ntile) * BNT;
     const int64_t m_begin = chunk * rows_per_chunk;
     const int64_t m_end = min(A.M, m_begin + rows_per_chunk);
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int wk = wave & 1, wn = wave >> 1;
+    const int wk = wave % WK, wn = wave / WK;
     const bool do_cs = part_cs && k0 == 0;
+    // item of this thread: rows 4*rq .. 4*rq+3 of the step, one vector column
+    const int a_rq = t % (MS / 4), a_cv = t / (MS / 4);
+    const int b_rq = t % (MS / 4), b_cv = t / (MS / 4);
 
-    uint4 ra[VA], rb[VB];
+    // raw loads are issued a step ahead; zeroing and masking happen when the
+    // step is written to LDS
+    uint4 ra[4], rb[4], rm[4];
+    int64_t step_m0 = m_begin;
     auto load_step = [&](int64_t m0) {
+        if (t < ITEMS_A) {
 #pragma unroll
-        for (int i = 0; i < VA; ++i) {
-            const int q = t + 256 * i;
-            const int r = q / (kBKT / V), c = (q % (kBKT / V)) * V;
-            ra[i] = (m0 + r < m_end) ? A.load(m0 + r, k0 + c) : make_uint4(0, 0, 0, 0);
-        }
-#pragma unroll
-        for (int i = 0; i < VB; ++i) {
-            const int q = t + 256 * i;
-            const int r = q / (BNT / V), c = (q % (BNT / V)) * V;
-            const int64_t row = m0 + r, col = n0 + c;
-            uint4 v = make_uint4(0, 0, 0, 0);
-            if (row < m_end && col < N) {
-                v = *reinterpret_cast<const uint4*>(B + row * ldb + col);
-                v = keep_first<T>(v, static_cast<int>(N - col));
-                if (mask) v = apply_mask<T>(v, *reinterpret_cast<const uint4*>(mask + row * ldmask + col));
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + a_rq * 4 + i;
+                ra[i] = *A.addr(row < m_end ? row : A.M, k0 + a_cv * V);
             }
-            rb[i] = v;
+        }
+        if (t < ITEMS_B) {
+            const int64_t col = n0 + b_cv * V;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = m0 + b_rq * 4 + i;
+                const bool ok = row < m_end && col < N;
+                rb[i] = *reinterpret_cast<const uint4*>(ok ? B + row * ldb + col : B);
+                if (mask) rm[i] = *reinterpret_cast<const uint4*>(ok ? mask + row * ldmask + col : mask);
+            }
+        }
+    };
+    auto fix_step = [&]() {
+        if (t < ITEMS_A) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = step_m0 + a_rq * 4 + i;
+                ra[i] = row < m_end ? A.fix(ra[i], row, k0 + a_cv * V) : make_uint4(0, 0, 0, 0);
+            }
+        }
+        if (t < ITEMS_B) {
+            const int64_t col = n0 + b_cv * V;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t row = step_m0 + b_rq * 4 + i;
+                uint4 v = make_uint4(0, 0, 0, 0);
+                if (row < m_end && col < N) {
+                    v = keep_first<T>(rb[i], static_cast<int>(N - col));
+                    if (mask) v = apply_mask<T>(v, rm[i]);
+                }
+                rb[i] = v;
+            }
         }
     };
     auto store_step = [&]() {
+        fix_step();
+        if constexpr (kBf16) {
+            // transpose: element (m, k) goes to As[k][m]; 4 m values per write
+            if (t < ITEMS_A) {
 #pragma unroll
-        for (int i = 0; i < VA; ++i) {
-            const int q = t + 256 * i;
-            const int r = q / (kBKT / V), c = (q % (kBKT / V)) * V;
-            if constexpr (kBf16) {
-                const uint32_t w[4] = {ra[i].x, ra[i].y, ra[i].z, ra[i].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    As[(c + e) * LPA + r] = static_cast<uint16_t>((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
-            } else {
-                *reinterpret_cast<uint4*>(&As[r * LPA + c]) = ra[i];
+                for (int e = 0; e < 8; ++e) {
+                    uint32_t lo = 0, hi = 0;
+                    const uint32_t w0[4] = {ra[0].x, ra[0].y, ra[0].z, ra[0].w};
+                    const uint32_t w1[4] = {ra[1].x, ra[1].y, ra[1].z, ra[1].w};
+                    const uint32_t w2[4] = {ra[2].x, ra[2].y, ra[2].z, ra[2].w};
+                    const uint32_t w3[4] = {ra[3].x, ra[3].y, ra[3].z, ra[3].w};
+                    const int sh = (e & 1) ? 16 : 0;
+                    lo = ((w0[e / 2] >> sh) & 0xffffu) | (((w1[e / 2] >> sh) & 0xffffu) << 16);
+                    hi = ((w2[e / 2] >> sh) & 0xffffu) | (((w3[e / 2] >> sh) & 0xffffu) << 16);
+                    *reinterpret_cast<uint2*>(&As[(a_cv * 8 + e) * LPA + a_rq * 4]) = make_uint2(lo, hi);
+                }
             }
-        }
+            if (t < ITEMS_B) {
 #pragma unroll
-        for (int i = 0; i < VB; ++i) {
-            const int q = t + 256 * i;
-            const int r = q / (BNT / V), c = (q % (BNT / V)) * V;
-            if constexpr (kBf16) {
-                const uint32_t w[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t w0[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
+                    const uint32_t w1[4] = {rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+                    const uint32_t w2[4] = {rb[2].x, rb[2].y, rb[2].z, rb[2].w};
+                    const uint32_t w3[4] = {rb[3].x, rb[3].y, rb[3].z, rb[3].w};
+                    const int sh = (e & 1) ? 16 : 0;
+                    const uint32_t lo = ((w0[e / 2] >> sh) & 0xffffu) | (((w1[e / 2] >> sh) & 0xffffu) << 16);
+                    const uint32_t hi = ((w2[e / 2] >> sh) & 0xffffu) | (((w3[e / 2] >> sh) & 0xffffu) << 16);
+                    *reinterpret_cast<uint2*>(&Bs[(b_cv * 8 + e) * LPB + b_rq * 4]) = make_uint2(lo, hi);
+                }
+            }
+        } else {
+            if (t < ITEMS_A) {
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    Bs[(c + e) * LPB + r] = static_cast<uint16_t>((e & 1) ? (w[e / 2] >> 16) : (w[e / 2] & 0xffffu));
-            } else {
-                *reinterpret_cast<uint4*>(&Bs[r * LPB + c]) = rb[i];
+                for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[(a_rq * 4 + i) * LPA + a_cv * V]) = ra[i];
+            }
+            if (t < ITEMS_B) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Bs[(b_rq * 4 + i) * LPB + b_cv * V]) = rb[i];
             }
         }
     };
@@ -372,10 +567,13 @@ __global__ __launch_bounds__(256) void gemm_tn(AOperand<T> A, const T* __restric
         for (int64_t m0 = m_begin; m0 < m_end; m0 += MS) {
             const bool more = m0 + MS < m_end;
             if (more) load_step(m0 + MS);
+            step_m0 = m0 + MS;
             if (do_cs && t < BNT) {
                 if constexpr (kBf16) {
+#pragma unroll
                     for (int r = 0; r < MS; ++r) cs += bf16_to_f32(Bs[t * LPB + r]);
                 } else {
+#pragma unroll
                     for (int r = 0; r < MS; ++r) cs += Bs[r * LPB + t];
                 }
             }
@@ -385,18 +583,18 @@ __global__ __launch_bounds__(256) void gemm_tn(AOperand<T> A, const T* __restric
                 if constexpr (kBf16) {
 #pragma unroll
                     for (int i = 0; i < NBK; ++i)
-                        fa[i] = Mfma<T>::ld(&As[(wk * (kBKT / 2) + i * 32 + lane % 32) * LPA], ks);
+                        fa[i] = Mfma<T>::ld(&As[(wk * TK + i * 32 + lane % 32) * LPA], ks);
 #pragma unroll
                     for (int j = 0; j < NBN; ++j)
-                        fb[j] = Mfma<T>::ld(&Bs[(wn * (BNT / 2) + j * 32 + lane % 32) * LPB], ks);
+                        fb[j] = Mfma<T>::ld(&Bs[(wn * TNW + j * 32 + lane % 32) * LPB], ks);
                 } else {
                     const int mr = ks + lane / 32;
 #pragma unroll
                     for (int i = 0; i < NBK; ++i)
-                        fa[i] = reinterpret_cast<const float*>(As)[mr * LPA + wk * (kBKT / 2) + i * 32 + lane % 32];
+                        fa[i] = reinterpret_cast<const float*>(As)[mr * LPA + wk * TK + i * 32 + lane % 32];
 #pragma unroll
                     for (int j = 0; j < NBN; ++j)
-                        fb[j] = reinterpret_cast<const float*>(Bs)[mr * LPB + wn * (BNT / 2) + j * 32 + lane % 32];
+                        fb[j] = reinterpret_cast<const float*>(Bs)[mr * LPB + wn * TNW + j * 32 + lane % 32];
                 }
 #pragma unroll
                 for (int i = 0; i < NBK; ++i)
@@ -416,10 +614,10 @@ __global__ __launch_bounds__(256) void gemm_tn(AOperand<T> A, const T* __restric
     for (int i = 0; i < NBK; ++i)
 #pragma unroll
         for (int j = 0; j < NBN; ++j) {
-            const int64_t col = n0 + wn * (BNT / 2) + j * 32 + lane % 32;
+            const int64_t col = n0 + wn * TNW + j * 32 + lane % 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = k0 + wk * (kBKT / 2) + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                const int64_t row = k0 + wk * TK + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
                 out[row * ldp_n + col] = acc[i][j][r];
             }
         }
@@ -492,79 +690,137 @@ __global__ void relu_mask_kernel(int64_t M, int64_t C, int64_t N, const T* __res
     }
 }
 
-template <class T>
-sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dtype dt, void* C, int64_t ldc,
-                    const Epilogue& epi, hipStream_t s) {
-    AOperand<T> ao = make_aop<T>(A, M, dt);
-    const int64_t Kt = k_total(A.k1, A.a2 ? A.k2 : 0, dt);
-    EpiT<T> e{static_cast<T*>(C), ldc, static_cast<T*>(epi.pre), static_cast<const T*>(epi.addend),
-              epi.ld_add, epi.addend ? epi.n_add : 0, epi.bias, epi.relu};
-    const int64_t mblk = cdiv(M, kBM);
-    const T* B = static_cast<const T*>(Bp);
-    if (N <= 64) {
-        const int64_t nblk = cdiv(N, 64);
-        gemm_nn<T, 64><<<dim3(static_cast<unsigned>(mblk * nblk)), 256, 0, s>>>(ao, B, Kt, N, nblk, e);
-    } else if (N <= 128) {
-        const int64_t nblk = cdiv(N, 128);
-        gemm_nn<T, 128><<<dim3(static_cast<unsigned>(mblk * nblk)), 256, 0, s>>>(ao, B, Kt, N, nblk, e);
-    } else {
-        const int64_t nblk = cdiv(N, 256);
-        gemm_nn<T, 256><<<dim3(static_cast<unsigned>(mblk * nblk)), 256, 0, s>>>(ao, B, Kt, N, nblk, e);
+int device_cus() {
+    static int cus = 0;
+    if (!cus) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+            cus = v;
+        else
+            cus = 256;
     }
+    return cus;
+}
+
+size_t max_lds_per_block() {
+    static size_t lds = 0;
+    if (!lds) {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) == hipSuccess &&
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
+            lds = static_cast<size_t>(v);
+        else
+            lds = 65536;
+    }
+    return lds;
+}
+
+template <class T, int BN, bool MASK>
+sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e, hipStream_t s) {
+    const size_t lds = static_cast<size_t>(BN) * (Kt + Vec<T>::N) * sizeof(T) + BN * sizeof(float);
+    static bool attr_set = false;
+    if (!attr_set) {
+        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize,
+                                          static_cast<int>(max_lds_per_block())));
+        attr_set = true;
+    }
+    const int64_t n_nblk = cdiv(N, BN);
+    const int64_t n_mblk = cdiv(ao.M, 32);
+    int64_t n_mgroups = device_cus() / n_nblk;
+    if (n_mgroups < 1) n_mgroups = 1;
+    const int64_t need = cdiv(n_mblk, kNnWaves);
+    if (n_mgroups > need) n_mgroups = need;
+    gemm_nn<T, BN, MASK><<<dim3(static_cast<unsigned>(n_nblk * n_mgroups)), kNnWaves * 64, lds, s>>>(
+        ao, B, Kt, N, n_nblk, n_mgroups, n_mblk, e);
     SAG_LAUNCH_CHECK();
     return SAG_OK;
 }
 
+template <class T>
+sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dtype dt, void* C, int64_t ldc,
+                    const Epilogue& epi, hipStream_t s) {
+    AOperand<T> ao = make_aop<T>(A, M, dt, Bp);
+    const int64_t Kt = k_total(A.a1 ? A.k1 : 0, A.a2 ? A.k2 : 0, dt);
+    EpiT<T> e{static_cast<T*>(C), ldc, static_cast<T*>(epi.pre), static_cast<const T*>(epi.addend),
+              epi.ld_add, epi.addend ? epi.n_add : 0, epi.bias, epi.relu};
+    const T* B = static_cast<const T*>(Bp);
+    // widest N block whose slice of B fits in LDS
+    const size_t lds = max_lds_per_block();
+    const int64_t n32 = round_up(N, 32);
+    const size_t row = static_cast<size_t>(Kt + Vec<T>::N) * sizeof(T) + sizeof(float);
+    // (a 256-column block would need more than the 256 registers a lane has
+    // at two wavefronts per SIMD; the column blocks of one row group run on
+    // the same XCD, so A is read from HBM about once)
+    const bool m = ao.mask != nullptr;
+    if (n32 >= 128 && 128 * row <= lds)
+        return m ? launch_nn<T, 128, true>(ao, B, Kt, N, e, s) : launch_nn<T, 128, false>(ao, B, Kt, N, e, s);
+    if (n32 >= 64 && 64 * row <= lds)
+        return m ? launch_nn<T, 64, true>(ao, B, Kt, N, e, s) : launch_nn<T, 64, false>(ao, B, Kt, N, e, s);
+    if (32 * row <= lds)
+        return m ? launch_nn<T, 32, true>(ao, B, Kt, N, e, s) : launch_nn<T, 32, false>(ao, B, Kt, N, e, s);
+    return fail(SAG_E_UNSUPPORTED, "gemm: K too large for one LDS-resident slice of B");
+}
+
 struct TnPlan {
-    int bnt;
+    int kt, bnt;
     int64_t n_ktile, n_ntile, n_chunks, rows_per_chunk, ldp_k, ldp_n;
 };
 
-// The chunk count depends on M only (so workspace sizes grow with K and N):
-// chunks of at least 256 rows, at most 512 chunks.
+// The chunk count depends on M and N only, so workspace sizes grow with K.
 TnPlan tn_plan(int64_t M, int64_t Kv, int64_t N, sag_dtype dt) {
     TnPlan p;
-    p.bnt = N <= 64 ? 64 : 128;
-    p.n_ktile = cdiv(Kv > 0 ? Kv : 1, kBKT);
+    const int64_t kv = Kv > 0 ? Kv : 1;
+    p.kt = kv <= 128 ? 128 : (kv <= 256 ? 256 : 512);
+    p.bnt = (N <= 64 && p.kt != 128) ? 64 : 128;
+    p.n_ktile = cdiv(kv, p.kt);
     p.n_ntile = cdiv(N > 0 ? N : 1, p.bnt);
     const int64_t ms = dt == SAG_BF16 ? 32 : 16;
     const int64_t m = M > 0 ? M : 1;
-    int64_t want = cdiv(m, 256);
-    if (want > 512) want = 512;
-    const int64_t rpc = round_up(cdiv(m, want), ms);
-    p.rows_per_chunk = rpc;
-    p.n_chunks = cdiv(m, rpc);
-    p.ldp_k = p.n_ktile * kBKT;
+    int64_t want = cdiv(256, p.n_ntile);
+    const int64_t max_chunks = cdiv(m, ms);
+    if (want > max_chunks) want = max_chunks;
+    p.rows_per_chunk = round_up(cdiv(m, want), ms);
+    p.n_chunks = cdiv(m, p.rows_per_chunk);
+    p.ldp_k = p.n_ktile * p.kt;
     p.ldp_n = p.n_ntile * p.bnt;
     return p;
+}
+
+template <class T, int KT, int BNT>
+void launch_tn(const TnPlan& p, const AOperand<T>& ao, const void* B, int64_t ldb, const void* mask, int64_t ldmask,
+               int64_t N, float* part, float* pcs, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(p.n_chunks * p.n_ktile * p.n_ntile);
+    gemm_tn<T, KT, BNT><<<grid, kTnThreads, 0, s>>>(ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask),
+                                                     ldmask, N, p.n_ktile, p.n_ntile, p.rows_per_chunk, part,
+                                                     p.ldp_k, p.ldp_n, pcs);
 }
 
 template <class T>
 sag_status tn_typed(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t ldb, const void* mask,
                     int64_t ldmask, float* C, int64_t ldc, float* colsum, sag_dtype dt, void* ws, size_t ws_bytes,
                     hipStream_t s) {
-    AOperand<T> ao = make_aop<T>(A, M, dt);
-    const int64_t k2 = A.a2 ? A.k2 : 0;
-    const int64_t Kv = kp(A.k1, dt) + kp(k2, dt);
+    AOperand<T> ao = make_aop<T>(A, M, dt, B);
+    const int64_t k1 = ao.k1;
+    const int64_t k2 = ao.k2;
+    const int64_t Kv = kp(k1, dt) + kp(k2, dt);
     TnPlan p = tn_plan(M, Kv, N, dt);
     Carver c(ws, ws_bytes);
     float* part = c.take<float>(p.n_chunks * p.ldp_k * p.ldp_n);
     float* pcs = c.take<float>(p.n_chunks * p.ldp_n);
     if (!c.fits()) return fail(SAG_E_WORKSPACE, "gemm_tn: workspace too small");
-    const unsigned grid = static_cast<unsigned>(p.n_chunks * p.n_ktile * p.n_ntile);
-    if (p.bnt == 64)
-        gemm_tn<T, 64><<<grid, 256, 0, s>>>(ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask), ldmask, N,
-                                            p.n_ktile, p.n_ntile, p.rows_per_chunk, part, p.ldp_k, p.ldp_n,
-                                            colsum ? pcs : nullptr);
-    else
-        gemm_tn<T, 128><<<grid, 256, 0, s>>>(ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask), ldmask, N,
-                                             p.n_ktile, p.n_ntile, p.rows_per_chunk, part, p.ldp_k, p.ldp_n,
-                                             colsum ? pcs : nullptr);
+    float* cs = colsum ? pcs : nullptr;
+    if (p.kt == 512 && p.bnt == 64) launch_tn<T, 512, 64>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+    else if (p.kt == 512) launch_tn<T, 512, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+    else if (p.kt == 256 && p.bnt == 64) launch_tn<T, 256, 64>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+    else if (p.kt == 256) launch_tn<T, 256, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+    else launch_tn<T, 128, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
     SAG_LAUNCH_CHECK();
-    const int64_t total = (A.k1 + k2) * N;
+    const int64_t total = (k1 + k2) * N;
     const int64_t work = total > N ? total : N;
     tn_reduce<<<dim3(static_cast<unsigned>(cdiv(work, 256))), 256, 0, s>>>(
-        part, p.n_chunks, p.ldp_k, p.ldp_n, A.k1, kp(A.k1, dt), k2, N, C, ldc, pcs, colsum);
+        part, p.n_chunks, p.ldp_k, p.ldp_n, k1, kp(k1, dt), k2, N, C, ldc, pcs, colsum);
     SAG_LAUNCH_CHECK();
     return SAG_OK;
 }

@@ -27,7 +27,13 @@ namespace sag {
 namespace {
 
 inline bool aggregate_first(int64_t d_in, int64_t d_out) { return d_in <= d_out; }
-inline int64_t ldv(int64_t d, sag_dtype dt) { return round_up(d > 0 ? d : 1, vec_elems(dt)); }
+// Leading dimension of the library's own dense buffers: rows wider than 64
+// bytes start on a 128-byte cache line and span whole lines, so a gathered
+// row touches as few lines as possible; narrower rows are padded to 16 bytes.
+inline int64_t ldv(int64_t d, sag_dtype dt) {
+    const int64_t e = elt_size(dt), bytes = (d > 0 ? d : 1) * e;
+    return (bytes > 64 ? round_up(bytes, 128) : round_up(bytes, 16)) / e;
+}
 
 struct LayerWs {
     void* Bp = nullptr;

@@ -36,8 +36,13 @@ def dtype_code(dtype: torch.dtype) -> int:
 
 
 def padded_ld(d: int, dtype: torch.dtype) -> int:
-    v = 16 // torch.empty(0, dtype=dtype).element_size()
-    return max(v, (d + v - 1) // v * v)
+    """Row pitch in elements: rows wider than 64 bytes span whole 128-byte
+    cache lines (a gathered row then touches as few lines as possible),
+    narrower rows are padded to 16 bytes."""
+    es = torch.empty(0, dtype=dtype).element_size()
+    nbytes = max(d, 1) * es
+    line = 128 if nbytes > 64 else 16
+    return (nbytes + line - 1) // line * line // es
 
 
 def empty_dense(rows: int, d: int, dtype: torch.dtype, device, fill=None) -> torch.Tensor:

@@ -96,7 +96,7 @@ def test_workspace_queries_are_host_only():
     A = L.SagCsr()
     A.n_rows, A.n_cols, A.nnz = 100, 100, 1000
     assert lib.sag_spmm_workspace_bytes(ctypes.byref(A), 64) == 0   # no long rows without a schedule
-    assert lib.sag_gcn_save_bytes(100, 16, 64, 0) == 100 * 16 * 4   # aggregate first: Z is saved
+    assert lib.sag_gcn_save_bytes(100, 16, 64, 0) == 100 * 16 * 4   # aggregate first: Z is saved (64-B rows)
     assert lib.sag_gcn_save_bytes(100, 64, 16, 0) == 0              # transform first: nothing
-    assert lib.sag_sage_save_bytes(100, 100, 256, 1) == 100 * 104 * 2
+    assert lib.sag_sage_save_bytes(100, 100, 256, 1) == 100 * 128 * 2   # rows padded to 128-B lines
     assert lib.sag_gemm_tn_workspace_bytes(10000, 512, 256, 1) > 0
