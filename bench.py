@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--seg-len", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU baseline sample (0: auto)")
+    p.add_argument("--copy-calib", action="store_true",
+                   help="run one 1 GiB device copy before the steps (a kernel of known traffic for "
+                        "scaling hardware byte counters)")
     return p.parse_args()
 
 
@@ -121,19 +124,15 @@ class Model:
         return x
 
 
-def cpu_baseline(w, rows_hint: int):
-    """The oracle (float64, as it stands) on a bounded sample: the local row
-    range [0, R) of the workload's graph treated as a partition (its halo
-    columns included), every layer's forward and backward; scaled to the
-    full graph by n_local / R."""
+def _oracle_sample(w, R: int):
+    """Seconds the oracle takes for every layer's forward and backward on
+    the local rows [0, R) of the workload's graph treated as a partition
+    (its halo columns included), and the partition's column count."""
     import numpy as np
 
-    import gen
-    from oracle import csr as ocsr, layers as olay, native
+    from oracle import csr as ocsr, layers as olay
 
     src, dst = w.edges
-    n_l = w.hi - w.lo
-    R = rows_hint or max(1024, min(n_l, 16384))
     g = np.random.default_rng(0)
     deg = None
     if w.norm == "gcn":
@@ -145,7 +144,6 @@ def cpu_baseline(w, rows_hint: int):
     ob = ocsr.build(src, dst, w.n_global, w.lo, w.lo + R, w.symmetrize, w.self_loops, w.norm, deg_global=deg)
     n_ext = ob.A.n_cols
     total = 0.0
-    per_layer = []
     for l in range(w.n_layers):
         d_in, d_out = w.dims[l], w.dims[l + 1]
         H = g.standard_normal((n_ext, d_in))
@@ -159,15 +157,32 @@ def cpu_baseline(w, rows_hint: int):
         else:
             M, Y, _ = olay.sage_forward(ob.A, H, R, W, b, w.relu[l])
             olay.sage_backward(ob.AT, H[:R], M, W, Y, w.relu[l], G, want_dH=l > 0)
-        dt = time.perf_counter() - t0
-        per_layer.append(dt)
-        total += dt
+        total += time.perf_counter() - t0
+        del H, G
+    return total, n_ext
+
+
+def cpu_baseline(w, rows_hint: int, target_s: float = 15.0):
+    """The oracle (float64, as it stands) timed on a bounded sample of the
+    same workload: a row range sized from a short first run so that the
+    layers take about target_s seconds, scaled to the full graph by
+    n_local / R."""
+    from oracle import native
+
+    n_l = w.hi - w.lo
+    if rows_hint:
+        R = min(n_l, rows_hint)
+    else:
+        R0 = min(n_l, 16384)
+        t0, _ = _oracle_sample(w, R0)
+        R = min(n_l, max(R0, int(R0 * target_s / max(t0, 1e-3))))
+    total, n_ext = _oracle_sample(w, R)
     scale = n_l / R
     ms = total * scale * 1e3
     return {
         "value": round(ms, 1), "unit": "ms", "cores": native.num_threads(), "kind": "oracle",
         "sample": (f"local rows [0,{R}) of the {n_l}-row graph as a partition ({n_ext - R} halo columns), "
-                   f"{w.n_layers}-layer fwd+bwd in float64 took {total:.2f} s, scaled by {scale:.1f}"),
+                   f"{w.n_layers}-layer fwd+bwd in float64 took {total:.2f} s, scaled by {scale:.2f}"),
     }
 
 
@@ -193,6 +208,13 @@ def main():
     log(f"[bench] graph drawn in {time.perf_counter() - t0:.1f} s")
     m = Model(w, sag, torch, args.seg_len)
 
+    if args.copy_calib:
+        src_t = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
+        dst_t = torch.empty_like(src_t)
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 1 GiB read + 1 GiB written")
+        del src_t, dst_t
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         m.step()

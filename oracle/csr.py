@@ -162,3 +162,92 @@ def gather(src: np.ndarray, rows: np.ndarray) -> np.ndarray:
 def halo_rows(built: Built, stale_base: int) -> np.ndarray:
     """Stale-buffer row of each halo node: halo_gid[k] - stale_base."""
     return built.halo_gid.astype(np.int64) - stale_base
+
+
+def _adjacent_pairs(src, dst, nodes, symmetrize):
+    """(v, u) pairs with v in `nodes` aggregating u != v (each once)."""
+    src = np.asarray(src, np.int64)
+    dst = np.asarray(dst, np.int64)
+    nodes = np.unique(np.asarray(nodes, np.int64))
+    sel = np.isin(dst, nodes)
+    v, u = dst[sel], src[sel]
+    if symmetrize:
+        sel2 = np.isin(src, nodes)
+        v = np.concatenate([v, src[sel2]])
+        u = np.concatenate([u, dst[sel2]])
+    keep = u != v
+    v, u = v[keep], u[keep]
+    if v.size == 0:
+        return v, u
+    n = int(max(v.max(), u.max())) + 1
+    key = np.unique(v * n + u)
+    return key // n, key % n
+
+
+def build_rows(src, dst, n_global: int, lo: int, hi: int, symmetrize: bool, self_loops: bool,
+               norm: str, rows, deg_global=None):
+    """The normalised adjacency restricted to the local rows `rows` (global
+    ids in [lo, hi)), from the definition, one row at a time -- for checks
+    at sizes where the whole-partition build is too slow.
+
+    Returns a list with, per requested row, (columns, values): the global ids
+    of the row's entries (ascending) and their fp32 values, computed exactly
+    as in ``build`` (same readings: 0/1 graph, one self connection, degree
+    of a halo column = deg_global or 1 + its local entries)."""
+    if norm not in NORMS:
+        raise ValueError(f"norm must be one of {NORMS}")
+    rows = np.asarray(rows, np.int64)
+    if rows.size and (rows.min() < lo or rows.max() >= hi):
+        raise ValueError("rows must be local")
+
+    def neighbours(nodes):
+        v, u = _adjacent_pairs(src, dst, nodes, symmetrize)
+        return v, u
+
+    v, u = neighbours(rows)
+    cols = {int(r): [] for r in rows}
+    for a, b in zip(v.tolist(), u.tolist()):
+        cols[a].append(b)
+    if self_loops:
+        for r in cols:
+            cols[r].append(r)
+    cols = {r: np.unique(np.asarray(c, np.int64)) for r, c in cols.items()}
+
+    def row_degree(nodes):
+        """Entries of local rows `nodes` (their degree in A + I)."""
+        nodes = np.unique(np.asarray(nodes, np.int64))
+        vv, _ = neighbours(nodes)
+        cnt = np.zeros(nodes.size, np.int64)
+        if vv.size:
+            cnt += np.bincount(np.searchsorted(nodes, vv), minlength=nodes.size)
+        if self_loops:
+            cnt += 1
+        return dict(zip(nodes.tolist(), cnt.tolist()))
+
+    all_cols = np.unique(np.concatenate([c for c in cols.values()])) if cols else np.zeros(0, np.int64)
+    local_cols = all_cols[(all_cols >= lo) & (all_cols < hi)]
+    halo_cols = all_cols[(all_cols < lo) | (all_cols >= hi)]
+    deg = row_degree(np.concatenate([rows, local_cols]))
+    if halo_cols.size:
+        if deg_global is not None:
+            dg = np.asarray(deg_global, np.int64)
+            deg.update({int(c): int(dg[c]) for c in halo_cols})
+        else:
+            # 1 + the number of local rows holding the halo column
+            hv, hu = _adjacent_pairs(dst, src, halo_cols, symmetrize)   # (halo c, row r) with r -> c reversed
+            local = (hu >= lo) & (hu < hi)
+            cnt = np.bincount(np.searchsorted(halo_cols, hv[local]), minlength=halo_cols.size)
+            deg.update({int(c): 1 + int(k) for c, k in zip(halo_cols.tolist(), cnt.tolist())})
+    out = []
+    for r in rows.tolist():
+        c = cols[r]
+        dr = float(max(deg[r], 1))
+        if norm == "gcn":
+            dc = np.array([max(deg[int(x)], 1) for x in c], np.float64)
+            val = (1.0 / np.sqrt(dr * dc)).astype(np.float32)
+        elif norm == "mean":
+            val = np.full(c.size, np.float32(1.0 / dr), np.float32)
+        else:
+            val = np.ones(c.size, np.float32)
+        out.append((c, val))
+    return out

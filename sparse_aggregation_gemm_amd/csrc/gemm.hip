@@ -36,13 +36,20 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-// K of a packed B is padded to a multiple of 8 MFMA k-steps (the prefetch
-// depth of the NN kernel): 128 for bf16, 64 for fp32.
 constexpr int kNPad = 256;   // N of a packed B is padded to this
 
 inline int64_t kp(int64_t k, sag_dtype dt) { return round_up(k, vec_elems(dt)); }
+// K blocks of the NN product are padded to whole MFMA k-steps (16 bf16, 8
+// fp32), so that every k-step lies inside one block.
+inline int64_t kstep(sag_dtype dt) { return dt == SAG_BF16 ? 16 : 8; }
+inline int64_t kpn(int64_t k, sag_dtype dt) { return round_up(k, kstep(dt)); }
+// K of a packed B: a multiple of 16 MFMA k-steps when that costs at most
+// 16 extra k-steps' worth of padding, else of 8 (the NN kernel keeps that
+// many A fragments in flight).
 inline int64_t k_total(int64_t k1, int64_t k2, sag_dtype dt) {
-    return round_up(kp(k1, dt) + kp(k2, dt), dt == SAG_BF16 ? 128 : 64);
+    const int64_t kv = kpn(k1, dt) + kpn(k2, dt);
+    const int64_t step = kstep(dt);
+    return kv >= 16 * step ? round_up(kv, 16 * step) : round_up(kv, 8 * step);
 }
 
 // ---- element tricks on 16-byte vectors ---------------------------------------------
@@ -161,18 +168,19 @@ struct AOperand {
     }
 };
 
+// pad: the K padding of each block (16-byte vectors for TN, k-steps for NN).
 template <class T>
-AOperand<T> make_aop(const GemmA& A, int64_t M, sag_dtype dt, const void* safe) {
+AOperand<T> make_aop(const GemmA& A, int64_t M, sag_dtype dt, const void* safe, int64_t pad) {
     AOperand<T> o;
     o.a1 = static_cast<const T*>(A.a1);
     o.lda1 = A.lda1;
     o.k1 = A.a1 ? A.k1 : 0;
     o.m1 = A.a1 ? (A.m1 > 0 ? A.m1 : M) : 0;
-    o.k1p = A.a1 ? kp(A.k1, dt) : 0;
+    o.k1p = A.a1 ? round_up(A.k1, pad) : 0;
     o.a2 = static_cast<const T*>(A.a2);
     o.lda2 = A.lda2;
     o.k2 = A.a2 ? A.k2 : 0;
-    o.k2p = A.a2 ? kp(A.k2, dt) : 0;
+    o.k2p = A.a2 ? round_up(A.k2, pad) : 0;
     o.mask = static_cast<const T*>(A.mask);
     o.ldmask = A.ldmask;
     o.M = M;
@@ -251,7 +259,6 @@ __device__ __forceinline__ void store4(T* p, const float* y, int n) {
 // flight, so the only HBM traffic is A once and C once.  Persistent: one
 // workgroup per CU walks the 32-row blocks of its N block.
 constexpr int kNnWaves = 8;
-constexpr int kDepth = 8;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -264,14 +271,14 @@ template <class T> struct StreamMfma;
 // exactly the operand of one 32x32x16 MFMA.
 template <> struct StreamMfma<uint16_t> {
     static constexpr int KSTEP = 16;
+    // Bk: the LDS slice of this k-step, [BN][16]; lane reads n = j*32 + l%32
     template <int NB>
-    __device__ static __forceinline__ void step(const uint4& a, const uint16_t* Bs, int64_t LP, int ks, int lane,
-                                                f32x16_t (&acc)[NB]) {
+    __device__ static __forceinline__ void step(const uint4& a, const uint16_t* Bk, int lane, f32x16_t (&acc)[NB]) {
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-        const uint16_t* bp = Bs + (lane % 32) * LP + ks * 16 + (lane / 32) * 8;
+        const uint16_t* bp = Bk + (lane % 32) * 16 + (lane / 32) * 8;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(bp + j * 32 * LP);
+            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(bp + j * 32 * 16);
             acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, acc[j], 0, 0, 0);
         }
     }
@@ -282,40 +289,43 @@ template <> struct StreamMfma<uint16_t> {
 template <> struct StreamMfma<float> {
     static constexpr int KSTEP = 8;
     template <int NB>
-    __device__ static __forceinline__ void step(const uint4& a, const float* Bs, int64_t LP, int ks, int lane,
-                                                f32x16_t (&acc)[NB]) {
+    __device__ static __forceinline__ void step(const uint4& a, const float* Bk, int lane, f32x16_t (&acc)[NB]) {
         const f32x4_t av = __builtin_bit_cast(f32x4_t, a);
-        const float* bp = Bs + (lane % 32) * LP + ks * 8 + (lane / 32) * 4;
+        const float* bp = Bk + (lane % 32) * 8 + (lane / 32) * 4;
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
-            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bp + j * 32 * LP);
+            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bp + j * 32 * 8);
 #pragma unroll
             for (int q = 0; q < 4; ++q) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[q], av[q], acc[j], 0, 0, 0);
         }
     }
 };
 
-template <class T, int BN, bool MASK>
+template <class T, int BN, bool MASK, int kDepth>
 __global__ __launch_bounds__(kNnWaves * 64) void gemm_nn(AOperand<T> A, const T* __restrict__ Bp, int64_t Kt,
                                                          int64_t N, int64_t n_nblk, int64_t n_mgroups,
                                                          int64_t n_mblk, EpiT<T> e) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    // B slice of this column block as [k-step][BN][KSTEP]: the fragment of
+    // column block j of a k-step sits at a fixed offset, an immediate.
     T* Bs = reinterpret_cast<T*>(lds_raw);
     constexpr int V = Vec<T>::N;
     constexpr int NB = BN / 32;
     constexpr int KSTEP = StreamMfma<T>::KSTEP;
-    const int64_t LP = Kt + V;
+    constexpr int KSV = KSTEP / V;                  // vectors per k-step
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t nb = tile % n_nblk, mg = tile / n_nblk;
     const int64_t n0 = nb * BN;
     const int64_t kvec = Kt / V;
     for (int64_t q = threadIdx.x; q < BN * kvec; q += kNnWaves * 64) {
-        const int64_t r = q / kvec, c = (q % kvec) * V;
-        *reinterpret_cast<uint4*>(Bs + r * LP + c) = *reinterpret_cast<const uint4*>(Bp + (n0 + r) * Kt + c);
+        const int64_t r = q / kvec, c = q % kvec;   // column r, vector c
+        const int64_t ks = c / KSV, w = c % KSV;
+        *reinterpret_cast<uint4*>(Bs + (ks * BN + r) * KSTEP + w * V) =
+            *reinterpret_cast<const uint4*>(Bp + (n0 + r) * Kt + c * V);
     }
     // the bias of the block's columns sits after B, so the epilogue never
     // waits on global memory behind the prefetched fragments
-    float* bias_lds = reinterpret_cast<float*>(lds_raw + static_cast<size_t>(BN) * LP * sizeof(T));
+    float* bias_lds = reinterpret_cast<float*>(lds_raw + static_cast<size_t>(BN) * Kt * sizeof(T));
     for (int q = threadIdx.x; q < BN; q += kNnWaves * 64)
         bias_lds[q] = (e.bias && n0 + q < N) ? e.bias[n0 + q] : 0.f;
     __syncthreads();
@@ -324,18 +334,58 @@ __global__ __launch_bounds__(kNnWaves * 64) void gemm_nn(AOperand<T> A, const T*
     int64_t mb = mg * kNnWaves + wave;
     if (mb >= n_mblk) return;
     const int nks = static_cast<int>(Kt / KSTEP);   // a multiple of kDepth
-    const int64_t koff = (lane / 32) * (KSTEP / 2);
+    const int nks1 = static_cast<int>(A.k1p / KSTEP);                // k-steps of block 1
+    // the only k-steps whose fragments need zeroing: the ragged end of block 1
+    // and everything from the ragged end of block 2 on
+    const int fix1 = A.k1 < A.k1p ? static_cast<int>(A.k1 / KSTEP) : -1;
+    const int fix2 = static_cast<int>((A.k1p + A.k2) / KSTEP);
+    const int koff = (lane / 32) * (KSTEP / 2);
     const int64_t rl = lane % 32;
-    // kDepth raw fragments (and mask fragments) in flight; fixed up at use
+    // per-lane bases: row of this block (and the next), shifted by the lane's
+    // half of the k-step; the k-step offset is a uniform scalar
+    auto bases = [&](int64_t blk, const T*& b1, const T*& b2, const T*& bm) {
+        const T *p1, *p2;
+        A.row_ptrs(blk * 32 + rl, p1, p2);
+        b1 = p1 + koff;
+        b2 = p2 + koff - A.k1p;   // block 2 addressed with the virtual column
+        if constexpr (MASK) {
+            const int64_t r = blk * 32 + rl;
+            bm = A.mask + (r < A.M ? r : A.M - 1) * A.ldmask + koff;
+        }
+    };
+    // last 16-byte vector of each block inside its rows (a block's k-step
+    // padding may reach past the row's leading dimension)
+    const int64_t last1 = (A.k1 + V - 1) / V * V - V, last2 = (A.k2 + V - 1) / V * V - V;
+    auto frag_ptr = [&](const T* b1, const T* b2, int ks) -> const uint4* {
+        const T* p;
+        if (ks == fix1 || ks >= fix2) {
+            // edge or past the data (the value is zeroed at use): clamp the
+            // lane's column into the block's real vectors
+            const int64_t col = static_cast<int64_t>(ks) * KSTEP + koff;
+            if (col < A.k1p || !A.a2) {
+                const int64_t c = col < last1 ? col : last1;
+                p = b1 - koff + c;
+            } else {
+                const int64_t c2 = col - A.k1p;
+                p = b2 - koff + A.k1p + (c2 < last2 ? c2 : last2);
+            }
+        } else {
+            p = ks < nks1 ? b1 + ks * KSTEP : b2 + ks * KSTEP;
+        }
+        return reinterpret_cast<const uint4*>(p);
+    };
+    auto mask_ptr = [&](const T* bm_, int ks) -> const uint4* {
+        const int64_t col = static_cast<int64_t>(ks) * KSTEP + koff;
+        const int64_t c = col < last1 ? col : last1;
+        return reinterpret_cast<const uint4*>(bm_ - koff + c);
+    };
     uint4 buf[kDepth], mbuf[MASK ? kDepth : 1];
-    const T *p1, *p2, *q1, *q2;           // row pointers of this block and the next
-    A.row_ptrs(mb * 32 + rl, p1, p2);
-    const T* mrow = MASK ? A.mask + (mb * 32 + rl < A.M ? mb * 32 + rl : A.M - 1) * A.ldmask : nullptr;
-    const T* mrow_next = mrow;
+    const T *b1, *b2, *bm = nullptr, *c1, *c2, *cm = nullptr;
+    bases(mb, b1, b2, bm);
     static_for<0, kDepth>([&](auto dc) {
         constexpr int d = decltype(dc)::value;
-        buf[d] = *A.stream_addr(p1, p2, d * KSTEP + koff);
-        if constexpr (MASK) mbuf[d] = *reinterpret_cast<const uint4*>(mrow + min<int64_t>(d * KSTEP + koff, A.k1p - V));
+        buf[d] = *frag_ptr(b1, b2, d);
+        if constexpr (MASK) mbuf[d] = *mask_ptr(bm, d);
     });
     for (;;) {
         f32x16_t acc[NB];
@@ -344,39 +394,30 @@ __global__ __launch_bounds__(kNnWaves * 64) void gemm_nn(AOperand<T> A, const T*
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
         const int64_t mb_next = mb + stride;
-        A.row_ptrs(mb_next * 32 + rl, q1, q2);
-        if constexpr (MASK) {
-            const int64_t rn = mb_next * 32 + rl;
-            mrow_next = A.mask + (rn < A.M ? rn : A.M - 1) * A.ldmask;
-        }
-        // rows of this block at or past m1 read block 1 as zero
-        const bool zero_rows = A.a1 && (mb * 32 + 31 >= A.m1) && (mb * 32 < A.M);
+        bases(mb_next, c1, c2, cm);
+        // rows of this block at or past m1 (or M) read block 1 as zero
+        const bool zero_rows = mb * 32 + 31 >= A.m1;
         for (int ks0 = 0; ks0 < nks; ks0 += kDepth) {
             static_for<0, kDepth>([&](auto dc) {
                 constexpr int d = decltype(dc)::value;
                 const int ks = ks0 + d;
-                const int64_t k_use = static_cast<int64_t>(ks) * KSTEP + koff;
                 uint4 a = buf[d];
                 if constexpr (MASK) {
-                    // block 1 only; on the boundary step the upper half-wave is in block 2
-                    if (ks * KSTEP < A.k1p) {
-                        a = sel(k_use < A.k1p, apply_mask<T>(a, mbuf[d]), a);
-                    }
+                    if (ks < nks1) a = apply_mask<T>(a, mbuf[d]);
                 }
-                if (zero_rows || A.needs_fix(static_cast<int64_t>(ks) * KSTEP, KSTEP))
-                    a = A.fix(a, mb * 32 + rl, k_use);
+                if (zero_rows || ks == fix1 || ks >= fix2)
+                    a = A.fix(a, mb * 32 + rl, static_cast<int64_t>(ks) * KSTEP + koff);
                 int kn = ks + kDepth;
-                const T *r1 = p1, *r2 = p2, *mr = mrow;
+                const T *r1 = b1, *r2 = b2, *rm = bm;
                 if (kn >= nks) {
                     kn -= nks;
-                    r1 = q1;
-                    r2 = q2;
-                    mr = mrow_next;
+                    r1 = c1;
+                    r2 = c2;
+                    rm = cm;
                 }
-                const int64_t k_next = static_cast<int64_t>(kn) * KSTEP + koff;
-                buf[d] = *A.stream_addr(r1, r2, k_next);
-                if constexpr (MASK) mbuf[d] = *reinterpret_cast<const uint4*>(mr + min<int64_t>(k_next, A.k1p - V));
-                StreamMfma<T>::template step<NB>(a, Bs, LP, ks, lane, acc);
+                buf[d] = *frag_ptr(r1, r2, kn);
+                if constexpr (MASK) mbuf[d] = *mask_ptr(rm, kn);
+                StreamMfma<T>::template step<NB>(a, Bs + static_cast<int64_t>(ks) * BN * KSTEP, lane, acc);
             });
         }
         // epilogue: lane l holds row l%32 of the block; register quad q of
@@ -410,9 +451,9 @@ __global__ __launch_bounds__(kNnWaves * 64) void gemm_nn(AOperand<T> A, const T*
         }
         mb = mb_next;
         if (mb >= n_mblk) break;
-        p1 = q1;
-        p2 = q2;
-        mrow = mrow_next;
+        b1 = c1;
+        b2 = c2;
+        bm = cm;
     }
 }
 
@@ -513,29 +554,29 @@ __global__ __launch_bounds__(kTnThreads) void gemm_tn(AOperand<T> A, const T* __
         if constexpr (kBf16) {
             // transpose: element (m, k) goes to As[k][m]; 4 m values per write
             if (t < ITEMS_A) {
+                const uint32_t w0[4] = {ra[0].x, ra[0].y, ra[0].z, ra[0].w};
+                const uint32_t w1[4] = {ra[1].x, ra[1].y, ra[1].z, ra[1].w};
+                const uint32_t w2[4] = {ra[2].x, ra[2].y, ra[2].z, ra[2].w};
+                const uint32_t w3[4] = {ra[3].x, ra[3].y, ra[3].z, ra[3].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    uint32_t lo = 0, hi = 0;
-                    const uint32_t w0[4] = {ra[0].x, ra[0].y, ra[0].z, ra[0].w};
-                    const uint32_t w1[4] = {ra[1].x, ra[1].y, ra[1].z, ra[1].w};
-                    const uint32_t w2[4] = {ra[2].x, ra[2].y, ra[2].z, ra[2].w};
-                    const uint32_t w3[4] = {ra[3].x, ra[3].y, ra[3].z, ra[3].w};
-                    const int sh = (e & 1) ? 16 : 0;
-                    lo = ((w0[e / 2] >> sh) & 0xffffu) | (((w1[e / 2] >> sh) & 0xffffu) << 16);
-                    hi = ((w2[e / 2] >> sh) & 0xffffu) | (((w3[e / 2] >> sh) & 0xffffu) << 16);
+                    // halves e of rows m, m+1 (and m+2, m+3) side by side
+                    const uint32_t sel_b = (e & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = __builtin_amdgcn_perm(w1[e / 2], w0[e / 2], sel_b);
+                    const uint32_t hi = __builtin_amdgcn_perm(w3[e / 2], w2[e / 2], sel_b);
                     *reinterpret_cast<uint2*>(&As[(a_cv * 8 + e) * LPA + a_rq * 4]) = make_uint2(lo, hi);
                 }
             }
             if (t < ITEMS_B) {
+                const uint32_t w0[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
+                const uint32_t w1[4] = {rb[1].x, rb[1].y, rb[1].z, rb[1].w};
+                const uint32_t w2[4] = {rb[2].x, rb[2].y, rb[2].z, rb[2].w};
+                const uint32_t w3[4] = {rb[3].x, rb[3].y, rb[3].z, rb[3].w};
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t w0[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
-                    const uint32_t w1[4] = {rb[1].x, rb[1].y, rb[1].z, rb[1].w};
-                    const uint32_t w2[4] = {rb[2].x, rb[2].y, rb[2].z, rb[2].w};
-                    const uint32_t w3[4] = {rb[3].x, rb[3].y, rb[3].z, rb[3].w};
-                    const int sh = (e & 1) ? 16 : 0;
-                    const uint32_t lo = ((w0[e / 2] >> sh) & 0xffffu) | (((w1[e / 2] >> sh) & 0xffffu) << 16);
-                    const uint32_t hi = ((w2[e / 2] >> sh) & 0xffffu) | (((w3[e / 2] >> sh) & 0xffffu) << 16);
+                    const uint32_t sel_b = (e & 1) ? 0x07060302u : 0x05040100u;
+                    const uint32_t lo = __builtin_amdgcn_perm(w1[e / 2], w0[e / 2], sel_b);
+                    const uint32_t hi = __builtin_amdgcn_perm(w3[e / 2], w2[e / 2], sel_b);
                     *reinterpret_cast<uint2*>(&Bs[(b_cv * 8 + e) * LPB + b_rq * 4]) = make_uint2(lo, hi);
                 }
             }
@@ -716,12 +757,12 @@ size_t max_lds_per_block() {
     return lds;
 }
 
-template <class T, int BN, bool MASK>
-sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e, hipStream_t s) {
-    const size_t lds = static_cast<size_t>(BN) * (Kt + Vec<T>::N) * sizeof(T) + BN * sizeof(float);
+template <class T, int BN, bool MASK, int D>
+sag_status launch_nn_d(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e, hipStream_t s) {
+    const size_t lds = static_cast<size_t>(BN) * Kt * sizeof(T) + BN * sizeof(float);
     static bool attr_set = false;
     if (!attr_set) {
-        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK>),
+        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK, D>),
                                           hipFuncAttributeMaxDynamicSharedMemorySize,
                                           static_cast<int>(max_lds_per_block())));
         attr_set = true;
@@ -732,16 +773,23 @@ sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, c
     if (n_mgroups < 1) n_mgroups = 1;
     const int64_t need = cdiv(n_mblk, kNnWaves);
     if (n_mgroups > need) n_mgroups = need;
-    gemm_nn<T, BN, MASK><<<dim3(static_cast<unsigned>(n_nblk * n_mgroups)), kNnWaves * 64, lds, s>>>(
+    gemm_nn<T, BN, MASK, D><<<dim3(static_cast<unsigned>(n_nblk * n_mgroups)), kNnWaves * 64, lds, s>>>(
         ao, B, Kt, N, n_nblk, n_mgroups, n_mblk, e);
     SAG_LAUNCH_CHECK();
     return SAG_OK;
 }
 
+template <class T, int BN, bool MASK>
+sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e, hipStream_t s) {
+    const int64_t nks = Kt / StreamMfma<T>::KSTEP;
+    if (nks % 16 == 0) return launch_nn_d<T, BN, MASK, 16>(ao, B, Kt, N, e, s);
+    return launch_nn_d<T, BN, MASK, 8>(ao, B, Kt, N, e, s);
+}
+
 template <class T>
 sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dtype dt, void* C, int64_t ldc,
                     const Epilogue& epi, hipStream_t s) {
-    AOperand<T> ao = make_aop<T>(A, M, dt, Bp);
+    AOperand<T> ao = make_aop<T>(A, M, dt, Bp, kstep(dt));
     const int64_t Kt = k_total(A.a1 ? A.k1 : 0, A.a2 ? A.k2 : 0, dt);
     EpiT<T> e{static_cast<T*>(C), ldc, static_cast<T*>(epi.pre), static_cast<const T*>(epi.addend),
               epi.ld_add, epi.addend ? epi.n_add : 0, epi.bias, epi.relu};
@@ -749,7 +797,7 @@ sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dt
     // widest N block whose slice of B fits in LDS
     const size_t lds = max_lds_per_block();
     const int64_t n32 = round_up(N, 32);
-    const size_t row = static_cast<size_t>(Kt + Vec<T>::N) * sizeof(T) + sizeof(float);
+    const size_t row = static_cast<size_t>(Kt) * sizeof(T) + sizeof(float);
     // (a 256-column block would need more than the 256 registers a lane has
     // at two wavefronts per SIMD; the column blocks of one row group run on
     // the same XCD, so A is read from HBM about once)
@@ -801,7 +849,7 @@ template <class T>
 sag_status tn_typed(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t ldb, const void* mask,
                     int64_t ldmask, float* C, int64_t ldc, float* colsum, sag_dtype dt, void* ws, size_t ws_bytes,
                     hipStream_t s) {
-    AOperand<T> ao = make_aop<T>(A, M, dt, B);
+    AOperand<T> ao = make_aop<T>(A, M, dt, B, vec_elems(dt));
     const int64_t k1 = ao.k1;
     const int64_t k2 = ao.k2;
     const int64_t Kv = kp(k1, dt) + kp(k2, dt);
@@ -841,9 +889,9 @@ sag_status pack_b(const PackSrc& src, int64_t k1, int64_t k2, const NLayout& nl,
                      s, elt_size(dt) * ((k1 + k2) * nl.total() + total), 0);
     const dim3 grid(static_cast<unsigned>(cdiv(total, 256)));
     if (dt == SAG_BF16)
-        pack_kernel<uint16_t><<<grid, 256, 0, s>>>(src, k1, kp(k1, dt), k2, Kt, nl, n_pad, static_cast<uint16_t*>(Bp));
+        pack_kernel<uint16_t><<<grid, 256, 0, s>>>(src, k1, kpn(k1, dt), k2, Kt, nl, n_pad, static_cast<uint16_t*>(Bp));
     else
-        pack_kernel<float><<<grid, 256, 0, s>>>(src, k1, kp(k1, dt), k2, Kt, nl, n_pad, static_cast<float*>(Bp));
+        pack_kernel<float><<<grid, 256, 0, s>>>(src, k1, kpn(k1, dt), k2, Kt, nl, n_pad, static_cast<float*>(Bp));
     SAG_LAUNCH_CHECK();
     return SAG_OK;
 }

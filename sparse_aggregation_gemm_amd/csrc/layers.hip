@@ -328,14 +328,15 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
         a.a2 = save; a.lda2 = ldm; a.k2 = d_in;
         return gemm_run(n_l, d_out, a, w.Bp, dt, Out, ldo, e, s);
     }
-    // transform first: [P | T] = H_ext [W_self | W_neigh]; Out = A T + P + b
+    // transform first: [T | P] = H_ext [W_neigh | W_self]; Out = A T + P + b
+    // (T first, so a gathered row of T starts on a cache line)
     const int64_t np = ldv(d_out, dt);
     const int64_t ldpt = ldv(np + d_out, dt);
     PackSrc src;
-    src.p[0][0] = W;
+    src.p[0][0] = Wc + d_in * d_out * es;
     src.sk[0][0] = d_out;
     src.sn[0][0] = 1;
-    src.p[0][1] = Wc + d_in * d_out * es;
+    src.p[0][1] = W;
     src.sk[0][1] = d_out;
     src.sn[0][1] = 1;
     NLayout nl;
@@ -346,11 +347,10 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
     GemmA a;
     a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = A->n_cols;
     SAG_TRY(gemm_run(A->n_cols, np + d_out, a, w.Bp, dt, w.t1, ldpt, Epilogue{}, s));
-    e.addend = w.t1;
+    e.addend = static_cast<const char*>(w.t1) + np * es;
     e.ld_add = ldpt;
     e.n_add = n_l;
-    const void* T = static_cast<const char*>(w.t1) + np * es;
-    return spmm_run(*A, T, ldpt, dt, d_out, Out, ldo, dt, e, w.spmm, w.spmm_bytes, s);
+    return spmm_run(*A, w.t1, ldpt, dt, d_out, Out, ldo, dt, e, w.spmm, w.spmm_bytes, s);
 }
 
 extern "C" size_t sag_sage_backward_workspace_bytes(const sag_csr* AT, int64_t n_local, int64_t d_in, int64_t d_out,

@@ -110,3 +110,33 @@ def test_gemm_tn_two_blocks():
     ref = A64.T @ f64(B)
     den = np.abs(A64).T @ np.abs(f64(B))
     assert _err(f64(C), ref, den) <= 1e-5
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("masked", [False, True])
+def test_gemm_tight_row_pitch(dt, masked):
+    """Operands whose row pitch is the width rounded to 16 bytes only (e.g.
+    100 bf16 in rows of 104) and that end exactly at the end of their
+    allocation: the padded k-steps must not read past the rows."""
+    g = np.random.default_rng(31)
+    M, K1, K2, N = 333, 100, 42, 96
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    v = 4 if dt == "f32" else 8
+
+    def tight(rows, cols):
+        ld = (cols + v - 1) // v * v
+        buf = torch.empty(rows * ld, dtype=tdt, device=DEV)
+        t = buf.view(rows, ld)[:, :cols]
+        t.copy_(torch.from_numpy(g.standard_normal((rows, cols)).astype(np.float32)).to(tdt).to(DEV))
+        return t
+
+    A1, A2 = tight(M, K1), tight(M, K2)
+    Mk = tight(M, K1) if masked else None
+    W = torch.from_numpy(g.standard_normal((K1 + K2, N)).astype(np.float32)).to(tdt).to(DEV)
+    say(f"gemm tight pitch dt={dt} masked={masked}")
+    C = sag.gemm(A1, W, A2=A2, mask=Mk)
+    a1 = f64(A1) * ((f64(Mk) > 0) if masked else 1.0)
+    A64 = np.concatenate([a1, f64(A2)], 1)
+    ref = A64 @ f64(W)
+    den = np.abs(A64) @ np.abs(f64(W))
+    assert _err(f64(C), ref, den) <= tol(dt)

@@ -176,3 +176,28 @@ def test_empty_graph():
     assert b.A.n_rows == 0 and b.A.nnz == 0 and b.AT.n_rows == 0
     b = csr.build(np.zeros(0, np.int32), np.zeros(0, np.int32), 10, 0, 5, True, False, "mean")
     assert b.A.nnz == 0 and b.A.indptr.tolist() == [0] * 6
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_build_rows_matches_whole_build(seed):
+    """The row-by-row build (used for checks at full size) gives the same
+    entries and bit-identical values as the whole-partition build."""
+    g = np.random.default_rng(500 + seed)
+    n = int(g.integers(5, 90))
+    src, dst = _random_edges(g, n, int(g.integers(0, 5 * n)))
+    lo = int(g.integers(0, n))
+    hi = int(g.integers(lo + 1, n + 1))
+    sym, loops = bool(seed % 2), bool((seed // 2) % 2)
+    norm = ("gcn", "mean", "none")[seed % 3]
+    b = csr.build(src, dst, n, lo, hi, sym, loops, norm)
+    rows = np.arange(lo, hi)
+    got = csr.build_rows(src, dst, n, lo, hi, sym, loops, norm, rows)
+    n_l = hi - lo
+    halo = np.concatenate([b.halo_gid.astype(np.int64), [0]])
+    for i, (cols, vals) in enumerate(got):
+        s, e = b.A.indptr[i], b.A.indptr[i + 1]
+        c = b.A.indices[s:e].astype(np.int64)
+        glob = np.where(c < n_l, c + lo, halo[np.clip(c - n_l, 0, halo.size - 1)])
+        order = np.argsort(glob)
+        assert np.array_equal(glob[order], cols)
+        assert np.array_equal(b.A.values[s:e][order].view(np.uint32), vals.view(np.uint32))
