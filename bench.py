@@ -16,8 +16,12 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +31,18 @@ sys.path.insert(0, ROOT)
 METRIC = "GCN layer fwd+bwd ms; SpMM GB/s (% HBM peak) on 2.45M-node graph"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+# copy calibration: an identity row gather of 2^21 rows of 512 bytes through
+# the library (1 GiB read + the int32 row list, 1 GiB written)
+CALIB_ROWS = 1 << 21
+CALIB_ROW_BYTES = 512
+CALIB_READ = CALIB_ROWS * (CALIB_ROW_BYTES + 4)
+CALIB_WRITE = CALIB_ROWS * CALIB_ROW_BYTES
+CALIB_KERNEL = "gather_rows"
+CSRC = os.path.join(ROOT, "sparse_aggregation_gemm_amd", "csrc")
+# sources whose text decides each op family's kernels (a counter summary is
+# valid only for the sources it was taken on)
+OP_SOURCES = {"spmm": ["spmm.hip", "common.h", "ops.h"], "gemm_nn": ["gemm.hip", "common.h", "ops.h"],
+              "gemm_tn": ["gemm.hip", "common.h", "ops.h"], "gather": ["gather.hip", "common.h"]}
 
 
 def log(*a):
@@ -44,9 +60,116 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU baseline sample (0: auto)")
     p.add_argument("--copy-calib", action="store_true",
-                   help="run one 1 GiB device copy before the steps (a kernel of known traffic for "
-                        "scaling hardware byte counters)")
+                   help="run one 1 GiB identity row gather before the steps (a copy kernel of known "
+                        "traffic for scaling hardware byte counters)")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                   help="no GPU work: read two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
+                        "of a --copy-calib run and write the dominant kernel's HBM traffic summary")
+    p.add_argument("--op", help="trace op name the summary is for (with --summarize-counters)")
+    p.add_argument("--kernel", help="kernel name substring of that op (with --summarize-counters)")
+    p.add_argument("--out", help="summary file to write (with --summarize-counters)")
     return p.parse_args()
+
+
+def sources_digest(op: str) -> str:
+    fam = op.split("[", 1)[0]
+    h = hashlib.sha256()
+    for f in OP_SOURCES.get(fam, []):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_means(folder: str, counter: str):
+    """Per kernel name: list of per-dispatch values of `counter` (KiB)."""
+    per = {}
+    for f in glob.glob(os.path.join(folder, "**", "*counter_collection.csv"), recursive=True):
+        acc = {}
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+        for (k, _), v in acc.items():
+            per.setdefault(k, []).append(v)
+    return per
+
+
+def _pick(per, sub):
+    hits = {k: v for k, v in per.items() if sub in k}
+    if len(hits) != 1:
+        raise SystemExit(f"kernel substring {sub!r} matches {len(hits)} kernels: {list(hits)[:4]}")
+    (k, v), = hits.items()
+    return k, v
+
+
+def summarize_counters(args):
+    """HBM traffic of one kernel from FETCH_SIZE / WRITE_SIZE passes, each
+    scaled by what the counter reads for the calibration copy of known size."""
+    fetch = _counter_means(args.summarize_counters[0], "FETCH_SIZE")
+    write = _counter_means(args.summarize_counters[1], "WRITE_SIZE")
+    _, cf = _pick(fetch, CALIB_KERNEL)
+    _, cw = _pick(write, CALIB_KERNEL)
+    kname, kf = _pick(fetch, args.kernel)
+    _, kw = _pick(write, args.kernel)
+    f_fetch = CALIB_READ / (sum(cf) / len(cf) * 1024)
+    f_write = CALIB_WRITE / (sum(cw) / len(cw) * 1024)
+    fetch_b = sum(kf) / len(kf) * 1024 * f_fetch
+    write_b = sum(kw) / len(kw) * 1024 * f_write
+    rec = {"op": args.op, "kernel": kname, "sources_sha256_16": sources_digest(args.op),
+           "dispatches": [len(kf), len(kw)], "calib_fetch_kib": sum(cf) / len(cf),
+           "calib_write_kib": sum(cw) / len(cw), "calib_read_bytes": CALIB_READ,
+           "calib_write_bytes": CALIB_WRITE, "scale_fetch": round(f_fetch, 4), "scale_write": round(f_write, 4),
+           "kernel_fetch_kib": sum(kf) / len(kf), "kernel_write_kib": sum(kw) / len(kw),
+           "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
+           "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b))}
+    cmd = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib")
+    text = f"""# HBM traffic of `{args.op}` from TCC byte counters
+
+Kernel: `{kname}`
+
+Commands (each a run of its own, from the repository root):
+
+```
+rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize_counters[0]} -o fetch -- {cmd}
+rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize_counters[1]} -o write -- {cmd}
+python3 bench.py --summarize-counters {args.summarize_counters[0]} {args.summarize_counters[1]} \\
+    --op '{args.op}' --kernel '{args.kernel}' --out {args.out}
+```
+
+`--copy-calib` runs one identity row gather through the library before the steps:
+{CALIB_ROWS} rows of {CALIB_ROW_BYTES} B, so {CALIB_READ} bytes read (rows + int32 row list) and
+{CALIB_WRITE} bytes written.  Each counter is scaled by known bytes / counted bytes of that copy.
+
+| | calibration copy (KiB/dispatch) | scale | kernel (KiB/dispatch, mean of {len(kf)}) | kernel bytes/launch |
+|---|---|---|---|---|
+| FETCH_SIZE | {rec['calib_fetch_kib']:.0f} | {f_fetch:.4f} | {rec['kernel_fetch_kib']:.0f} | {fetch_b:.4e} |
+| WRITE_SIZE | {rec['calib_write_kib']:.0f} | {f_write:.4f} | {rec['kernel_write_kib']:.0f} | {write_b:.4e} |
+
+Traffic per launch: {fetch_b + write_b:.4e} bytes.  The counters count L2 <-> fabric bytes, so
+hits in the memory-side cache (MALL) are included: an upper proxy for DRAM bytes.
+
+Machine-readable record (bench.py reads it while the kernel sources keep this digest):
+
+<!-- counters {json.dumps(rec)} -->
+"""
+    with open(args.out, "w") as fh:
+        fh.write(text)
+    print(json.dumps(rec))
+
+
+def stored_traffic(op: str):
+    """Traffic per launch of `op` from a committed counter summary taken on
+    the current kernel sources, else None."""
+    dig = sources_digest(op)
+    for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(f) as fh:
+            for m in re.finditer(r"<!-- counters (\{.*\}) -->", fh.read()):
+                rec = json.loads(m.group(1))
+                if rec.get("op") == op and rec.get("sources_sha256_16") == dig:
+                    return rec["traffic_bytes_per_launch"], os.path.relpath(f, ROOT)
+    return None, None
 
 
 class Model:
@@ -188,6 +311,9 @@ def cpu_baseline(w, rows_hint: int, target_s: float = 15.0):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path here is one "
               "GPU's share of a graph, with no collectives.", file=sys.stderr)
@@ -209,12 +335,14 @@ def main():
     m = Model(w, sag, torch, args.seg_len)
 
     if args.copy_calib:
-        src_t = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0").fill_(1.0)
-        dst_t = torch.empty_like(src_t)
-        dst_t.copy_(src_t)
+        es = CALIB_ROW_BYTES // 2
+        src_t = sag.empty_dense(CALIB_ROWS, es, torch.bfloat16, "cuda:0", fill=1.0)
+        dst_t = sag.empty_dense(CALIB_ROWS, es, torch.bfloat16, "cuda:0")
+        rows_t = torch.arange(CALIB_ROWS, dtype=torch.int32, device="cuda:0")
+        sag.halo_gather(src_t, rows_t, dst_t)
         torch.cuda.synchronize()
-        log("[bench] copy calibration: 1 GiB read + 1 GiB written")
-        del src_t, dst_t
+        log(f"[bench] copy calibration: {CALIB_READ} bytes read, {CALIB_WRITE} written")
+        del src_t, dst_t, rows_t
     log(f"[bench] warmup {args.warmup} steps")
     for _ in range(args.warmup):
         m.step()
@@ -259,7 +387,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(dom_o["bytes"] / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    traffic, tsrc = stored_traffic(dom["op"])
+    roof["traffic"] = traffic
+    roof["traffic_source"] = tsrc
     roof["kernel"] = dom["op"]
     roof["alg_bytes_per_launch"] = dom_o["bytes"]
     roof["avg_launch_ms"] = dom["avg_ms"]
@@ -275,7 +405,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
-                   "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "model": w.model,
+                   "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
                    "seg_len": args.seg_len, "schedule": sag.csr_info(A)},
         "build_ms": round(m.build_ms, 1),
         "spmm": spmm,
