@@ -39,17 +39,16 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 constexpr int kNPad = 256;   // N of a packed B is padded to this
 
 inline int64_t kp(int64_t k, sag_dtype dt) { return round_up(k, vec_elems(dt)); }
-// K blocks of the NN product are padded to whole MFMA k-steps (16 bf16, 8
-// fp32), so that every k-step lies inside one block.
-inline int64_t kstep(sag_dtype dt) { return dt == SAG_BF16 ? 16 : 8; }
-inline int64_t kpn(int64_t k, sag_dtype dt) { return round_up(k, kstep(dt)); }
-// K of a packed B: a multiple of 16 MFMA k-steps when that costs at most
-// 16 extra k-steps' worth of padding, else of 8 (the NN kernel keeps that
-// many A fragments in flight).
+// K blocks of the NN product are padded to whole 128-byte chunks (64 bf16,
+// 32 fp32: four MFMA k-steps), so that every chunk lies inside one block.
+inline int64_t kchunk(sag_dtype dt) { return dt == SAG_BF16 ? 64 : 32; }
+inline int64_t kpc(int64_t k, sag_dtype dt) { return round_up(k, kchunk(dt)); }
+// K of a packed B: a multiple of four chunks once it holds four, else of
+// two (the NN kernel keeps that many chunks in flight).
 inline int64_t k_total(int64_t k1, int64_t k2, sag_dtype dt) {
-    const int64_t kv = kpn(k1, dt) + kpn(k2, dt);
-    const int64_t step = kstep(dt);
-    return kv >= 16 * step ? round_up(kv, 16 * step) : round_up(kv, 8 * step);
+    const int64_t kv = kpc(k1, dt) + kpc(k2, dt);
+    const int64_t c = kchunk(dt);
+    return kv >= 4 * c ? round_up(kv, 4 * c) : round_up(kv, 2 * c);
 }
 
 // ---- element tricks on 16-byte vectors ---------------------------------------------
@@ -253,207 +252,277 @@ __device__ __forceinline__ void store4(T* p, const float* y, int n) {
 
 // ---- NN ------------------------------------------------------------------------------
 // C = A B with M huge and K, N small (the layer's transform and input
-// gradient).  A workgroup keeps its BN columns of the packed B (all of K) in
-// LDS for its whole life; each of its wavefronts streams 32-row blocks of A
-// straight from memory into MFMA operands with kDepth 16-byte fragments in
-// flight, so the only HBM traffic is A once and C once.  Persistent: one
-// workgroup per CU walks the 32-row blocks of its N block.
+// gradient).  A workgroup keeps its BN columns of the packed B (all of K)
+// in LDS for its whole life; each of its eight wavefronts walks 32-row
+// blocks of A.  A is read in chunks of 128 bytes of k per row with eight
+// lanes per row, so every load instruction fetches four whole cache lines;
+// the chunk goes through a per-wavefront LDS tile into the MFMA operand
+// layout, PD chunks ahead in registers.  The results go back through the
+// same tile so that C is written in whole lines as well.  The tile and the
+// B slice XOR-swizzle their 16-byte units so that row-strided fragment
+// reads do not collide in banks.  The K blocks
+// A1 and A2 are padded to whole chunks in the packed B, so each chunk comes
+// from one block and only the last chunk of a block needs zeroing.
+//
+// The MFMAs compute transposed blocks, C^T = B^T A^T: B supplies the first
+// operand and A the second, so lane l accumulates row l%32 of a 32x32 block
+// of C and register r holds column 8*(r/4) + 4*(l/32) + r%4.  bf16: unit
+// h of a k-step holds its k 8h..8h+7, the operand of one 32x32x16 MFMA.
+// fp32: unit h holds k 4h..4h+3 of the k-step; four 32x32x2 MFMAs pair
+// k+q with k+4+q (B is stored with the same pairing).
 constexpr int kNnWaves = 8;
+constexpr int kNnRows = 32;                       // rows of a wavefront block
+constexpr int kNnTile = kNnRows * 128;            // bytes of a wavefront's tile
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-template <class T> struct StreamMfma;
-// The MFMAs compute transposed blocks, C^T = B^T A^T: B supplies the first
-// operand and A the second, so lane l accumulates row l%32 of a 32x32 block
-// of C and register r holds column 8*(r/4) + 4*(l/32) + r%4 -- four
-// consecutive columns per register quad, stored as one vector.
-// bf16: one A load holds k0..k0+7 (lanes 0-31) or k0+8..k0+15 (lanes 32-63),
-// exactly the operand of one 32x32x16 MFMA.
-template <> struct StreamMfma<uint16_t> {
-    static constexpr int KSTEP = 16;
-    // Bk: the LDS slice of this k-step, [BN][16]; lane reads n = j*32 + l%32
-    template <int NB>
-    __device__ static __forceinline__ void step(const uint4& a, const uint16_t* Bk, int lane, f32x16_t (&acc)[NB]) {
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-        const uint16_t* bp = Bk + (lane % 32) * 16 + (lane / 32) * 8;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(bp + j * 32 * 16);
-            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bv, av, acc[j], 0, 0, 0);
-        }
-    }
-};
-// fp32: one A load holds k0..k0+3 (lanes 0-31) or k0+4..k0+7 (lanes 32-63);
-// four 32x32x2 MFMAs pair k0+s with k0+4+s, and B is read with the same
-// pairing, so the products sum over k0..k0+7.
-template <> struct StreamMfma<float> {
-    static constexpr int KSTEP = 8;
-    template <int NB>
-    __device__ static __forceinline__ void step(const uint4& a, const float* Bk, int lane, f32x16_t (&acc)[NB]) {
-        const f32x4_t av = __builtin_bit_cast(f32x4_t, a);
-        const float* bp = Bk + (lane % 32) * 8 + (lane / 32) * 4;
-#pragma unroll
-        for (int j = 0; j < NB; ++j) {
-            const f32x4_t bv = *reinterpret_cast<const f32x4_t*>(bp + j * 32 * 8);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bv[q], av[q], acc[j], 0, 0, 0);
-        }
-    }
-};
+// LDS swizzles, free of bank conflicts whether a 16-byte access of 16 lanes
+// is served from a 256-byte or (8 lanes) from a 128-byte window:
+// the 16-byte unit of row r of a 128-byte-row tile is XORed with asw(r),
+// the unit (0/1) of column n of the 32-byte-unit B slice with bsw(n).
+__device__ __forceinline__ int asw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int bsw(int n) { return ((n >> 2) ^ (n >> 3)) & 1; }
 
-template <class T, int BN, bool MASK, int kDepth>
-__global__ __launch_bounds__(kNnWaves * 64) void gemm_nn(AOperand<T> A, const T* __restrict__ Bp, int64_t Kt,
-                                                         int64_t N, int64_t n_nblk, int64_t n_mgroups,
-                                                         int64_t n_mblk, EpiT<T> e) {
+// Two fp32 values as packed bf16 (round to nearest even, one instruction).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const f32x2_t v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+template <class T, int BN, bool MASK, int PD>
+__global__ __launch_bounds__(kNnWaves * 64, 1) void gemm_nn(AOperand<T> A, const T* __restrict__ Bp, int64_t Kt,
+                                                             int64_t N, int64_t n_nblk, int64_t n_mgroups,
+                                                             int64_t n_blk, EpiT<T> e,
+                                                             const float* __restrict__ bias) {
     extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
-    // B slice of this column block as [k-step][BN][KSTEP]: the fragment of
-    // column block j of a k-step sits at a fixed offset, an immediate.
-    T* Bs = reinterpret_cast<T*>(lds_raw);
-    constexpr int V = Vec<T>::N;
+    constexpr int V = Vec<T>::N;                  // elements per 16-byte unit
+    constexpr int CKE = 128 / static_cast<int>(sizeof(T));   // elements per chunk (4 k-steps)
     constexpr int NB = BN / 32;
-    constexpr int KSTEP = StreamMfma<T>::KSTEP;
-    constexpr int KSV = KSTEP / V;                  // vectors per k-step
+    constexpr int LPR = kNnRows / 8;              // loads per lane per chunk
+    // epilogue groups: 64 columns of bf16 or 32 of fp32 make one 128-byte row
+    constexpr int GB = (sizeof(T) == 2 && NB % 2 == 0) ? 2 : 1;   // 32-column blocks per group
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int rr = lane >> 3, u = lane & 7;       // chunk load: sub-row, 16-byte unit
     const int64_t tile = xcd_tile(blockIdx.x, gridDim.x);
     const int64_t nb = tile % n_nblk, mg = tile / n_nblk;
     const int64_t n0 = nb * BN;
-    const int64_t kvec = Kt / V;
-    for (int64_t q = threadIdx.x; q < BN * kvec; q += kNnWaves * 64) {
-        const int64_t r = q / kvec, c = q % kvec;   // column r, vector c
-        const int64_t ks = c / KSV, w = c % KSV;
-        *reinterpret_cast<uint4*>(Bs + (ks * BN + r) * KSTEP + w * V) =
-            *reinterpret_cast<const uint4*>(Bp + (n0 + r) * Kt + c * V);
+    unsigned char* Bs = lds_raw;                  // [k-step][BN] 32-byte units
+    unsigned char* At = lds_raw + static_cast<size_t>(BN) * Kt * sizeof(T) + wave * kNnTile;
+    {
+        // unit w (0/1) of k-step ks of column n sits at (ks*BN + n)*32 + 16*(w ^ bsw(n))
+        const int64_t kvec = Kt / V;
+        for (int64_t q = threadIdx.x; q < BN * kvec; q += kNnWaves * 64) {
+            const int64_t n = q / kvec, c = q % kvec;
+            const int64_t ks = c >> 1, w = c & 1;
+            *reinterpret_cast<uint4*>(Bs + (ks * BN + n) * 32 + ((w ^ bsw(static_cast<int>(n))) << 4)) =
+                *reinterpret_cast<const uint4*>(Bp + (n0 + n) * Kt + c * V);
+        }
     }
-    // the bias of the block's columns sits after B, so the epilogue never
-    // waits on global memory behind the prefetched fragments
-    float* bias_lds = reinterpret_cast<float*>(lds_raw + static_cast<size_t>(BN) * Kt * sizeof(T));
-    for (int q = threadIdx.x; q < BN; q += kNnWaves * 64)
-        bias_lds[q] = (e.bias && n0 + q < N) ? e.bias[n0 + q] : 0.f;
     __syncthreads();
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t stride = n_mgroups * kNnWaves;
-    int64_t mb = mg * kNnWaves + wave;
-    if (mb >= n_mblk) return;
-    const int nks = static_cast<int>(Kt / KSTEP);   // a multiple of kDepth
-    const int nks1 = static_cast<int>(A.k1p / KSTEP);                // k-steps of block 1
-    // the only k-steps whose fragments need zeroing: the ragged end of block 1
-    // and everything from the ragged end of block 2 on
-    const int fix1 = A.k1 < A.k1p ? static_cast<int>(A.k1 / KSTEP) : -1;
-    const int fix2 = static_cast<int>((A.k1p + A.k2) / KSTEP);
-    const int koff = (lane / 32) * (KSTEP / 2);
-    const int64_t rl = lane % 32;
-    // per-lane bases: row of this block (and the next), shifted by the lane's
-    // half of the k-step; the k-step offset is a uniform scalar
-    auto bases = [&](int64_t blk, const T*& b1, const T*& b2, const T*& bm) {
-        const T *p1, *p2;
-        A.row_ptrs(blk * 32 + rl, p1, p2);
-        b1 = p1 + koff;
-        b2 = p2 + koff - A.k1p;   // block 2 addressed with the virtual column
-        if constexpr (MASK) {
-            const int64_t r = blk * 32 + rl;
-            bm = A.mask + (r < A.M ? r : A.M - 1) * A.ldmask + koff;
-        }
-    };
-    // last 16-byte vector of each block inside its rows (a block's k-step
-    // padding may reach past the row's leading dimension)
+    int64_t b = mg * kNnWaves + wave;
+    if (b >= n_blk) return;
+    const int nch = static_cast<int>(Kt / CKE);   // a multiple of PD
+    const int nc1 = static_cast<int>(A.k1p / CKE);
     const int64_t last1 = (A.k1 + V - 1) / V * V - V, last2 = (A.k2 + V - 1) / V * V - V;
-    auto frag_ptr = [&](const T* b1, const T* b2, int ks) -> const uint4* {
-        const T* p;
-        if (ks == fix1 || ks >= fix2) {
-            // edge or past the data (the value is zeroed at use): clamp the
-            // lane's column into the block's real vectors
-            const int64_t col = static_cast<int64_t>(ks) * KSTEP + koff;
-            if (col < A.k1p || !A.a2) {
-                const int64_t c = col < last1 ? col : last1;
-                p = b1 - koff + c;
-            } else {
-                const int64_t c2 = col - A.k1p;
-                p = b2 - koff + A.k1p + (c2 < last2 ? c2 : last2);
+    const int64_t m1c = A.m1 > 0 ? A.m1 - 1 : 0, mc = A.M - 1;
+    // source of chunk c: block 1 for c < nc1, else block 2 (or, past both
+    // blocks, block 1 clamped: read and then zeroed)
+    struct Src {
+        const T* base;
+        int64_t ld, lim, col;
+    };
+    auto src_of = [&](int c) -> Src {
+        Src s;
+        const bool p1 = c < nc1 || !A.a2;
+        const int64_t cc = static_cast<int64_t>(p1 ? c : c - nc1) * CKE + u * V;
+        const int64_t last = p1 ? last1 : last2;
+        s.base = p1 ? A.a1 : A.a2;
+        s.ld = p1 ? A.lda1 : A.lda2;
+        s.lim = p1 ? m1c : mc;
+        s.col = cc < last ? cc : last;
+        return s;
+    };
+    uint4 ra[PD][LPR], rm[MASK ? PD : 1][LPR];
+    auto issue = [&](auto slot_c, int64_t blk, int c) {
+        constexpr int slot = decltype(slot_c)::value;
+        const Src s = src_of(c);
+        const int64_t row0 = blk * kNnRows + rr;
+        // the mask of a chunk past block 1 is read (clamped) but not used
+        const int64_t mcol = s.col < last1 ? s.col : last1;
+#pragma unroll
+        for (int i = 0; i < LPR; ++i) {
+            const int64_t r = row0 + 8 * i < s.lim ? row0 + 8 * i : s.lim;
+            ra[slot][i] = *reinterpret_cast<const uint4*>(s.base + r * s.ld + s.col);
+            if constexpr (MASK) {
+                const int64_t rmk = row0 + 8 * i < m1c ? row0 + 8 * i : m1c;
+                rm[slot][i] = *reinterpret_cast<const uint4*>(A.mask + rmk * A.ldmask + mcol);
             }
-        } else {
-            p = ks < nks1 ? b1 + ks * KSTEP : b2 + ks * KSTEP;
         }
-        return reinterpret_cast<const uint4*>(p);
     };
-    auto mask_ptr = [&](const T* bm_, int ks) -> const uint4* {
-        const int64_t col = static_cast<int64_t>(ks) * KSTEP + koff;
-        const int64_t c = col < last1 ? col : last1;
-        return reinterpret_cast<const uint4*>(bm_ - koff + c);
-    };
-    uint4 buf[kDepth], mbuf[MASK ? kDepth : 1];
-    const T *b1, *b2, *bm = nullptr, *c1, *c2, *cm = nullptr;
-    bases(mb, b1, b2, bm);
-    static_for<0, kDepth>([&](auto dc) {
-        constexpr int d = decltype(dc)::value;
-        buf[d] = *frag_ptr(b1, b2, d);
-        if constexpr (MASK) mbuf[d] = *mask_ptr(bm, d);
-    });
+    // fragment read offsets: A row l32, unit 2s + h; B column l32 of a block, unit h
+    int aoff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) aoff[s] = l32 * 128 + (((2 * s + h) ^ asw(l32)) << 4);
+    const int boff = l32 * 32 + ((h ^ bsw(l32)) << 4);
+    static_for<0, PD>([&](auto sc) { issue(sc, b, decltype(sc)::value); });
     for (;;) {
         f32x16_t acc[NB];
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
-        const int64_t mb_next = mb + stride;
-        bases(mb_next, c1, c2, cm);
-        // rows of this block at or past m1 (or M) read block 1 as zero
-        const bool zero_rows = mb * 32 + 31 >= A.m1;
-        for (int ks0 = 0; ks0 < nks; ks0 += kDepth) {
-            static_for<0, kDepth>([&](auto dc) {
-                constexpr int d = decltype(dc)::value;
-                const int ks = ks0 + d;
-                uint4 a = buf[d];
-                if constexpr (MASK) {
-                    if (ks < nks1) a = apply_mask<T>(a, mbuf[d]);
+        const int64_t b_next = b + stride;
+        const int64_t b_end = b * kNnRows + kNnRows;
+        const bool edge_rows = b_end > A.M || (A.a1 && b_end > A.m1);
+        for (int c0 = 0; c0 < nch; c0 += PD) {
+            static_for<0, PD>([&](auto sc) {
+                constexpr int slot = decltype(sc)::value;
+                const int c = c0 + slot;
+                const bool p1 = c < nc1 || !A.a2;
+                const int64_t kpart = p1 ? A.k1 : A.k2;
+                const int64_t cc = static_cast<int64_t>(p1 ? c : c - nc1) * CKE;
+                const bool edge_k = cc + CKE > kpart;
+#pragma unroll
+                for (int i = 0; i < LPR; ++i) {
+                    uint4 v = ra[slot][i];
+                    if constexpr (MASK) {
+                        if (c < nc1) v = apply_mask<T>(v, rm[slot][i]);
+                    }
+                    if (edge_rows || edge_k) {
+                        const int64_t row = b * kNnRows + 8 * i + rr;
+                        const bool ok = row < A.M && (!p1 || !A.a1 || row < A.m1);
+                        v = sel(ok, keep_first<T>(v, static_cast<int>(kpart - cc - u * V)), make_uint4(0, 0, 0, 0));
+                    }
+                    *reinterpret_cast<uint4*>(At + (8 * i + rr) * 128 + ((u ^ asw(8 * i + rr)) << 4)) = v;
                 }
-                if (zero_rows || ks == fix1 || ks >= fix2)
-                    a = A.fix(a, mb * 32 + rl, static_cast<int64_t>(ks) * KSTEP + koff);
-                int kn = ks + kDepth;
-                const T *r1 = b1, *r2 = b2, *rm = bm;
-                if (kn >= nks) {
-                    kn -= nks;
-                    r1 = c1;
-                    r2 = c2;
-                    rm = cm;
+                int cn = c + PD;
+                int64_t bn = b;
+                if (cn >= nch) {
+                    cn -= nch;
+                    bn = b_next;
                 }
-                buf[d] = *frag_ptr(r1, r2, kn);
-                if constexpr (MASK) mbuf[d] = *mask_ptr(rm, kn);
-                StreamMfma<T>::template step<NB>(a, Bs + static_cast<int64_t>(ks) * BN * KSTEP, lane, acc);
+                issue(sc, bn, cn);
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    const uint4 a = *reinterpret_cast<const uint4*>(At + aoff[s]);
+                    const unsigned char* bk = Bs + static_cast<int64_t>(c * 4 + s) * BN * 32 + boff;
+#pragma unroll
+                    for (int j = 0; j < NB; ++j) {
+                        const uint4 bv = *reinterpret_cast<const uint4*>(bk + j * 32 * 32);
+                        if constexpr (sizeof(T) == 2) {
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, bv),
+                                                                              __builtin_bit_cast(bf16x8_t, a),
+                                                                              acc[j], 0, 0, 0);
+                        } else {
+                            const f32x4_t bb = __builtin_bit_cast(f32x4_t, bv);
+                            const f32x4_t aa = __builtin_bit_cast(f32x4_t, a);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(bb[q], aa[q], acc[j], 0, 0, 0);
+                        }
+                    }
+                }
             });
         }
-        // epilogue: lane l holds row l%32 of the block; register quad q of
-        // column block j holds columns j*32 + 8q + 4(l/32) .. +3
-        const int64_t row = mb * 32 + rl;
-        if (row < A.M) {
+        // ---- epilogue: per group of GB column blocks, bias (+ addend), then
+        // Y_pre and/or the (ReLU'd) output through the tile as whole rows
+        const int64_t row = b * kNnRows + l32;
 #pragma unroll
-            for (int j = 0; j < NB; ++j) {
+        for (int g = 0; g < NB / GB; ++g) {
+            float y[GB][4][4];
+#pragma unroll
+            for (int jj = 0; jj < GB; ++jj) {
+                const int j = g * GB + jj;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
-                    const int64_t cl = j * 32 + 8 * q + 4 * (lane / 32);
-                    const int64_t col = n0 + cl;
-                    if (col >= N) continue;
-                    const int n = static_cast<int>(N - col < 4 ? N - col : 4);
-                    float y[4];
+                    const int64_t cb = n0 + j * 32 + 8 * q;   // uniform: columns cb + 4h + t
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) y[t] = acc[j][4 * q + t] + bias_lds[cl + t];
+                    for (int t = 0; t < 4; ++t) {
+                        float bv = 0.f;
+                        if (bias) {
+                            const float lo = cb + t < N ? bias[cb + t] : 0.f;
+                            const float hi = cb + 4 + t < N ? bias[cb + 4 + t] : 0.f;
+                            bv = h ? hi : lo;
+                        }
+                        y[jj][q][t] = acc[j][4 * q + t] + bv;
+                    }
                     if (e.add && row < e.n_add) {
+                        const int64_t col = cb + 4 * h;
 #pragma unroll
                         for (int t = 0; t < 4; ++t)
-                            if (t < n) y[t] += to_f32(e.add[row * e.ld_add + col + t]);
+                            if (col + t < N) y[jj][q][t] += to_f32(e.add[row * e.ld_add + col + t]);
                     }
-                    if (e.pre) store4<T>(e.pre + row * e.ldc + col, y, n);
+                }
+            }
+            const int64_t gc0 = n0 + g * GB * 32;       // first column of the group
+            // two passes when Y_pre is wanted: pre-activation, then output
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                T* dst;
+                if (pass == 0) {
+                    if (!e.pre) continue;
+                    dst = e.pre;
+                } else {
+                    dst = e.c;
                     if (e.relu) {
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) y[t] = y[t] < 0.f ? 0.f : y[t];
+                        for (int jj = 0; jj < GB; ++jj)
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                                for (int t = 0; t < 4; ++t) y[jj][q][t] = y[jj][q][t] < 0.f ? 0.f : y[jj][q][t];
                     }
-                    store4<T>(e.c + row * e.ldc + col, y, n);
+                }
+                // stage: row l32, columns jj*32 + 8q + 4h .. +3 of the group
+#pragma unroll
+                for (int jj = 0; jj < GB; ++jj) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (sizeof(T) == 2) {
+                            const uint32_t lo = pack_bf16x2(y[jj][q][0], y[jj][q][1]);
+                            const uint32_t hi = pack_bf16x2(y[jj][q][2], y[jj][q][3]);
+                            const int w = jj * 4 + q;     // 16-byte unit of the 128-byte row
+                            *reinterpret_cast<uint2*>(At + l32 * 128 + ((w ^ asw(l32)) << 4) + h * 8) =
+                                make_uint2(lo, hi);
+                        } else {
+                            const int w = 2 * q + h;
+                            *reinterpret_cast<float4*>(At + l32 * 128 + ((w ^ asw(l32)) << 4)) =
+                                make_float4(y[jj][q][0], y[jj][q][1], y[jj][q][2], y[jj][q][3]);
+                        }
+                    }
+                }
+                // whole rows back out: lane -> row 8i + rr, unit u
+                constexpr int UNITS = GB * 32 * static_cast<int>(sizeof(T)) / 16;   // 16-byte units per row
+#pragma unroll
+                for (int i = 0; i < LPR; ++i) {
+                    const int r = 8 * i + rr;
+                    const int64_t grow = b * kNnRows + r;
+                    if (u >= UNITS) continue;
+                    const uint4 v = *reinterpret_cast<const uint4*>(At + r * 128 + ((u ^ asw(r)) << 4));
+                    const int64_t col = gc0 + u * V;
+                    if (grow >= A.M || col >= N) continue;
+                    T* p = dst + grow * e.ldc + col;
+                    if (col + V <= N) {
+                        *reinterpret_cast<uint4*>(p) = v;
+                    } else {
+                        const int n = static_cast<int>(N - col);
+                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+                        for (int t = 0; t < n; ++t) {
+                            if constexpr (sizeof(T) == 2)
+                                p[t] = static_cast<T>((t & 1) ? (wv[t / 2] >> 16) : (wv[t / 2] & 0xffffu));
+                            else
+                                p[t] = __uint_as_float(wv[t]);
+                        }
+                    }
                 }
             }
         }
-        mb = mb_next;
-        if (mb >= n_mblk) break;
-        b1 = c1;
-        b2 = c2;
-        bm = cm;
+        b = b_next;
+        if (b >= n_blk) break;
     }
 }
 
@@ -757,57 +826,69 @@ size_t max_lds_per_block() {
     return lds;
 }
 
-template <class T, int BN, bool MASK, int D>
-sag_status launch_nn_d(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e, hipStream_t s) {
-    const size_t lds = static_cast<size_t>(BN) * Kt * sizeof(T) + BN * sizeof(float);
+template <class T, int BN, bool MASK, int PD>
+sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e,
+                     const float* bias, hipStream_t s) {
+    const size_t lds = static_cast<size_t>(BN) * Kt * sizeof(T) + static_cast<size_t>(kNnWaves) * kNnTile;
     static bool attr_set = false;
     if (!attr_set) {
-        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK, D>),
+        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK, PD>),
                                           hipFuncAttributeMaxDynamicSharedMemorySize,
                                           static_cast<int>(max_lds_per_block())));
         attr_set = true;
     }
     const int64_t n_nblk = cdiv(N, BN);
-    const int64_t n_mblk = cdiv(ao.M, 32);
+    const int64_t n_blk = cdiv(ao.M, kNnRows);
     int64_t n_mgroups = device_cus() / n_nblk;
     if (n_mgroups < 1) n_mgroups = 1;
-    const int64_t need = cdiv(n_mblk, kNnWaves);
+    const int64_t need = cdiv(n_blk, kNnWaves);
     if (n_mgroups > need) n_mgroups = need;
-    gemm_nn<T, BN, MASK, D><<<dim3(static_cast<unsigned>(n_nblk * n_mgroups)), kNnWaves * 64, lds, s>>>(
-        ao, B, Kt, N, n_nblk, n_mgroups, n_mblk, e);
+    gemm_nn<T, BN, MASK, PD><<<dim3(static_cast<unsigned>(n_nblk * n_mgroups)), kNnWaves * 64, lds, s>>>(
+        ao, B, Kt, N, n_nblk, n_mgroups, n_blk, e, bias);
     SAG_LAUNCH_CHECK();
     return SAG_OK;
 }
 
-template <class T, int BN, bool MASK>
-sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e, hipStream_t s) {
-    const int64_t nks = Kt / StreamMfma<T>::KSTEP;
-    if (nks % 16 == 0) return launch_nn_d<T, BN, MASK, 16>(ao, B, Kt, N, e, s);
-    return launch_nn_d<T, BN, MASK, 8>(ao, B, Kt, N, e, s);
+// Chunks in flight: four where the registers allow (no mask; fp32 only
+// below 128 columns), else two.
+template <class T, int BN>
+sag_status launch_nn_bn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e,
+                        const float* bias, hipStream_t s) {
+    const bool pd4 = (Kt / (128 / static_cast<int64_t>(sizeof(T)))) % 4 == 0;
+    if (ao.mask) {
+        if constexpr (sizeof(T) == 4 && BN == 128)
+            return fail(SAG_E_UNSUPPORTED, "gemm: no fp32 masked kernel for 128 columns");
+        else
+            return launch_nn<T, BN, true, 2>(ao, B, Kt, N, e, bias, s);
+    }
+    if constexpr (sizeof(T) == 4 && BN == 128) return launch_nn<T, BN, false, 2>(ao, B, Kt, N, e, bias, s);
+    else
+        return pd4 ? launch_nn<T, BN, false, 4>(ao, B, Kt, N, e, bias, s)
+                   : launch_nn<T, BN, false, 2>(ao, B, Kt, N, e, bias, s);
+}
+
+// LDS bytes the NN kernel needs for a column block of bn over Kt.
+inline size_t nn_lds_bytes(int64_t bn, int64_t Kt, sag_dtype dt) {
+    return static_cast<size_t>(bn) * Kt * elt_size(dt) + static_cast<size_t>(kNnWaves) * kNnTile;
 }
 
 template <class T>
 sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dtype dt, void* C, int64_t ldc,
                     const Epilogue& epi, hipStream_t s) {
-    AOperand<T> ao = make_aop<T>(A, M, dt, Bp, kstep(dt));
+    AOperand<T> ao = make_aop<T>(A, M, dt, Bp, kchunk(dt));
     const int64_t Kt = k_total(A.a1 ? A.k1 : 0, A.a2 ? A.k2 : 0, dt);
     EpiT<T> e{static_cast<T*>(C), ldc, static_cast<T*>(epi.pre), static_cast<const T*>(epi.addend),
               epi.ld_add, epi.addend ? epi.n_add : 0, epi.bias, epi.relu};
     const T* B = static_cast<const T*>(Bp);
-    // widest N block whose slice of B fits in LDS
+    // widest column block whose slice of B fits in LDS beside the tiles
     const size_t lds = max_lds_per_block();
     const int64_t n32 = round_up(N, 32);
-    const size_t row = static_cast<size_t>(Kt) * sizeof(T) + sizeof(float);
-    // (a 256-column block would need more than the 256 registers a lane has
-    // at two wavefronts per SIMD; the column blocks of one row group run on
-    // the same XCD, so A is read from HBM about once)
-    const bool m = ao.mask != nullptr;
-    if (n32 >= 128 && 128 * row <= lds)
-        return m ? launch_nn<T, 128, true>(ao, B, Kt, N, e, s) : launch_nn<T, 128, false>(ao, B, Kt, N, e, s);
-    if (n32 >= 64 && 64 * row <= lds)
-        return m ? launch_nn<T, 64, true>(ao, B, Kt, N, e, s) : launch_nn<T, 64, false>(ao, B, Kt, N, e, s);
-    if (32 * row <= lds)
-        return m ? launch_nn<T, 32, true>(ao, B, Kt, N, e, s) : launch_nn<T, 32, false>(ao, B, Kt, N, e, s);
+    // (fp32 with a mask stays at 64 columns: 128 would spill registers)
+    const bool w128 = !(sizeof(T) == 4 && ao.mask);
+    if (w128 && n32 >= 128 && nn_lds_bytes(128, Kt, dt) <= lds)
+        return launch_nn_bn<T, 128>(ao, B, Kt, N, e, epi.bias, s);
+    if (n32 >= 64 && nn_lds_bytes(64, Kt, dt) <= lds) return launch_nn_bn<T, 64>(ao, B, Kt, N, e, epi.bias, s);
+    if (nn_lds_bytes(32, Kt, dt) <= lds) return launch_nn_bn<T, 32>(ao, B, Kt, N, e, epi.bias, s);
     return fail(SAG_E_UNSUPPORTED, "gemm: K too large for one LDS-resident slice of B");
 }
 
@@ -889,9 +970,9 @@ sag_status pack_b(const PackSrc& src, int64_t k1, int64_t k2, const NLayout& nl,
                      s, elt_size(dt) * ((k1 + k2) * nl.total() + total), 0);
     const dim3 grid(static_cast<unsigned>(cdiv(total, 256)));
     if (dt == SAG_BF16)
-        pack_kernel<uint16_t><<<grid, 256, 0, s>>>(src, k1, kpn(k1, dt), k2, Kt, nl, n_pad, static_cast<uint16_t*>(Bp));
+        pack_kernel<uint16_t><<<grid, 256, 0, s>>>(src, k1, kpc(k1, dt), k2, Kt, nl, n_pad, static_cast<uint16_t*>(Bp));
     else
-        pack_kernel<float><<<grid, 256, 0, s>>>(src, k1, kpn(k1, dt), k2, Kt, nl, n_pad, static_cast<float*>(Bp));
+        pack_kernel<float><<<grid, 256, 0, s>>>(src, k1, kpc(k1, dt), k2, Kt, nl, n_pad, static_cast<float*>(Bp));
     SAG_LAUNCH_CHECK();
     return SAG_OK;
 }
@@ -969,8 +1050,8 @@ sag_status check_gemm_a(const char* who, int64_t M, const void* A1, int64_t lda1
 extern "C" size_t sag_gemm_workspace_bytes(int64_t M, int64_t K, int64_t N, sag_dtype dt) {
     (void)M;
     if (K < 0 || N < 0) return 0;
-    // two K blocks pad K by at most two vectors
-    return packed_b_bytes(K + 2 * vec_elems(dt), 0, N, dt);
+    // two K blocks pad K by less than two chunks
+    return packed_b_bytes(K + 2 * kchunk(dt), 0, N, dt);
 }
 
 extern "C" sag_status sag_gemm(int64_t M, int64_t N, const void* A1, int64_t lda1, int64_t K1, const void* A2,
