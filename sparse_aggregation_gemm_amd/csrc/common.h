@@ -74,12 +74,12 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
     return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// Round to nearest even, NaN to a quiet NaN, in one hardware conversion
+// (on every fp32 bit pattern the same bits as the rounding written out:
+// add 0x7fff plus the kept low bit, keep the high half, set the quiet bit
+// of a NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -187,30 +187,6 @@ AOperand<T> make_aop(const GemmA& A, int64_t M, sag_dtype dt, const void* safe, 
     return o;
 }
 
-// MFMA traits: k per instruction and fragment loads from LDS rows with k
-// contiguous.
-template <class T> struct Mfma;
-template <> struct Mfma<uint16_t> {
-    static constexpr int KI = 16;   // k per instruction
-    using frag = bf16x8_t;
-    __device__ static __forceinline__ frag ld(const uint16_t* row, int k) {
-        return *reinterpret_cast<const bf16x8_t*>(row + k + (threadIdx.x & 63) / 32 * 8);
-    }
-    __device__ static __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
-};
-template <> struct Mfma<float> {
-    static constexpr int KI = 2;
-    using frag = float;
-    __device__ static __forceinline__ frag ld(const float* row, int k) {
-        return row[k + (threadIdx.x & 63) / 32];
-    }
-    __device__ static __forceinline__ f32x16_t mma(frag a, frag b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-    }
-};
-
 // Workgroup id -> logical tile id with the tiles of one XCD contiguous
 // (workgroups are dealt to the 8 XCDs round-robin).
 __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t total) {
@@ -529,38 +505,51 @@ __global__ __launch_bounds__(kNnWaves * 64, 1) void gemm_nn(AOperand<T> A, const
 // ---- TN (weight gradient) -----------------------------------------------------------
 // C[k, n] = sum over a chunk of rows m of A[m, k] B[m, n].  Tile: KT rows of C
 // (K up to 512 in one tile) by BNT columns; 8 wavefronts, WK along K by WN
-// along N.  Each step stages MS rows of A and B in LDS; for bf16 they are
-// stored transposed (k-major, m contiguous) because the MFMA reduction runs
-// over m, with each thread writing 4 consecutive m values at once.
+// along N, each owning a 64 x TNW block of C.  Steps of 32 rows of A and B
+// are copied row-major into padded LDS tiles by whole-line loads (two steps
+// in flight in registers, one barrier per step); the MFMA reduction runs
+// over m, so bf16 operands are read with the LDS transpose load: for four
+// consecutive rows and sixteen columns, lane i of a 16-lane group receives
+// column i of the four rows.  Two such reads give a lane the eight m values
+// of its column that one 32x32x16 MFMA takes.  fp32 operands (one m per
+// lane half) are plain reads.  The column sums of B (the bias gradient) are
+// kept in the registers that load B.  The tiles of one row chunk run on the
+// same XCD, so the rows they share are read from HBM once.
 constexpr int kTnThreads = 512;
+constexpr int kTnRows = 32;                       // rows per step
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+
+template <class T> constexpr int tn_pad() { return sizeof(T) == 2 ? 64 : 128; }   // bytes after each LDS row
+template <class T, int KT, int BNT> constexpr int tn_stage_bytes() {
+    return kTnRows * (KT * static_cast<int>(sizeof(T)) + tn_pad<T>()) +
+           kTnRows * (BNT * static_cast<int>(sizeof(T)) + tn_pad<T>());
+}
 
 template <class T, int KT, int BNT>
-__global__ __launch_bounds__(kTnThreads) void gemm_tn(AOperand<T> A, const T* __restrict__ B, int64_t ldb,
-                                                      const T* __restrict__ mask, int64_t ldmask, int64_t N,
-                                                      int64_t n_ktile, int64_t n_ntile, int64_t rows_per_chunk,
-                                                      float* __restrict__ part, int64_t ldp_k, int64_t ldp_n,
-                                                      float* __restrict__ part_cs) {
+__global__ __launch_bounds__(kTnThreads, 1) void gemm_tn(AOperand<T> A, const T* __restrict__ B, int64_t ldb,
+                                                         const T* __restrict__ mask, int64_t ldmask, int64_t N,
+                                                         int64_t n_ktile, int64_t n_ntile, int64_t rows_per_chunk,
+                                                         float* __restrict__ part, int64_t ldp_k, int64_t ldp_n,
+                                                         float* __restrict__ part_cs) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
     constexpr bool kBf16 = sizeof(T) == 2;
+    constexpr int ES = static_cast<int>(sizeof(T));
     constexpr int V = Vec<T>::N;
-    constexpr int KI = Mfma<T>::KI;
-    constexpr int MS = kBf16 ? 32 : 16;               // rows per step
+    constexpr int PA = KT * ES + tn_pad<T>(), PB = BNT * ES + tn_pad<T>();    // LDS row pitches
+    constexpr int SA = kTnRows * PA;
+    constexpr int STAGE = tn_stage_bytes<T, KT, BNT>();
     constexpr int WK = KT / 64, WN = 8 / WK;
-    constexpr int TK = KT / WK, TNW = BNT / WN;       // wave tile
-    constexpr int NBK = TK / 32, NBN = TNW / 32;
+    constexpr int TNW = BNT / WN;                     // wave tile: 64 x TNW
+    constexpr int NBK = 2, NBN = TNW / 32;
     static_assert(TNW >= 32 && TNW % 32 == 0, "wave tile too narrow");
-    constexpr int LPA = kBf16 ? MS + 8 : KT + 4;
-    constexpr int LPB = kBf16 ? MS + 8 : BNT + 4;
-    constexpr int SA = kBf16 ? KT * LPA : MS * LPA;
-    constexpr int SB = kBf16 ? BNT * LPB : MS * LPB;
-    __shared__ __attribute__((aligned(16))) T As[SA];
-    __shared__ __attribute__((aligned(16))) T Bs[SB];
-    constexpr int ITEMS_A = (MS / 4) * (KT / V);      // 4 rows x one vector each
-    constexpr int ITEMS_B = (MS / 4) * (BNT / V);
-    static_assert(ITEMS_A <= kTnThreads && ITEMS_B <= kTnThreads, "too many items");
+    constexpr int UPA = KT / V, UPB = BNT / V;        // 16-byte units per row
+    constexpr int NA = kTnRows * UPA, NBU = kTnRows * UPB;
+    constexpr int UA = (NA + kTnThreads - 1) / kTnThreads, UB = (NBU + kTnThreads - 1) / kTnThreads;
 
     const int64_t tiles = n_ktile * n_ntile;
-    const int64_t chunk = blockIdx.x / tiles;
-    const int64_t tt = blockIdx.x % tiles;
+    const int64_t logical = xcd_tile(blockIdx.x, gridDim.x);
+    const int64_t chunk = logical / tiles, tt = logical % tiles;
     const int64_t k0 = (tt / n_ntile) * KT;
     const int64_t n0 = (tt % n_ntile) * BNT;
     const int64_t m_begin = chunk * rows_per_chunk;
@@ -569,94 +558,93 @@ __global__ __launch_bounds__(kTnThreads) void gemm_tn(AOperand<T> A, const T* __
     const int lane = t & 63, wave = t >> 6;
     const int wk = wave % WK, wn = wave / WK;
     const bool do_cs = part_cs && k0 == 0;
-    // item of this thread: rows 4*rq .. 4*rq+3 of the step, one vector column
-    const int a_rq = t % (MS / 4), a_cv = t / (MS / 4);
-    const int b_rq = t % (MS / 4), b_cv = t / (MS / 4);
+    const int64_t lastn = (N + V - 1) / V * V - V;    // last 16-byte unit of a B row
 
-    // raw loads are issued a step ahead; zeroing and masking happen when the
-    // step is written to LDS
-    uint4 ra[4], rb[4], rm[4];
-    int64_t step_m0 = m_begin;
-    auto load_step = [&](int64_t m0) {
-        if (t < ITEMS_A) {
+    // the A units of this thread keep their column for the whole kernel:
+    // source pointer at that column, row pitch and the first row that reads
+    // as zero (m1 for block 1, M for block 2, 0 past both blocks)
+    const T* abase[UA];
+    int64_t ald[UA], alim[UA];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + a_rq * 4 + i;
-                ra[i] = *A.addr(row < m_end ? row : A.M, k0 + a_cv * V);
-            }
-        }
-        if (t < ITEMS_B) {
-            const int64_t col = n0 + b_cv * V;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = m0 + b_rq * 4 + i;
-                const bool ok = row < m_end && col < N;
-                rb[i] = *reinterpret_cast<const uint4*>(ok ? B + row * ldb + col : B);
-                if (mask) rm[i] = *reinterpret_cast<const uint4*>(ok ? mask + row * ldmask + col : mask);
-            }
-        }
-    };
-    auto fix_step = [&]() {
-        if (t < ITEMS_A) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = step_m0 + a_rq * 4 + i;
-                ra[i] = row < m_end ? A.fix(ra[i], row, k0 + a_cv * V) : make_uint4(0, 0, 0, 0);
-            }
-        }
-        if (t < ITEMS_B) {
-            const int64_t col = n0 + b_cv * V;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t row = step_m0 + b_rq * 4 + i;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (row < m_end && col < N) {
-                    v = keep_first<T>(rb[i], static_cast<int>(N - col));
-                    if (mask) v = apply_mask<T>(v, rm[i]);
-                }
-                rb[i] = v;
-            }
-        }
-    };
-    auto store_step = [&]() {
-        fix_step();
-        if constexpr (kBf16) {
-            // transpose: element (m, k) goes to As[k][m]; 4 m values per write
-            if (t < ITEMS_A) {
-                const uint32_t w0[4] = {ra[0].x, ra[0].y, ra[0].z, ra[0].w};
-                const uint32_t w1[4] = {ra[1].x, ra[1].y, ra[1].z, ra[1].w};
-                const uint32_t w2[4] = {ra[2].x, ra[2].y, ra[2].z, ra[2].w};
-                const uint32_t w3[4] = {ra[3].x, ra[3].y, ra[3].z, ra[3].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // halves e of rows m, m+1 (and m+2, m+3) side by side
-                    const uint32_t sel_b = (e & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t lo = __builtin_amdgcn_perm(w1[e / 2], w0[e / 2], sel_b);
-                    const uint32_t hi = __builtin_amdgcn_perm(w3[e / 2], w2[e / 2], sel_b);
-                    *reinterpret_cast<uint2*>(&As[(a_cv * 8 + e) * LPA + a_rq * 4]) = make_uint2(lo, hi);
-                }
-            }
-            if (t < ITEMS_B) {
-                const uint32_t w0[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
-                const uint32_t w1[4] = {rb[1].x, rb[1].y, rb[1].z, rb[1].w};
-                const uint32_t w2[4] = {rb[2].x, rb[2].y, rb[2].z, rb[2].w};
-                const uint32_t w3[4] = {rb[3].x, rb[3].y, rb[3].z, rb[3].w};
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t sel_b = (e & 1) ? 0x07060302u : 0x05040100u;
-                    const uint32_t lo = __builtin_amdgcn_perm(w1[e / 2], w0[e / 2], sel_b);
-                    const uint32_t hi = __builtin_amdgcn_perm(w3[e / 2], w2[e / 2], sel_b);
-                    *reinterpret_cast<uint2*>(&Bs[(b_cv * 8 + e) * LPB + b_rq * 4]) = make_uint2(lo, hi);
-                }
-            }
+    for (int j = 0; j < UA; ++j) {
+        const int q = t + j * kTnThreads;
+        const int64_t kv = k0 + (q % UPA) * V;
+        const int64_t last1 = (A.k1 + V - 1) / V * V - V, last2 = (A.k2 + V - 1) / V * V - V;
+        if (A.a1 && kv < A.k1p) {
+            abase[j] = A.a1 + (kv < last1 ? kv : last1);
+            ald[j] = A.lda1;
+            alim[j] = A.m1;
+        } else if (A.a2 && kv < A.k1p + A.k2p) {
+            abase[j] = A.a2 + (kv - A.k1p < last2 ? kv - A.k1p : last2);
+            ald[j] = A.lda2;
+            alim[j] = A.M;
         } else {
-            if (t < ITEMS_A) {
+            abase[j] = A.safe;
+            ald[j] = 0;
+            alim[j] = 0;
+        }
+    }
+    uint4 ra[2][UA], rb[2][UB], rm[2][UB];
+    auto load = [&](auto buf_c, int64_t m0) {
+        constexpr int bsel = decltype(buf_c)::value;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&As[(a_rq * 4 + i) * LPA + a_cv * V]) = ra[i];
+        for (int j = 0; j < UA; ++j) {
+            const int q = t + j * kTnThreads;
+            if (q < NA) {
+                const int64_t row = m0 + q / UPA;
+                const int64_t rc = row < alim[j] ? row : (alim[j] > 0 ? alim[j] - 1 : 0);
+                ra[bsel][j] = *reinterpret_cast<const uint4*>(abase[j] + rc * ald[j]);
             }
-            if (t < ITEMS_B) {
+        }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Bs[(b_rq * 4 + i) * LPB + b_cv * V]) = rb[i];
+        for (int j = 0; j < UB; ++j) {
+            const int q = t + j * kTnThreads;
+            if (q < NBU) {
+                int64_t row = m0 + q / UPB;
+                row = row < A.M ? row : A.M - 1;
+                int64_t col = n0 + (q % UPB) * V;
+                col = col < lastn ? col : lastn;
+                rb[bsel][j] = *reinterpret_cast<const uint4*>(B + row * ldb + col);
+                if (mask) rm[bsel][j] = *reinterpret_cast<const uint4*>(mask + row * ldmask + col);
+            }
+        }
+    };
+    float cs[UB][V];
+#pragma unroll
+    for (int j = 0; j < UB; ++j)
+#pragma unroll
+        for (int e = 0; e < V; ++e) cs[j][e] = 0.f;
+    // masks B, zeroes rows past the chunk, adds B into the column sums and
+    // writes the step into stage st
+    auto store = [&](auto buf_c, int st, int64_t m0) {
+        constexpr int bsel = decltype(buf_c)::value;
+        unsigned char* As = lds_raw + st * STAGE;
+        unsigned char* Bs = As + SA;
+        const bool tail = m0 + kTnRows > m_end;
+#pragma unroll
+        for (int j = 0; j < UA; ++j) {
+            const int q = t + j * kTnThreads;
+            if (q < NA) {
+                uint4 v = ra[bsel][j];
+                const int64_t row = m0 + q / UPA;
+                if (row >= m_end || row >= alim[j]) v = make_uint4(0, 0, 0, 0);
+                *reinterpret_cast<uint4*>(As + (q / UPA) * PA + (q % UPA) * 16) = v;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < UB; ++j) {
+            const int q = t + j * kTnThreads;
+            if (q < NBU) {
+                uint4 v = rb[bsel][j];
+                if (mask) v = apply_mask<T>(v, rm[bsel][j]);
+                if (tail && m0 + q / UPB >= m_end) v = make_uint4(0, 0, 0, 0);
+                if (do_cs) {
+                    float f[V];
+                    unpack<T>(v, f);
+#pragma unroll
+                    for (int e = 0; e < V; ++e) cs[j][e] += f[e];
+                }
+                *reinterpret_cast<uint4*>(Bs + (q / UPB) * PB + (q % UPB) * 16) = v;
             }
         }
     };
@@ -668,55 +656,87 @@ __global__ __launch_bounds__(kTnThreads) void gemm_tn(AOperand<T> A, const T* __
         for (int j = 0; j < NBN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    float cs = 0.f;
 
-    if (m_begin < m_end) {
-        load_step(m_begin);
-        store_step();
-        __syncthreads();
-        for (int64_t m0 = m_begin; m0 < m_end; m0 += MS) {
-            const bool more = m0 + MS < m_end;
-            if (more) load_step(m0 + MS);
-            step_m0 = m0 + MS;
-            if (do_cs && t < BNT) {
-                if constexpr (kBf16) {
+    // operand read offsets (bytes within a stage tile)
+    const int g = lane >> 4, i16 = lane & 15;
+    const int q4 = i16 >> 2, r4 = i16 & 3;
+    auto compute = [&](int st) {
+        const unsigned char* As = lds_raw + st * STAGE;
+        const unsigned char* Bs = As + SA;
+        if constexpr (kBf16) {
 #pragma unroll
-                    for (int r = 0; r < MS; ++r) cs += bf16_to_f32(Bs[t * LPB + r]);
-                } else {
+            for (int s = 0; s < 2; ++s) {           // 16 rows per MFMA
+                const int mrow = 16 * s + 8 * (g >> 1) + q4;
+                bf16x8_t xa[NBK], yb[NBN];
 #pragma unroll
-                    for (int r = 0; r < MS; ++r) cs += Bs[r * LPB + t];
+                for (int i = 0; i < NBK; ++i) {
+                    const int col = wk * 64 + 32 * i + 16 * (g & 1) + 4 * r4;
+                    const unsigned char* p = As + mrow * PA + col * 2;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(p));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(p + 4 * PA));
+                    xa[i] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
-            }
 #pragma unroll
-            for (int ks = 0; ks < MS; ks += KI) {
-                typename Mfma<T>::frag fa[NBK], fb[NBN];
-                if constexpr (kBf16) {
-#pragma unroll
-                    for (int i = 0; i < NBK; ++i)
-                        fa[i] = Mfma<T>::ld(&As[(wk * TK + i * 32 + lane % 32) * LPA], ks);
-#pragma unroll
-                    for (int j = 0; j < NBN; ++j)
-                        fb[j] = Mfma<T>::ld(&Bs[(wn * TNW + j * 32 + lane % 32) * LPB], ks);
-                } else {
-                    const int mr = ks + lane / 32;
-#pragma unroll
-                    for (int i = 0; i < NBK; ++i)
-                        fa[i] = reinterpret_cast<const float*>(As)[mr * LPA + wk * TK + i * 32 + lane % 32];
-#pragma unroll
-                    for (int j = 0; j < NBN; ++j)
-                        fb[j] = reinterpret_cast<const float*>(Bs)[mr * LPB + wn * TNW + j * 32 + lane % 32];
+                for (int j = 0; j < NBN; ++j) {
+                    const int col = wn * TNW + 32 * j + 16 * (g & 1) + 4 * r4;
+                    const unsigned char* p = Bs + mrow * PB + col * 2;
+                    const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(p));
+                    const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) i16x4_t*)(p + 4 * PB));
+                    yb[j] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                 }
 #pragma unroll
                 for (int i = 0; i < NBK; ++i)
 #pragma unroll
-                    for (int j = 0; j < NBN; ++j) acc[i][j] = Mfma<T>::mma(fa[i], fb[j], acc[i][j]);
+                    for (int j = 0; j < NBN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[i], yb[j], acc[i][j], 0, 0, 0);
             }
-            __syncthreads();
-            if (more) {
-                store_step();
-                __syncthreads();
+        } else {
+#pragma unroll
+            for (int s = 0; s < kTnRows / 2; ++s) {   // 2 rows per MFMA, one per lane half
+                const int mrow = 2 * s + (lane >> 5);
+                float xa[NBK], yb[NBN];
+#pragma unroll
+                for (int i = 0; i < NBK; ++i)
+                    xa[i] = *reinterpret_cast<const float*>(As + mrow * PA + (wk * 64 + 32 * i + (lane & 31)) * 4);
+#pragma unroll
+                for (int j = 0; j < NBN; ++j)
+                    yb[j] = *reinterpret_cast<const float*>(Bs + mrow * PB + (wn * TNW + 32 * j + (lane & 31)) * 4);
+#pragma unroll
+                for (int i = 0; i < NBK; ++i)
+#pragma unroll
+                    for (int j = 0; j < NBN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(xa[i], yb[j], acc[i][j], 0, 0, 0);
             }
         }
+    };
+
+    const int64_t nsteps = m_begin < m_end ? (m_end - m_begin + kTnRows - 1) / kTnRows : 0;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    if (nsteps > 0) {
+        load(I0{}, m_begin);
+        store(I0{}, 0, m_begin);
+    }
+    if (nsteps > 1) load(I1{}, m_begin + kTnRows);
+    if (nsteps > 2) load(I0{}, m_begin + 2 * kTnRows);
+    __syncthreads();
+    // step s: write step s+1 (register buffer (s+1)%2) into stage (s+1)%2,
+    // refill that buffer with step s+3, then multiply stage s%2
+    for (int64_t s0 = 0; s0 < nsteps; s0 += 2) {
+        static_for<0, 2>([&](auto dc) {
+            constexpr int d = decltype(dc)::value;
+            const int64_t s = s0 + d;
+            if (s < nsteps) {
+                if (s + 1 < nsteps) store(std::integral_constant<int, 1 - d>{}, 1 - d, m_begin + (s + 1) * kTnRows);
+                if (s + 3 < nsteps) load(std::integral_constant<int, 1 - d>{}, m_begin + (s + 3) * kTnRows);
+                compute(d);
+                __syncthreads();
+            }
+        });
     }
 
     float* out = part + chunk * ldp_k * ldp_n;
@@ -727,11 +747,27 @@ __global__ __launch_bounds__(kTnThreads) void gemm_tn(AOperand<T> A, const T* __
             const int64_t col = n0 + wn * TNW + j * 32 + lane % 32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int64_t row = k0 + wk * TK + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
+                const int64_t row = k0 + wk * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
                 out[row * ldp_n + col] = acc[i][j][r];
             }
         }
-    if (do_cs && t < BNT) part_cs[chunk * ldp_n + n0 + t] = cs;
+    if (do_cs) {
+        // column sums: the per-thread sums of each step row, added in row order
+        float* red = reinterpret_cast<float*>(lds_raw);      // [kTnRows][BNT]
+#pragma unroll
+        for (int j = 0; j < UB; ++j) {
+            const int q = t + j * kTnThreads;
+            if (q < NBU)
+#pragma unroll
+                for (int e = 0; e < V; ++e) red[(q / UPB) * BNT + (q % UPB) * V + e] = cs[j][e];
+        }
+        __syncthreads();
+        if (t < BNT) {
+            float sum = 0.f;
+            for (int r = 0; r < kTnRows; ++r) sum += red[r * BNT + t];
+            part_cs[chunk * ldp_n + n0 + t] = sum;
+        }
+    }
 }
 
 // C[k, n] = sum over chunks of the partials, in chunk order.
@@ -901,11 +937,12 @@ struct TnPlan {
 TnPlan tn_plan(int64_t M, int64_t Kv, int64_t N, sag_dtype dt) {
     TnPlan p;
     const int64_t kv = Kv > 0 ? Kv : 1;
-    p.kt = kv <= 128 ? 128 : (kv <= 256 ? 256 : 512);
+    // (fp32 stops at 256: a 512 tile and its B slice would not fit twice in LDS)
+    p.kt = kv <= 128 ? 128 : ((kv <= 256 || dt != SAG_BF16) ? 256 : 512);
     p.bnt = (N <= 64 && p.kt != 128) ? 64 : 128;
     p.n_ktile = cdiv(kv, p.kt);
     p.n_ntile = cdiv(N > 0 ? N : 1, p.bnt);
-    const int64_t ms = dt == SAG_BF16 ? 32 : 16;
+    const int64_t ms = kTnRows;
     const int64_t m = M > 0 ? M : 1;
     int64_t want = cdiv(256, p.n_ntile);
     const int64_t max_chunks = cdiv(m, ms);
@@ -920,8 +957,16 @@ TnPlan tn_plan(int64_t M, int64_t Kv, int64_t N, sag_dtype dt) {
 template <class T, int KT, int BNT>
 void launch_tn(const TnPlan& p, const AOperand<T>& ao, const void* B, int64_t ldb, const void* mask, int64_t ldmask,
                int64_t N, float* part, float* pcs, hipStream_t s) {
+    constexpr size_t lds = 2 * static_cast<size_t>(tn_stage_bytes<T, KT, BNT>());
+    static_assert(lds >= static_cast<size_t>(kTnRows) * BNT * 4, "column-sum buffer");
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn<T, KT, BNT>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+        attr_set = true;
+    }
     const unsigned grid = static_cast<unsigned>(p.n_chunks * p.n_ktile * p.n_ntile);
-    gemm_tn<T, KT, BNT><<<grid, kTnThreads, 0, s>>>(ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask),
+    gemm_tn<T, KT, BNT><<<grid, kTnThreads, lds, s>>>(ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask),
                                                      ldmask, N, p.n_ktile, p.n_ntile, p.rows_per_chunk, part,
                                                      p.ldp_k, p.ldp_n, pcs);
 }
@@ -940,9 +985,13 @@ sag_status tn_typed(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t
     float* pcs = c.take<float>(p.n_chunks * p.ldp_n);
     if (!c.fits()) return fail(SAG_E_WORKSPACE, "gemm_tn: workspace too small");
     float* cs = colsum ? pcs : nullptr;
-    if (p.kt == 512 && p.bnt == 64) launch_tn<T, 512, 64>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
-    else if (p.kt == 512) launch_tn<T, 512, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
-    else if (p.kt == 256 && p.bnt == 64) launch_tn<T, 256, 64>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+    if (p.kt == 512) {
+        // (bf16 only: the plan keeps fp32 tiles at 256)
+        if constexpr (sizeof(T) == 2) {
+            if (p.bnt == 64) launch_tn<T, 512, 64>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+            else launch_tn<T, 512, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
+        }
+    } else if (p.kt == 256 && p.bnt == 64) launch_tn<T, 256, 64>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
     else if (p.kt == 256) launch_tn<T, 256, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
     else launch_tn<T, 128, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
     SAG_LAUNCH_CHECK();
