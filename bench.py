@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--op", help="trace op name the summary is for (with --summarize-counters)")
     p.add_argument("--kernel", help="kernel name substring of that op (with --summarize-counters)")
     p.add_argument("--out", help="summary file to write (with --summarize-counters)")
+    p.add_argument("--sizes-dir", help="optional third pass (TCC_EA0_RDREQ_sum and its 32B/64B/128B parts) "
+                                       "for an independent count of the bytes read (with --summarize-counters)")
     return p.parse_args()
 
 
@@ -125,6 +127,31 @@ def summarize_counters(args):
            "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
            "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b))}
     cmd = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib")
+    sizes = ""
+    if args.sizes_dir:
+        names = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
+        per = {n: _counter_means(args.sizes_dir, n) for n in names}
+        rows = []
+        for label, sub in (("calibration copy", CALIB_KERNEL), ("kernel", args.kernel)):
+            v = {}
+            for n in names:
+                _, vals = _pick(per[n], sub)
+                v[n] = sum(vals) / len(vals)
+            b = 32 * v[names[1]] + 64 * v[names[2]] + 128 * v[names[3]]
+            rows.append(f"| {label} | {v[names[0]]:.0f} | {v[names[1]]:.0f} | {v[names[2]]:.0f} | "
+                        f"{v[names[3]]:.0f} | {b:.4e} |")
+            rec["sized_read_bytes_" + ("calib" if label.startswith("cal") else "kernel")] = int(round(b))
+        sizes = f"""
+Cross-check: read requests by size (one more pass), bytes = 32 n32 + 64 n64 + 128 n128:
+
+```
+rocprofv3 --pmc {' '.join(names)} --output-format csv -d {args.sizes_dir} -o sizes -- {cmd}
+```
+
+| | requests | 32 B | 64 B | 128 B | bytes/dispatch |
+|---|---|---|---|---|---|
+{chr(10).join(rows)}
+"""
     text = f"""# HBM traffic of `{args.op}` from TCC byte counters
 
 Kernel: `{kname}`
@@ -149,7 +176,7 @@ python3 bench.py --summarize-counters {args.summarize_counters[0]} {args.summari
 
 Traffic per launch: {fetch_b + write_b:.4e} bytes.  The counters count L2 <-> fabric bytes, so
 hits in the memory-side cache (MALL) are included: an upper proxy for DRAM bytes.
-
+{sizes}
 Machine-readable record (bench.py reads it while the kernel sources keep this digest):
 
 <!-- counters {json.dumps(rec)} -->

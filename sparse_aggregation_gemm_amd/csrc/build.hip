@@ -25,26 +25,16 @@ struct BuildGeom {
     uint64_t nc;  // key divisor
 };
 
-// Wave-aggregated append: one atomic per wavefront.
-__device__ __forceinline__ void append_key(bool emit, uint64_t key, uint64_t* keys,
-                                           unsigned long long* counter) {
-    const uint64_t m = __ballot(emit);
-    if (m == 0) return;
-    const int lane = threadIdx.x & 63;
-    const int leader = __ffsll(static_cast<unsigned long long>(m)) - 1;
-    unsigned long long base = 0;
-    if (lane == leader) base = atomicAdd(counter, static_cast<unsigned long long>(__popcll(m)));
-    base = __shfl(base, leader, 64);
-    if (emit) {
-        const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        keys[base + __popcll(m & lt)] = key;
-    }
-}
-
 __device__ __forceinline__ uint64_t col_code(int64_t c, const BuildGeom& g) {
     return (c >= g.lo && c < g.hi) ? static_cast<uint64_t>(c - g.lo)
                                    : static_cast<uint64_t>(g.n_local + c);
 }
+
+// Each thread takes kExpandItems edges (strided by the block size, so loads
+// stay coalesced) and emits up to two keys per edge; a workgroup reserves
+// room for all its keys with one atomic and writes them at block-scan
+// offsets.
+constexpr int kExpandItems = 8;
 
 __global__ __launch_bounds__(256) void expand_edges(const int32_t* __restrict__ src,
                                                     const int32_t* __restrict__ dst, int64_t n_edges,
@@ -52,23 +42,53 @@ __global__ __launch_bounds__(256) void expand_edges(const int32_t* __restrict__ 
                                                     uint64_t* __restrict__ keys,
                                                     unsigned long long* __restrict__ counter,
                                                     int* __restrict__ bad) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    int64_t u = -1, v = -1;
-    if (e < n_edges) {
-        u = src[e];
-        v = dst[e];
-        if (u < 0 || v < 0 || u >= g.n_global || v >= g.n_global) {
-            atomicOr(bad, 1);
-            u = v = -1;
+    __shared__ int wave_tot[4];
+    __shared__ unsigned long long block_base;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t e0 = static_cast<int64_t>(blockIdx.x) * (256 * kExpandItems) + threadIdx.x;
+    uint64_t key[2 * kExpandItems];
+    bool em[2 * kExpandItems];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < kExpandItems; ++i) {
+        const int64_t e = e0 + static_cast<int64_t>(i) * 256;
+        int64_t u = -1, v = -1;
+        if (e < n_edges) {
+            u = src[e];
+            v = dst[e];
+            if (u < 0 || v < 0 || u >= g.n_global || v >= g.n_global) {
+                atomicOr(bad, 1);
+                u = v = -1;
+            }
         }
+        // u -> v: row v aggregates column u
+        em[2 * i] = u >= 0 && u != v && v >= g.lo && v < g.hi;
+        key[2 * i] = em[2 * i] ? static_cast<uint64_t>(v - g.lo) * g.nc + col_code(u, g) : 0;
+        em[2 * i + 1] = symmetrize && u >= 0 && u != v && u >= g.lo && u < g.hi;
+        key[2 * i + 1] = em[2 * i + 1] ? static_cast<uint64_t>(u - g.lo) * g.nc + col_code(v, g) : 0;
+        cnt += (em[2 * i] ? 1 : 0) + (em[2 * i + 1] ? 1 : 0);
     }
-    // u -> v: row v aggregates column u
-    bool emit = u >= 0 && u != v && v >= g.lo && v < g.hi;
-    append_key(emit, emit ? static_cast<uint64_t>(v - g.lo) * g.nc + col_code(u, g) : 0, keys, counter);
-    if (symmetrize) {
-        emit = u >= 0 && u != v && u >= g.lo && u < g.hi;
-        append_key(emit, emit ? static_cast<uint64_t>(u - g.lo) * g.nc + col_code(v, g) : 0, keys, counter);
+    // exclusive prefix of cnt over the workgroup
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
     }
+    if (lane == 63) wave_tot[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        before += w < wave ? wave_tot[w] : 0;
+        total += wave_tot[w];
+    }
+    if (threadIdx.x == 0) block_base = total ? atomicAdd(counter, static_cast<unsigned long long>(total)) : 0ull;
+    __syncthreads();
+    unsigned long long pos = block_base + static_cast<unsigned long long>(before + incl - cnt);
+#pragma unroll
+    for (int j = 0; j < 2 * kExpandItems; ++j)
+        if (em[j]) keys[pos++] = key[j];
 }
 
 __global__ void self_loop_keys(uint64_t* __restrict__ keys, int64_t n_local, uint64_t nc) {
@@ -263,8 +283,8 @@ extern "C" sag_status sag_csr_build_normalize(const int32_t* src, const int32_t*
     SAG_CHECK_HIP(hipMemsetAsync(w.counter, 0, sizeof(unsigned long long), s));
     SAG_CHECK_HIP(hipMemsetAsync(w.bad, 0, sizeof(int), s));
     if (n_edges > 0) {
-        expand_edges<<<grid_for(n_edges), 256, 0, s>>>(src, dst, n_edges, g, (flags & SAG_SYMMETRIZE) ? 1 : 0,
-                                                       w.keys_a, w.counter, w.bad);
+        expand_edges<<<dim3(static_cast<unsigned>(cdiv(n_edges, 256 * kExpandItems))), 256, 0, s>>>(
+            src, dst, n_edges, g, (flags & SAG_SYMMETRIZE) ? 1 : 0, w.keys_a, w.counter, w.bad);
         SAG_LAUNCH_CHECK();
     }
     unsigned long long m_edges = 0;

@@ -771,6 +771,22 @@ __global__ __launch_bounds__(kTnThreads, 1) void gemm_tn(AOperand<T> A, const T*
 }
 
 // C[k, n] = sum over chunks of the partials, in chunk order.
+// p[0] + p[stride] + ... + p[(n-1) stride], added in that order; eight loads
+// are issued before their additions.
+__device__ __forceinline__ float sum_chunks(const float* __restrict__ p, int64_t stride, int64_t n) {
+    float s = 0.f;
+    int64_t c = 0;
+    for (; c + 8 <= n; c += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = p[(c + u) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; c < n; ++c) s += p[c * stride];
+    return s;
+}
+
 __global__ void tn_reduce(const float* __restrict__ part, int64_t n_chunks, int64_t ldp_k, int64_t ldp_n,
                           int64_t k1, int64_t k1p, int64_t k2, int64_t N, float* __restrict__ C, int64_t ldc,
                           const float* __restrict__ part_cs, float* __restrict__ colsum) {
@@ -779,15 +795,9 @@ __global__ void tn_reduce(const float* __restrict__ part, int64_t n_chunks, int6
     if (idx < rows * N) {
         const int64_t k = idx / N, n = idx % N;
         const int64_t kv = k < k1 ? k : k1p + (k - k1);
-        float s = 0.f;
-        for (int64_t c = 0; c < n_chunks; ++c) s += part[(c * ldp_k + kv) * ldp_n + n];
-        C[k * ldc + n] = s;
+        C[k * ldc + n] = sum_chunks(part + kv * ldp_n + n, ldp_k * ldp_n, n_chunks);
     }
-    if (colsum && idx < N) {
-        float s = 0.f;
-        for (int64_t c = 0; c < n_chunks; ++c) s += part_cs[c * ldp_n + idx];
-        colsum[idx] = s;
-    }
+    if (colsum && idx < N) colsum[idx] = sum_chunks(part_cs + idx, ldp_n, n_chunks);
 }
 
 // ---- packing of B -----------------------------------------------------------------

@@ -17,16 +17,32 @@ constexpr int kShortMax = 32;
 
 namespace {
 
+// Sort key of each row (bin, length class, row) and the bin counts; the
+// counts are added per wavefront (one atomic per wavefront and counter).
 __global__ void sched_keys(const int64_t* __restrict__ indptr, int64_t n, int32_t seg_len, int row_bits,
                            uint64_t* __restrict__ keys, unsigned long long* __restrict__ counts) {
     const int64_t r = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (r >= n) return;
-    const int64_t len = indptr[r + 1] - indptr[r];
-    const uint64_t bin = len <= kShortMax ? 0 : (len <= seg_len ? 1 : 2);
-    const uint64_t cls = len == 0 ? 0 : static_cast<uint64_t>(64 - __clzll(static_cast<unsigned long long>(len)));
-    keys[r] = ((bin * 64 + cls) << row_bits) | static_cast<uint64_t>(r);
-    atomicAdd(&counts[bin], 1ull);
-    if (bin == 2) atomicAdd(&counts[3], static_cast<unsigned long long>((len + seg_len - 1) / seg_len));
+    const bool valid = r < n;
+    uint64_t bin = 3;
+    unsigned long long segs = 0;
+    if (valid) {
+        const int64_t len = indptr[r + 1] - indptr[r];
+        bin = len <= kShortMax ? 0 : (len <= seg_len ? 1 : 2);
+        const uint64_t cls = len == 0 ? 0 : static_cast<uint64_t>(64 - __clzll(static_cast<unsigned long long>(len)));
+        keys[r] = ((bin * 64 + cls) << row_bits) | static_cast<uint64_t>(r);
+        if (bin == 2) segs = static_cast<unsigned long long>((len + seg_len - 1) / seg_len);
+    }
+    const unsigned long long m0 = __ballot(bin == 0), m1 = __ballot(bin == 1), m2 = __ballot(bin == 2);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) segs += __shfl_xor(segs, off, 64);
+    if ((threadIdx.x & 63) == 0) {
+        if (m0) atomicAdd(&counts[0], static_cast<unsigned long long>(__popcll(m0)));
+        if (m1) atomicAdd(&counts[1], static_cast<unsigned long long>(__popcll(m1)));
+        if (m2) {
+            atomicAdd(&counts[2], static_cast<unsigned long long>(__popcll(m2)));
+            atomicAdd(&counts[3], segs);
+        }
+    }
 }
 
 __global__ void sched_records(const uint64_t* __restrict__ keys, int64_t n, int row_bits,
