@@ -23,10 +23,15 @@ What it computes, in float64 unless noted, and where each step is defined:
   the same SpMM and GEMM primitives).
 * ``native``     -- the fp64 CSR SpMM in plain C (each output row summed over
   its entries in ascending order).
+* ``lowbit``     -- Sylvie's Low-bit Module (b-bit stochastic quantization of
+  halo rows with a per-row scale and zero-point; dequantization) with the
+  Philox4x32-10 counter-based generator for its draws, and DIGEST's push of
+  a partition's rows into the representation store (plus the accumulating
+  form used for halo gradients).
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it.  Every function is pinned by tests
 under ``tests/`` that do not re-type its formulas: closed forms, invariants,
 brute force on tiny inputs and finite differences.
 """
-from . import csr, layers, native  # noqa: F401
+from . import csr, layers, lowbit, native  # noqa: F401
