@@ -192,6 +192,66 @@ sag_status sag_halo_gather(const void* src, int64_t ld_src, const int32_t* rows,
                            void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Halo push -- the DIGEST "push" (DIGEST, system design: after an epoch a
+ * partition stores its newly computed rows of its own nodes in the
+ * representation store): dst[ids[k] - row_base, :] = src[k, :] for k < n,
+ * a bitwise row copy.  With accumulate = 1 the rows are added instead,
+ * dst += src in fp32 with one rounding to dt: the return of halo-node
+ * gradients to their owner, which integrates them into its own rows
+ * (Sylvie, "Backward Propagation").
+ * src: [n, d] (ld_src); dst: [n_dst, d] (ld_dst); ids: device int32[n].
+ * Targets outside [0, n_dst) are skipped.  Two equal targets in one call
+ * race (the result is one of the writes, or an incomplete sum).  src and
+ * dst must not overlap.  Asynchronous on `stream`.
+ */
+sag_status sag_halo_push(const void* src, int64_t ld_src, const int32_t* ids, int64_t row_base,
+                         int64_t n, int64_t d, sag_dtype dt, int accumulate, void* dst,
+                         int64_t ld_dst, int64_t n_dst, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Low-bit halo messages -- Sylvie's Quantizer and Dequantizer (Sylvie,
+ * system overview, "Quantizer", "Communicator", "Dequantizer"; convergence
+ * section, "Unbiased Low-bit Module").
+ *
+ * Each message row is one node feature vector h quantized to bits-bit codes
+ * (bits in {1, 2, 4, 8}; B = 2^bits - 1) with zero = min(h),
+ * scale = (max(h) - min(h)) / B, and per element t = (h - zero) / scale,
+ * code = floor(t) + 1 with probability t - floor(t), at most B (stochastic
+ * rounding; a row with scale 0 has all codes 0).  Each step is an fp32
+ * operation rounded to nearest even, in that order.  The draw of element j
+ * of stream id `node` in call `epoch`: Philox4x32-10 (Salmon, Moraes, Dror,
+ * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
+ * (j / 4, node, epoch, 0), key (seed & 0xffffffff, seed >> 32), word j % 4,
+ * top 24 bits times 2^-24; code + 1 when the draw is below t - floor(t).
+ *
+ * Codes: row k at codes + k * ld_codes (bytes); element j in bits
+ * [bits*j, bits*j + bits) little-endian; codes must be 16-byte aligned and
+ * ld_codes a multiple of 16 and >= sag_code_row_bytes(d, bits) (0 for bad
+ * arguments).  Bits of elements >= d are written as 0 up to
+ * ceil(d / 8) * bits bytes; the rest of a row is not touched.
+ *
+ * sag_quantize_rows: message row k quantizes src[rows[k]] (rows NULL:
+ * src[k]) with stream id nodes[k] (nodes NULL: k); a row index outside
+ * [0, n_src) gives an all-zero message row (codes, scale and zero 0).
+ * scale, zero: device float[n].
+ * sag_dequantize_rows: the recovered row zero[k] + code * scale[k] (fp32,
+ * multiply then add, each rounded) goes to dst[ids[k] - row_base] (ids
+ * NULL: dst[k]), or is added to it in fp32 when accumulate = 1 (the
+ * gradient return); one rounding to dt.  Targets outside [0, n_dst) are
+ * skipped.  Both calls are asynchronous on `stream`; inputs are caller-owned
+ * device memory.
+ */
+size_t sag_code_row_bytes(int64_t d, int bits);
+sag_status sag_quantize_rows(const void* src, int64_t ld_src, sag_dtype dt, const int32_t* rows,
+                             int64_t n_src, const int32_t* nodes, int64_t n, int64_t d, int bits,
+                             uint64_t seed, uint32_t epoch, uint8_t* codes, int64_t ld_codes,
+                             float* scale, float* zero, void* stream);
+sag_status sag_dequantize_rows(const uint8_t* codes, int64_t ld_codes, const float* scale,
+                               const float* zero, int64_t n, int64_t d, int bits,
+                               const int32_t* ids, int64_t row_base, int accumulate, sag_dtype dt,
+                               void* dst, int64_t ld_dst, int64_t n_dst, void* stream);
+
+/* ---------------------------------------------------------------------------
  * SpMM: Y = A X (CAGNET page: the aggregation A^T H of a layer, one output
  * row per CSR row; DIGEST: P_in H_in + P_out H~_out when X = [H_in ; H~_out]).
  * X: [A->n_cols, d] of type xt; Y: [A->n_rows, d] of type yt.  Supported

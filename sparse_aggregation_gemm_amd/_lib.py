@@ -44,6 +44,11 @@ SIGNATURES = {
     "sag_csr_schedule_workspace_bytes": (sz, [i64]),
     "sag_csr_schedule": (cint, [PCSR, i32, vp, sz, vp, sz, vp]),
     "sag_halo_gather": (cint, [vp, i64, vp, i64, i64, i64, cint, vp, i64, vp]),
+    "sag_halo_push": (cint, [vp, i64, vp, i64, i64, i64, cint, cint, vp, i64, i64, vp]),
+    "sag_code_row_bytes": (sz, [i64, cint]),
+    "sag_quantize_rows": (cint, [vp, i64, cint, vp, i64, vp, i64, i64, cint, ctypes.c_uint64, u32,
+                                 vp, i64, vp, vp, vp]),
+    "sag_dequantize_rows": (cint, [vp, i64, vp, vp, i64, i64, cint, vp, i64, cint, cint, vp, i64, i64, vp]),
     "sag_spmm_workspace_bytes": (sz, [PCSR, i64]),
     "sag_spmm_csr": (cint, [PCSR, vp, i64, cint, i64, vp, i64, cint, vp, i64, i64, vp, sz, vp]),
     "sag_spmm_csr_t": (cint, [PCSR, vp, i64, cint, i64, vp, i64, cint, vp, i64, i64, vp, sz, vp]),

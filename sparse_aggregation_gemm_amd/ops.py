@@ -197,6 +197,67 @@ def halo_gather(src: torch.Tensor, rows: torch.Tensor, out: torch.Tensor, row_ba
     return out
 
 
+def halo_push(src: torch.Tensor, ids: torch.Tensor, dst: torch.Tensor, row_base: int = 0,
+              accumulate: bool = False) -> torch.Tensor:
+    """sag_halo_push: dst[ids[k] - row_base] = src[k] (or += for gradients);
+    targets outside dst's rows are skipped."""
+    ids = ids.to(torch.int32).contiguous()
+    st = L.lib().sag_halo_push(_ptr(src), _ld(src), _ptr(ids), row_base, ids.numel(), src.shape[1],
+                               dtype_code(src.dtype), int(bool(accumulate)), _ptr(dst), _ld(dst), dst.shape[0],
+                               _stream(src.device))
+    L.check("sag_halo_push", st)
+    return dst
+
+
+def code_row_bytes(d: int, bits: int) -> int:
+    return int(L.lib().sag_code_row_bytes(d, bits))
+
+
+def quantize_rows(src: torch.Tensor, bits: int, seed: int, epoch: int, rows: torch.Tensor | None = None,
+                  nodes: torch.Tensor | None = None, n: int | None = None, out=None):
+    """sag_quantize_rows: message row k = Sylvie's b-bit quantization of
+    src[rows[k]] (rows None: src[k]) with stream id nodes[k] (None: k).
+    Returns (codes uint8 [n, code_row_bytes], scale float32 [n], zero float32 [n])."""
+    dev = src.device
+    if rows is not None:
+        rows = rows.to(torch.int32).contiguous()
+        n = rows.numel()
+    elif n is None:
+        n = src.shape[0]
+    if nodes is not None:
+        nodes = nodes.to(torch.int32).contiguous()
+        if nodes.numel() != n:
+            raise ValueError("nodes must have one id per message row")
+    d = src.shape[1]
+    if out is None:
+        codes = torch.empty((n, code_row_bytes(d, bits)), dtype=torch.uint8, device=dev)
+        scale = torch.empty(n, dtype=torch.float32, device=dev)
+        zero = torch.empty(n, dtype=torch.float32, device=dev)
+    else:
+        codes, scale, zero = out
+    st = L.lib().sag_quantize_rows(_ptr(src), _ld(src), dtype_code(src.dtype), _ptr(rows),
+                                   src.shape[0], _ptr(nodes), n, d, bits,
+                                   seed & (2 ** 64 - 1), epoch & 0xFFFFFFFF, _ptr(codes), codes.stride(0),
+                                   _ptr(scale), _ptr(zero), _stream(dev))
+    L.check("sag_quantize_rows", st)
+    return codes, scale, zero
+
+
+def dequantize_rows(codes: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor, d: int, bits: int,
+                    dst: torch.Tensor, ids: torch.Tensor | None = None, row_base: int = 0,
+                    accumulate: bool = False) -> torch.Tensor:
+    """sag_dequantize_rows: dst[ids[k] - row_base] (ids None: dst[k]) =
+    zero[k] + code * scale[k] (or += for gradients)."""
+    if ids is not None:
+        ids = ids.to(torch.int32).contiguous()
+    st = L.lib().sag_dequantize_rows(_ptr(codes), codes.stride(0), _ptr(scale), _ptr(zero), codes.shape[0], d,
+                                     bits, _ptr(ids), row_base,
+                                     int(bool(accumulate)), dtype_code(dst.dtype), _ptr(dst), _ld(dst),
+                                     dst.shape[0], _stream(codes.device))
+    L.check("sag_dequantize_rows", st)
+    return dst
+
+
 def _spmm(name, A: Csr, X, out_dtype=None, Y=None, addend=None):
     lib = L.lib()
     d = X.shape[1]
