@@ -37,7 +37,7 @@ CALIB_ROWS = 1 << 21
 CALIB_ROW_BYTES = 512
 CALIB_READ = CALIB_ROWS * (CALIB_ROW_BYTES + 4)
 CALIB_WRITE = CALIB_ROWS * CALIB_ROW_BYTES
-CALIB_KERNEL = "gather_rows"
+CALIB_KERNEL = "gather_rows<32>"   # the 512-byte-row instance
 CSRC = os.path.join(ROOT, "sparse_aggregation_gemm_amd", "csrc")
 # sources whose text decides each op family's kernels (a counter summary is
 # valid only for the sources it was taken on)
@@ -336,6 +336,59 @@ def cpu_baseline(w, rows_hint: int, target_s: float = 15.0):
     }
 
 
+def halo_messages(sag, torch, np, n_store=4_000_000, n_halo=3_800_000, d=128, reps=5, cpu_rows=20_000):
+    """Halo traffic of one GPU's share of the 100M-node graph (GCN 128 wide,
+    bf16, a 4M-row stale store, ~3.8M halo rows, sorted ids): the
+    full-precision pull, Sylvie's quantizer and dequantizer at 1 and 8 bits,
+    and the DIGEST push, each timed with HIP events over `reps` calls; the
+    oracle quantizer on `cpu_rows` rows beside it."""
+    from oracle import lowbit as olb
+
+    dev = torch.device("cuda:0")
+    g = np.random.default_rng(55)
+    ids = np.sort(g.choice(n_store, n_halo, replace=False)).astype(np.int32)
+    store = sag.empty_dense(n_store, d, torch.bfloat16, dev)
+    store.copy_(torch.randn(n_store, d, device=dev).to(torch.bfloat16))
+    ids_d = torch.from_numpy(ids).to(dev)
+    halo = sag.empty_dense(n_halo, d, torch.bfloat16, dev)
+    codes = {b: torch.empty((n_halo, sag.code_row_bytes(d, b)), dtype=torch.uint8, device=dev) for b in (1, 8)}
+    scale = torch.empty(n_halo, dtype=torch.float32, device=dev)
+    zero = torch.empty(n_halo, dtype=torch.float32, device=dev)
+    calls = [("pull (gather)", lambda: sag.halo_gather(store, ids_d, halo))]
+    for b in (1, 8):
+        calls.append((f"quantize {b}-bit", lambda b=b: sag.quantize_rows(store, b, 7, 1, rows=ids_d, nodes=ids_d,
+                                                                         out=(codes[b], scale, zero))))
+        calls.append((f"dequantize {b}-bit", lambda b=b: sag.dequantize_rows(codes[b], scale, zero, d, b, halo)))
+    calls.append(("push", lambda: sag.halo_push(halo, ids_d, store)))
+    for _, f in calls:
+        f()
+    torch.cuda.synchronize()
+    sag.trace_enable(True)
+    for _, f in calls:
+        for _ in range(reps):
+            f()
+    torch.cuda.synchronize()
+    sag.trace_enable(False)
+    recs = sag.trace_records(clear=True)
+    out = []
+    for i, (label, _) in enumerate(calls):
+        rr = recs[i * reps:(i + 1) * reps]
+        ms = sum(r["ms"] for r in rr) / len(rr)
+        gbs = rr[0]["bytes"] / ms / 1e6
+        out.append({"op": label, "kernel_op": rr[0]["name"], "avg_ms": round(ms, 4), "GBps": round(gbs, 1),
+                    "frac_hbm": round(gbs / HBM_PEAK_GBS, 3), "alg_bytes": rr[0]["bytes"]})
+    x = g.standard_normal((cpu_rows, d)).astype(np.float32)
+    t0 = time.perf_counter()
+    olb.quantize_rows(x, np.arange(cpu_rows), 1, 7, 1)
+    cpu_s = time.perf_counter() - t0
+    msg = {b: sag.code_row_bytes(d, b) + 8 for b in (1, 8)}
+    return {"n_store": n_store, "n_halo": n_halo, "d": d, "dtype": "bf16", "ops": out,
+            "message_bytes_per_row": {"full": 2 * d, "1-bit": msg[1], "8-bit": msg[8]},
+            "cpu_baseline_quantize": {"value": round(cpu_s * n_halo / cpu_rows * 1e3, 1), "unit": "ms",
+                                      "cores": 1, "kind": "oracle",
+                                      "sample": f"{cpu_rows} rows x {d}, 1-bit, numpy, scaled to {n_halo} rows"}}
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -421,24 +474,31 @@ def main():
     roof["alg_bytes_per_launch"] = dom_o["bytes"]
     roof["avg_launch_ms"] = dom["avg_ms"]
 
+    A = m.built.A
+    conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
+            "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
+            "seg_len": args.seg_len, "schedule": sag.csr_info(A)}
+    build_ms = m.build_ms
+    log("[bench] halo messages (pull, low-bit quantize/dequantize, push) at the 100M-graph share's shape")
+    del m, A
+    torch.cuda.empty_cache()
+    halo = halo_messages(sag, torch, np)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle on a row sample)")
         cpu = cpu_baseline(w, args.cpu_rows)
 
-    A = m.built.A
     out = {
         "metric": METRIC, "value": round(ms_step, 4), "unit": "ms", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": False,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
-        "config": {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
-                   "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
-                   "seg_len": args.seg_len, "schedule": sag.csr_info(A)},
-        "build_ms": round(m.build_ms, 1),
+        "config": conf,
+        "build_ms": round(build_ms, 1),
         "spmm": spmm,
         "ops": table,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "halo_messages": halo,
     }
     print(json.dumps(out), flush=True)
 
