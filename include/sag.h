@@ -213,16 +213,18 @@ sag_status sag_halo_push(const void* src, int64_t ld_src, const int32_t* ids, in
  * system overview, "Quantizer", "Communicator", "Dequantizer"; convergence
  * section, "Unbiased Low-bit Module").
  *
- * Each message row is one node feature vector h quantized to bits-bit codes
- * (bits in {1, 2, 4, 8}; B = 2^bits - 1) with zero = min(h),
- * scale = (max(h) - min(h)) / B, and per element t = (h - zero) / scale,
- * code = floor(t) + 1 with probability t - floor(t), at most B (stochastic
- * rounding; a row with scale 0 has all codes 0).  Each step is an fp32
+ * Each message row is one node feature vector h (finite values) quantized
+ * to bits-bit codes (bits in {1, 2, 4, 8}; B = 2^bits - 1) with
+ * zero = min(h), R = max(h) - min(h), scale = R / B, and per element
+ * t = (h - zero) * (B / R), code = floor(t) + 1 with probability
+ * t - floor(t), at most B (stochastic rounding; a row with R = 0 has all
+ * codes 0; a subnormal R gives unspecified codes).  Each step is an fp32
  * operation rounded to nearest even, in that order.  The draw of element j
  * of stream id `node` in call `epoch`: Philox4x32-10 (Salmon, Moraes, Dror,
  * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
- * (j / 4, node, epoch, 0), key (seed & 0xffffffff, seed >> 32), word j % 4,
- * top 24 bits times 2^-24; code + 1 when the draw is below t - floor(t).
+ * (j / 8, node, epoch, 0), key (seed & 0xffffffff, seed >> 32), 16-bit half
+ * j % 2 (low first) of word (j / 2) % 4, times 2^-16; code + 1 when the
+ * draw is below t - floor(t).
  *
  * Codes: row k at codes + k * ld_codes (bytes); element j in bits
  * [bits*j, bits*j + bits) little-endian; codes must be 16-byte aligned and

@@ -4,14 +4,15 @@
 // (B = 2^b - 1 bins) by stochastic rounding, with a per-row scale
 // (max(h) - min(h)) / B and zero-point min(h); the receiver recovers
 // zero + code * scale.  The page's equations are missing from the text; the
-// plain reading is taken: t = (h - zero) / scale, code = floor(t) + 1 with
-// probability t - floor(t) (at most B), every step an fp32 operation rounded
-// to nearest even in that order, so that the integer decisions are
-// reproducible.  The uniform draws come from the Philox4x32-10 counter-based
-// generator (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
-// easy as 1, 2, 3", SC'11): element j of node `node` in call `epoch` uses
-// word j % 4 of the block at counter (j / 4, node, epoch, 0) under key
-// (seed low, seed high), its top 24 bits times 2^-24.
+// plain reading is taken: t = (h - zero) * (B / (max - min)), the position
+// in bins, code = floor(t) + 1 with probability t - floor(t) (at most B),
+// every step an fp32 operation rounded to nearest even in that order, so
+// that the integer decisions are reproducible.  The uniform draws come from
+// the Philox4x32-10 counter-based generator (Salmon, Moraes, Dror and Shaw,
+// "Parallel random numbers: as easy as 1, 2, 3", SC'11): element j of node
+// `node` in call `epoch` uses 16-bit half j % 2 (low first) of word
+// (j / 2) % 4 of the block at counter (j / 8, node, epoch, 0) under key
+// (seed low, seed high), times 2^-16 -- one block per eight elements.
 //
 // A group of G lanes handles a row, each lane eight consecutive elements at
 // a time (one 16-byte bf16 vector or two fp32 vectors), so that a lane's
@@ -109,11 +110,18 @@ __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
     const bool ok = valid && r >= 0 && r < a.n_src;
     const T* row = reinterpret_cast<const T*>(a.src) + (ok ? r : 0) * a.ld_src;
     const int64_t groups = (a.d + 7) / 8;
+    // a lane's first group stays in registers for the coding pass (the only
+    // one when d <= 8 G); later groups are loaded again
+    float f0[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float mn = __builtin_huge_valf(), mx = -__builtin_huge_valf();
     if (ok) {
         for (int64_t g = gl; g < groups; g += G) {
             float f[8];
             load8<T>(row, g, a.d, f);
+            if (g == gl) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f0[e] = f[e];
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 if (8 * g + e < a.d) {
@@ -129,30 +137,31 @@ __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
     }
     const float B = static_cast<float>((1 << a.bits) - 1);
     const float z = ok && a.d > 0 ? mn : 0.f;
-    const float s = ok && a.d > 0 ? (mx - mn) / B : 0.f;
+    const float R = ok && a.d > 0 ? mx - mn : 0.f;
+    const float s = R / B;
+    const float inv = R > 0.f ? B / R : 0.f;
     if (!valid) return;
     const uint32_t node = static_cast<uint32_t>(a.nodes ? a.nodes[k] : k);
     uint8_t* out = a.codes + k * a.ld_codes;
     for (int64_t g = gl; g < groups; g += G) {
         uint64_t packed = 0;
-        if (s > 0.f) {
+        if (R > 0.f) {
             float f[8];
-            load8<T>(row, g, a.d, f);
-            uint32_t w[8];
+            if (g == gl) {
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                uint32_t c[4] = {static_cast<uint32_t>(2 * g + h), node, a.epoch, 0u};
-                philox4x32_10(c, a.key0, a.key1);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) w[4 * h + q] = c[q];
+                for (int e = 0; e < 8; ++e) f[e] = f0[e];
+            } else {
+                load8<T>(row, g, a.d, f);
             }
+            uint32_t w[4] = {static_cast<uint32_t>(g), node, a.epoch, 0u};
+            philox4x32_10(w, a.key0, a.key1);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 if (8 * g + e >= a.d) continue;
-                const float t = (f[e] - z) / s;
+                const float t = (f[e] - z) * inv;
                 const float fl = floorf(t);
                 const float fr = t - fl;
-                const float u = static_cast<float>(w[e] >> 8) * 5.9604644775390625e-8f;   // 2^-24
+                const float u = static_cast<float>((w[e / 2] >> (16 * (e & 1))) & 0xffffu) * 1.52587890625e-5f;   // 2^-16
                 float q = u < fr ? fl + 1.f : fl;
                 q = q < B ? q : B;
                 packed |= static_cast<uint64_t>(static_cast<uint32_t>(q)) << (a.bits * e);
