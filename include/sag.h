@@ -290,6 +290,13 @@ sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dty
  * (the aggregate when aggregating first, nothing otherwise); its size is
  * sag_*_save_bytes and its content is private to the library.  The
  * backward call must get the same A^T, H_ext, W, save and sizes.
+ *
+ * Widths.  The SpMM width min(d_in, d_out) is at most 1024 (fp32) or 2048
+ * (bf16).  The dense products keep their weight slice in LDS, so the K of
+ * each (d_in for the GCN forward, 2 d_in for a SAGE layer that aggregates
+ * first, d_out or 2 d_out for the input-gradient products) must stay within
+ * about 1024 fp32 / 2048 bf16 elements after padding to 128-byte chunks;
+ * larger widths return SAG_E_UNSUPPORTED before any launch.
  */
 
 /* GCN layer (CAGNET page, forward-propagation equation; Sylvie, "Forward

@@ -1015,6 +1015,10 @@ sag_status tn_typed(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t
 
 }  // namespace
 
+bool nn_k_fits(int64_t k1, int64_t k2, sag_dtype dt) {
+    return nn_lds_bytes(32, k_total(k1, k2, dt), dt) <= max_lds_per_block();
+}
+
 size_t packed_b_bytes(int64_t k1, int64_t k2, int64_t n_total, sag_dtype dt) {
     return static_cast<size_t>(round_up(n_total > 0 ? n_total : 1, kNPad) * k_total(k1, k2, dt) * elt_size(dt));
 }

@@ -153,6 +153,7 @@ extern "C" sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext,
                                             void* Y_pre, void* Out, int64_t ldo, void* save, size_t save_bytes,
                                             void* ws, size_t ws_bytes, void* stream) {
     SAG_TRY(check_layer_common("gcn_forward", A, H_ext, ldh, d_in, W, d_out, dt));
+    if (!nn_k_fits(d_in, 0, dt)) return fail(SAG_E_UNSUPPORTED, "gcn_forward: d_in too large for the transform");
     const int64_t n_l = A->n_rows;
     SAG_TRY(check_dense("gcn_forward Out", Out, n_l, d_out, ldo, dt));
     if (Y_pre) SAG_TRY(check_dense("gcn_forward Y_pre", Y_pre, n_l, d_out, ldo, dt));
@@ -212,6 +213,8 @@ extern "C" sag_status sag_gcn_layer_backward(const sag_csr* AT, int64_t n_local,
     }
     const int64_t n_ext = AT ? AT->n_rows : n_local;
     if (!W || !dW) return fail(SAG_E_INVALID, "gcn_backward: null W or dW");
+    if ((dH_ext || !agg) && !nn_k_fits(d_out, 0, dt))
+        return fail(SAG_E_UNSUPPORTED, "gcn_backward: d_out too large for the input-gradient product");
     SAG_TRY(check_dense("gcn_backward G_out", G_out, n_local, d_out, ldg, dt));
     if (relu) SAG_TRY(check_dense("gcn_backward Y", Y, n_local, d_out, ldg, dt));
     if (dH_ext) SAG_TRY(check_dense("gcn_backward dH_ext", dH_ext, n_ext, d_in, ldd, dt));
@@ -291,6 +294,8 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
                                              void* Y_pre, void* Out, int64_t ldo, void* save, size_t save_bytes,
                                              void* ws, size_t ws_bytes, void* stream) {
     SAG_TRY(check_layer_common("sage_forward", A, H_ext, ldh, d_in, W, d_out, dt));
+    if (!nn_k_fits(d_in, aggregate_first(d_in, d_out) ? d_in : 0, dt))
+        return fail(SAG_E_UNSUPPORTED, "sage_forward: d_in too large for the transform");
     const int64_t n_l = A->n_rows;
     if (A->n_cols < n_l) return fail(SAG_E_INVALID, "sage_forward: fewer columns than local rows");
     SAG_TRY(check_dense("sage_forward Out", Out, n_l, d_out, ldo, dt));
@@ -375,6 +380,8 @@ extern "C" sag_status sag_sage_layer_backward(const sag_csr* AT, int64_t n_local
     }
     const int64_t n_ext = AT ? AT->n_rows : n_local;
     if (!W || !dW) return fail(SAG_E_INVALID, "sage_backward: null W or dW");
+    if (!nn_k_fits(d_out, agg ? 0 : d_out, dt))
+        return fail(SAG_E_UNSUPPORTED, "sage_backward: d_out too large for the input-gradient product");
     SAG_TRY(check_dense("sage_backward H_ext", H_ext, agg ? n_local : n_ext, d_in, ldh, dt));
     SAG_TRY(check_dense("sage_backward G_out", G_out, n_local, d_out, ldg, dt));
     if (relu) SAG_TRY(check_dense("sage_backward Y", Y, n_local, d_out, ldg, dt));

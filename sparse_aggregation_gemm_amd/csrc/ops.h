@@ -56,6 +56,9 @@ struct NLayout {
 };
 
 size_t packed_b_bytes(int64_t k1, int64_t k2, int64_t n_total, sag_dtype dt);
+// True when an NN product over K blocks (k1, k2) keeps its weight slice in
+// LDS (K up to about 1024 fp32 or 2048 bf16 elements).
+bool nn_k_fits(int64_t k1, int64_t k2, sag_dtype dt);
 sag_status pack_b(const PackSrc& src, int64_t k1, int64_t k2, const NLayout& nl, sag_dtype dt,
                   void* Bp, hipStream_t s);
 

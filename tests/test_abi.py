@@ -86,6 +86,25 @@ def test_host_side_validation():
                                       None, 0, fake, 1 << 20, None) == L.SAG_E_INVALID
     assert lib.sag_gemm(4, 4, fake, 4, 4, None, 0, 0, None, 0, fake, 4, 0, None, None, 0, 0, fake, None,
                         4, 3, fake, 1 << 20, None) == L.SAG_E_INVALID
+    # a width beyond what the dense products hold in LDS: refused before any launch
+    A.indptr = A.indices = A.values = fake
+    assert lib.sag_gcn_layer_forward(ctypes.byref(A), fake, 4096, 4096, fake, None, 16, 1, 0, None, fake, 16,
+                                     None, 0, fake, 1 << 30, None) == L.SAG_E_UNSUPPORTED
+    assert lib.sag_sage_layer_forward(ctypes.byref(A), fake, 4096, 2048, fake, None, 4096, 1, 0, None, fake,
+                                      4096, None, 0, fake, 1 << 30, None) == L.SAG_E_UNSUPPORTED
+    # push / low-bit messages: bad bits, misaligned code rows, null outputs
+    assert lib.sag_code_row_bytes(128, 3) == 0 and lib.sag_code_row_bytes(128, 1) == 16
+    assert lib.sag_code_row_bytes(100, 8) == 112 and lib.sag_code_row_bytes(1, 2) == 16
+    assert lib.sag_quantize_rows(fake, 8, 0, None, 4, None, 4, 8, 3, 1, 0, fake, 16, fake, fake,
+                                 None) == L.SAG_E_INVALID
+    assert lib.sag_quantize_rows(fake, 8, 0, None, 4, None, 4, 8, 1, 1, 0, fake, 8, fake, fake,
+                                 None) == L.SAG_E_ALIGN
+    assert lib.sag_quantize_rows(fake, 8, 0, None, 4, None, 4, 8, 1, 1, 0, fake, 16, None, fake,
+                                 None) == L.SAG_E_INVALID
+    assert lib.sag_dequantize_rows(fake, 16, fake, fake, 4, 8, 4, None, 0, 0, 5, fake, 8, 4,
+                                   None) == L.SAG_E_INVALID
+    assert lib.sag_halo_push(fake, 8, None, 0, 4, 8, 0, 0, fake, 8, 4, None) == L.SAG_E_INVALID
+    assert lib.sag_halo_push(fake, 6, rows, 0, 4, 5, 0, 0, fake, 8, 4, None) == L.SAG_E_ALIGN
 
 
 def test_workspace_queries_are_host_only():
