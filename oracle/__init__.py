@@ -28,10 +28,15 @@ What it computes, in float64 unless noted, and where each step is defined:
   Philox4x32-10 counter-based generator for its draws, and DIGEST's push of
   a partition's rows into the representation store (plus the accumulating
   form used for halo gradients).
+* ``gat``        -- the graph-attention layer the pages name (GAT, Velickovic
+  et al. 2018; Sylvie, first section; DIGEST, evaluation section), in its
+  textbook form since the pages print no formulas: per-entry LeakyReLU
+  scores, a softmax over each row, the attention-weighted sum of the
+  transformed rows, heads concatenated, and its backward pass.
 
 Where the pages leave a step open, the reading taken is stated in the
 docstring of the function that takes it.  Every function is pinned by tests
 under ``tests/`` that do not re-type its formulas: closed forms, invariants,
 brute force on tiny inputs and finite differences.
 """
-from . import csr, layers, lowbit, native  # noqa: F401
+from . import csr, gat, layers, lowbit, native  # noqa: F401
