@@ -389,6 +389,90 @@ def halo_messages(sag, torch, np, n_store=4_000_000, n_halo=3_800_000, d=128, re
                                       "sample": f"{cpu_rows} rows x {d}, 1-bit, numpy, scaled to {n_halo} rows"}}
 
 
+def gat_layer(m, sag, torch, np, heads=4, reps=5, cpu_rows=4096):
+    """A graph-attention layer over the same partition and CSR pair (its
+    pattern only): d -> heads x d / heads with d the workload's hidden width,
+    ReLU, forward + backward, timed with HIP events over `reps` calls; the
+    oracle's GAT forward + backward on local rows [0, cpu_rows) beside it."""
+    from oracle import csr as ocsr, gat as ogat
+
+    w, dev = m.w, m.dev
+    d = w.dims[1]
+    dh = d // heads
+    F = heads * dh
+    A, AT = m.built.A, m.built.AT
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    H = sag.empty_dense(m.n_ext, d, m.tdt, dev)
+    H.copy_(torch.randn(m.n_ext, d, device=dev, generator=g))
+    lim = (6.0 / (d + F)) ** 0.5
+    W = ((torch.rand(d, F, device=dev, generator=g) * 2 - 1) * lim).to(m.tdt).contiguous()
+    la = (6.0 / (dh + 1)) ** 0.5
+    a_src = (torch.rand(heads, dh, device=dev, generator=g) * 2 - 1) * la
+    a_dst = (torch.rand(heads, dh, device=dev, generator=g) * 2 - 1) * la
+    b = torch.rand(F, device=dev, generator=g) * 0.2 - 0.1
+    G = sag.empty_dense(m.n_l, F, m.tdt, dev)
+    G.copy_(torch.randn(m.n_l, F, device=dev, generator=g))
+    Out = sag.empty_dense(m.n_l, F, m.tdt, dev)
+    dH = sag.empty_dense(m.n_ext, d, m.tdt, dev)
+    L = sag._lib.lib()
+    dt = sag.dtype_code(m.tdt)
+    nws = max(L.sag_gat_forward_workspace_bytes(A.ref, d, heads, dh, dt),
+              L.sag_gat_backward_workspace_bytes(A.ref, AT.ref, d, heads, dh, dt), 256)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+
+    def run():
+        out, ctx = sag.gat_layer_forward(A, H, W, a_src, a_dst, b, heads=heads, relu=True, Out=Out, ws=ws)
+        sag.gat_layer_backward(ctx, A, AT, out, G, dH=dH, ws=ws)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    sag.trace_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        run()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / reps
+    sag.trace_enable(False)
+    recs = sag.trace_records(clear=True)
+    ops = {}
+    for r in recs:
+        o = ops.setdefault(r["name"], {"n": 0, "ms": 0.0, "bytes": r["bytes"]})
+        o["n"] += 1
+        o["ms"] += r["ms"]
+    table = []
+    for name, o in ops.items():
+        avg = o["ms"] / o["n"]
+        gbs = o["bytes"] / avg / 1e6 if avg > 0 else None
+        table.append({"op": name, "launches": o["n"] / reps, "avg_ms": round(avg, 4),
+                      "ms_per_layer": round(o["ms"] / reps, 4), "GBps": round(gbs, 1) if gbs else None,
+                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 3) if gbs else None})
+    table.sort(key=lambda t: -t["ms_per_layer"])
+    del H, W, G, Out, dH, ws
+    torch.cuda.empty_cache()
+
+    # the oracle on a bounded sample of the same graph
+    src, dst = w.edges
+    R = min(cpu_rows, m.n_l)
+    ob = ocsr.build(src, dst, w.n_global, w.lo, w.lo + R, w.symmetrize, w.self_loops, "none")
+    rg = np.random.default_rng(0)
+    Hc = rg.standard_normal((ob.A.n_cols, d))
+    Wc = rg.uniform(-lim, lim, (d, F))
+    ac = rg.uniform(-la, la, (2, heads, dh))
+    Gc = rg.standard_normal((R, F))
+    t0 = time.perf_counter()
+    f = ogat.gat_forward(ob.A, Hc, Wc, ac[0], ac[1], None, heads, 0.2, True, store=w.dtype)
+    ogat.gat_backward(ob.A, Hc, Wc, ac[0], ac[1], heads, 0.2, True, f, f["Y"], Gc, store=w.dtype)
+    cpu_s = time.perf_counter() - t0
+    scale = m.n_l / R
+    return {"layer": f"GAT {d} -> {heads} x {dh}, ReLU", "dtype": w.dtype, "n_local": m.n_l,
+            "n_ext": m.n_ext, "nnz": A.nnz, "ms_fwd_bwd": round(ms, 3), "ops": table,
+            "cpu_baseline": {"value": round(cpu_s * scale * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+                             "sample": (f"local rows [0,{R}) as a partition ({ob.A.n_cols - R} halo columns), "
+                                        f"fwd+bwd in float64 took {cpu_s:.2f} s, scaled by {scale:.1f}")}}
+
+
 def main():
     args = parse()
     if args.summarize_counters:
@@ -479,6 +563,8 @@ def main():
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
             "seg_len": args.seg_len, "schedule": sag.csr_info(A)}
     build_ms = m.build_ms
+    log("[bench] graph-attention layer on the same partition")
+    gat = gat_layer(m, sag, torch, np)
     log("[bench] halo messages (pull, low-bit quantize/dequantize, push) at the 100M-graph share's shape")
     del m, A
     torch.cuda.empty_cache()
@@ -499,6 +585,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "halo_messages": halo,
+        "gat": gat,
     }
     print(json.dumps(out), flush=True)
 

@@ -361,6 +361,57 @@ sag_status sag_sage_layer_backward(const sag_csr* AT_mean, int64_t n_local,
                                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Graph-attention layer.  The pages name GAT (Velickovic et al., 2018) among
+ * the models that partitioned full-graph training serves (Sylvie, first
+ * section and results table; DIGEST, evaluation section) without printing
+ * its formulas; the layer is the paper's, with H heads of width d_head side
+ * by side (head k owns columns [k d_head, (k + 1) d_head), F = H d_head):
+ *   Wh = H_ext W;  x_vu = a_dst_k . Wh_k[v] + a_src_k . Wh_k[u] for each
+ *   entry (v, u) of A;  e = LeakyReLU(x) with negative slope `slope`;
+ *   alpha_v. = softmax of e_v. over row v;
+ *   Y_k[v] = sum_u alpha_vu Wh_k[u] + b;  Out = relu ? max(Y, 0) : Y.
+ * A's values are ignored (its pattern is the neighbourhood; build it with
+ * SAG_SELF_LOOPS to include each node itself, SAG_NORM_NONE suffices).
+ * dt as for the other layers; W is [d_in, F] (ld F); a_src, a_dst are fp32
+ * [H, d_head]; b fp32 [F] (nullable).  Out is [n_local, F] (ld ldo).
+ * `save` (sag_gat_save_bytes) keeps Wh, the per-head scores and the
+ * softmax normalisers (nothing per entry) for the backward call.
+ * Supported: 1 <= H <= 64, d_head a power-of-two number of 16-byte vectors
+ * (8, 16, ..., 512 bf16; 4, ..., 256 fp32), F at most 2048 bf16 / 1024 fp32,
+ * d_in within the transform's K limit; else SAG_E_UNSUPPORTED before any
+ * launch.  A needs a schedule for power-law rows (as the SpMM). */
+size_t sag_gat_save_bytes(int64_t n_local, int64_t n_ext, int64_t heads, int64_t d_head,
+                          sag_dtype dt);
+size_t sag_gat_forward_workspace_bytes(const sag_csr* A, int64_t d_in, int64_t heads,
+                                       int64_t d_head, sag_dtype dt);
+sag_status sag_gat_layer_forward(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
+                                 const void* W, const float* a_src, const float* a_dst,
+                                 const float* b, int64_t heads, int64_t d_head, float slope,
+                                 int relu, sag_dtype dt, void* Out, int64_t ldo,
+                                 void* save, size_t save_bytes,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* GAT backward: the gradients of <G_out, Out> by the chain rule through the
+ * same steps (softmax derivative, LeakyReLU' = 1 where x > 0, else slope;
+ * ReLU'(0) = 0):  dW fp32 [d_in, F] (ld F, nullable), da_src and da_dst fp32
+ * [H, d_head] (nullable), db fp32 [F] (nullable), dH_ext [n_ext, d_in] (ld
+ * ldd, type dt, nullable; its halo rows are what the partition returns to
+ * their owners).  A and AT are the forward's matrix and its transpose (AT
+ * from the same build); H_ext, W, a_src, a_dst, heads, d_head, slope, relu
+ * and save must be the forward's.  Y (forward Out, ld ldg as G_out) gives
+ * the ReLU mask. */
+size_t sag_gat_backward_workspace_bytes(const sag_csr* A, const sag_csr* AT, int64_t d_in,
+                                        int64_t heads, int64_t d_head, sag_dtype dt);
+sag_status sag_gat_layer_backward(const sag_csr* A, const sag_csr* AT, const void* H_ext,
+                                  int64_t ldh, int64_t d_in, const void* W, const float* a_src,
+                                  const float* a_dst, int64_t heads, int64_t d_head, float slope,
+                                  int relu, const void* Y, const void* G_out, int64_t ldg,
+                                  float* dW, float* da_src, float* da_dst, float* db,
+                                  void* dH_ext, int64_t ldd, sag_dtype dt,
+                                  const void* save, size_t save_bytes,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * Dense building blocks of the layers, exported for tests and for callers
  * that compose their own layers.
  *

@@ -102,10 +102,29 @@ def gat_forward(A: CSR, H_ext, W, a_src, a_dst, b, heads: int, slope: float, rel
     return dict(Wh=Wh, el=el, er=er, x=x, alpha=alpha, lse=lse, Agg=Agg, Y=Y, Out=Out)
 
 
-def gat_forward_den(A: CSR, fwd: dict, b, heads: int):
-    """Magnitude bound of Y: sum_u alpha |Wh_u| + |b|."""
+def score_magnitude(A: CSR, H_ext, W, a_src, a_dst, heads: int, lse):
+    """Per entry and head, the magnitude of the terms summed into the
+    exponent of alpha_vu: the score on absolute values (|a| . (|H| |W|) for
+    both ends, which also bounds the transform's own terms) plus |lse_v|.
+    A relative perturbation eps of those terms moves alpha_vu by a factor
+    of about 1 + eps * (this magnitude)."""
+    HW = np.abs(np.asarray(H_ext, np.float64)) @ np.abs(np.asarray(W, np.float64))
+    H3 = _heads(HW, heads)
+    sl = np.einsum("nkd,kd->nk", H3, np.abs(np.asarray(a_src, np.float64)).reshape(heads, -1))
+    sr = np.einsum("nkd,kd->nk", H3, np.abs(np.asarray(a_dst, np.float64)).reshape(heads, -1))
+    rows = A.row_ids()
+    return sr[rows] + sl[A.indices] + np.abs(lse[rows])
+
+
+def gat_forward_den(A: CSR, fwd: dict, b, heads: int, H_ext, W, a_src, a_dst, score_weight: float = 0.0):
+    """Magnitude bound of Y: sum_u alpha_vu (1 + w S_vu) |Wh_u| + |b|, S the
+    score magnitude and w = score_weight.  With w = 0 it is the plain
+    magnitude of the summed terms; a caller that allows a relative error
+    tol adds the rounding of the weights' exponent (absolute error about
+    n eps S for n-term fp32 sums) with w = n eps / tol."""
     W3 = np.abs(_heads(fwd["Wh"], heads))
-    Aggd = np.concatenate([_alpha_matrix(A, fwd["alpha"][:, k]) @ W3[:, k, :] for k in range(heads)], axis=1)
+    ad = fwd["alpha"] * (1.0 + score_weight * score_magnitude(A, H_ext, W, a_src, a_dst, heads, fwd["lse"]))
+    Aggd = np.concatenate([_alpha_matrix(A, ad[:, k]) @ W3[:, k, :] for k in range(heads)], axis=1)
     return Aggd + (0.0 if b is None else np.abs(np.asarray(b, np.float64)))
 
 
@@ -156,12 +175,14 @@ def gat_backward(A: CSR, H_ext, W, a_src, a_dst, heads: int, slope: float, relu:
 
 
 def gat_backward_den(A: CSR, H_ext, W, a_src, a_dst, heads: int, slope: float, relu: bool, fwd: dict,
-                     Ymask, G):
+                     Ymask, G, score_weight: float = 0.0):
     """The backward expressions on absolute values (the softmax derivative's
-    difference becomes a sum)."""
+    difference becomes a sum), with alpha scaled by 1 + w S as in the
+    forward bound."""
     n_l, n_ext = A.n_rows, A.n_cols
     rows = A.row_ids()
-    alpha, x, Wh = fwd["alpha"], fwd["x"], np.abs(fwd["Wh"])
+    x, Wh = fwd["x"], np.abs(fwd["Wh"])
+    alpha = fwd["alpha"] * (1.0 + score_weight * score_magnitude(A, H_ext, W, a_src, a_dst, heads, fwd["lse"]))
     G = np.abs(np.asarray(G, np.float64))
     GY = G * (np.asarray(Ymask) > 0) if relu else G
     dalpha = _edge_dot(A, GY, Wh, heads)

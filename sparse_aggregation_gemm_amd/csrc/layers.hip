@@ -27,13 +27,6 @@ namespace sag {
 namespace {
 
 inline bool aggregate_first(int64_t d_in, int64_t d_out) { return d_in <= d_out; }
-// Leading dimension of the library's own dense buffers: rows wider than 64
-// bytes start on a 128-byte cache line and span whole lines, so a gathered
-// row touches as few lines as possible; narrower rows are padded to 16 bytes.
-inline int64_t ldv(int64_t d, sag_dtype dt) {
-    const int64_t e = elt_size(dt), bytes = (d > 0 ? d : 1) * e;
-    return (bytes > 64 ? round_up(bytes, 128) : round_up(bytes, 16)) / e;
-}
 
 struct LayerWs {
     void* Bp = nullptr;
@@ -59,10 +52,6 @@ LayerWs carve(void* ws, size_t bytes, size_t bp, size_t t1, size_t t2, size_t sp
     w.tn_bytes = tn;
     w.total = c.used();
     return w;
-}
-
-size_t dense_bytes(int64_t rows, int64_t d, sag_dtype dt) {
-    return static_cast<size_t>(rows > 0 ? rows : 0) * ldv(d, dt) * elt_size(dt);
 }
 
 sag_status check_layer_common(const char* who, const sag_csr* A, const void* H, int64_t ldh, int64_t d_in,

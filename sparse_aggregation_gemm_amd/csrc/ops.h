@@ -18,6 +18,17 @@ struct Epilogue {
     void* pre = nullptr;            // output type, same ld as the output; nullable
 };
 
+// Leading dimension of the library's own dense buffers: rows wider than 64
+// bytes start on a 128-byte cache line and span whole lines, so a gathered
+// row touches as few lines as possible; narrower rows are padded to 16 bytes.
+inline int64_t ldv(int64_t d, sag_dtype dt) {
+    const int64_t e = elt_size(dt), bytes = (d > 0 ? d : 1) * e;
+    return (bytes > 64 ? round_up(bytes, 128) : round_up(bytes, 16)) / e;
+}
+inline size_t dense_bytes(int64_t rows, int64_t d, sag_dtype dt) {
+    return static_cast<size_t>(rows > 0 ? rows : 0) * ldv(d, dt) * elt_size(dt);
+}
+
 // ---- SpMM ----------------------------------------------------------------------
 // Y[r, :d] = sum_p val[p] X[idx[p], :d]  for every row of A, with the epilogue.
 size_t spmm_ws_bytes(const sag_csr& A, int64_t d);

@@ -373,6 +373,77 @@ def sage_layer_backward(ctx, AT, n_local, Y, G_out, want_dH=True, want_db=True, 
     return _layer_backward(ctx, AT, n_local, Y, G_out, want_dH, want_db, **kw)
 
 
+@dataclass
+class GatCtx:
+    """What the GAT forward hands to its backward."""
+    save: torch.Tensor
+    H_ext: torch.Tensor
+    W: torch.Tensor
+    a_src: torch.Tensor
+    a_dst: torch.Tensor
+    heads: int
+    d_head: int
+    slope: float
+    relu: bool
+
+
+def gat_layer_forward(A: Csr, H_ext, W, a_src, a_dst, b=None, heads=1, slope=0.2, relu=True,
+                      Out=None, ws=None):
+    """sag_gat_layer_forward: Out = act(concat_k sum_u alpha^k_vu (H_ext W)_k[u] + b).
+    W [d_in, heads * d_head]; a_src, a_dst fp32 [heads, d_head].  Returns (Out, ctx)."""
+    lib = L.lib()
+    dt = dtype_code(H_ext.dtype)
+    d_in = H_ext.shape[1]
+    F = W.shape[1]
+    if F % heads:
+        raise ValueError("W's width must be heads * d_head")
+    d_head = F // heads
+    dev = H_ext.device
+    W = W.contiguous()
+    a_src = a_src.to(torch.float32).contiguous()
+    a_dst = a_dst.to(torch.float32).contiguous()
+    if Out is None:
+        Out = empty_dense(A.n_rows, F, H_ext.dtype, dev)
+    save = _ws(lib.sag_gat_save_bytes(A.n_rows, A.n_cols, heads, d_head, dt), dev)
+    nws = lib.sag_gat_forward_workspace_bytes(A.ref, d_in, heads, d_head, dt)
+    if ws is None or ws.numel() < nws:
+        ws = _ws(nws, dev)
+    st = lib.sag_gat_layer_forward(A.ref, _ptr(H_ext), _ld(H_ext), d_in, _ptr(W), _ptr(a_src), _ptr(a_dst),
+                                   _ptr(b), heads, d_head, float(slope), int(relu), dt, _ptr(Out), _ld(Out),
+                                   _ptr(save), save.numel(), _ptr(ws), ws.numel(), _stream(dev))
+    L.check("sag_gat_layer_forward", st)
+    return Out, GatCtx(save, H_ext, W, a_src, a_dst, heads, d_head, float(slope), bool(relu))
+
+
+def gat_layer_backward(ctx: GatCtx, A: Csr, AT: Csr, Y, G_out, want_dH=True, dH=None, ws=None):
+    """sag_gat_layer_backward: returns (dW, da_src, da_dst, db, dH_ext)."""
+    lib = L.lib()
+    dt = dtype_code(G_out.dtype)
+    dev = G_out.device
+    d_in = ctx.H_ext.shape[1]
+    F = ctx.heads * ctx.d_head
+    dW = torch.empty((d_in, F), dtype=torch.float32, device=dev)
+    da_src = torch.empty((ctx.heads, ctx.d_head), dtype=torch.float32, device=dev)
+    da_dst = torch.empty((ctx.heads, ctx.d_head), dtype=torch.float32, device=dev)
+    db = torch.empty(F, dtype=torch.float32, device=dev)
+    if want_dH and dH is None:
+        dH = empty_dense(A.n_cols, d_in, G_out.dtype, dev)
+    if not want_dH:
+        dH = None
+    if ctx.relu and _ld(Y) != _ld(G_out):
+        raise ValueError("Y and G_out must share their leading dimension")
+    nws = lib.sag_gat_backward_workspace_bytes(A.ref, AT.ref, d_in, ctx.heads, ctx.d_head, dt)
+    if ws is None or ws.numel() < nws:
+        ws = _ws(nws, dev)
+    st = lib.sag_gat_layer_backward(
+        A.ref, AT.ref, _ptr(ctx.H_ext), _ld(ctx.H_ext), d_in, _ptr(ctx.W), _ptr(ctx.a_src), _ptr(ctx.a_dst),
+        ctx.heads, ctx.d_head, ctx.slope, int(ctx.relu), _ptr(Y) if ctx.relu else None, _ptr(G_out),
+        _ld(G_out), _ptr(dW), _ptr(da_src), _ptr(da_dst), _ptr(db), _ptr(dH), _ld(dH) if dH is not None else 0,
+        dt, _ptr(ctx.save), ctx.save.numel(), _ptr(ws), ws.numel(), _stream(dev))
+    L.check("sag_gat_layer_backward", st)
+    return dW, da_src, da_dst, db, dH
+
+
 # ---- dense building blocks ------------------------------------------------------------
 
 def gemm(A1, B, A2=None, mask=None, trans_b=False, bias=None, addend=None, relu=False,

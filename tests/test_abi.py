@@ -105,6 +105,28 @@ def test_host_side_validation():
                                    None) == L.SAG_E_INVALID
     assert lib.sag_halo_push(fake, 8, None, 0, 4, 8, 0, 0, fake, 8, 4, None) == L.SAG_E_INVALID
     assert lib.sag_halo_push(fake, 6, rows, 0, 4, 5, 0, 0, fake, 8, 4, None) == L.SAG_E_ALIGN
+    # GAT: head widths the lane layout cannot take, too many heads, bad dtype
+    # or slope, a transpose of another shape
+    B = L.SagCsr()
+    B.n_rows, B.n_cols, B.nnz = 10, 12, 5
+    B.indptr = B.indices = fake
+    f32 = ctypes.c_float
+
+    def gat_fwd(heads, dh, dt, slope=0.2):
+        return lib.sag_gat_layer_forward(ctypes.byref(B), fake, 16, 16, fake, fake, fake, None, heads, dh,
+                                         f32(slope), 1, dt, fake, 1024, fake, 1 << 30, fake, 1 << 30, None)
+    assert gat_fwd(2, 12, 1) == L.SAG_E_UNSUPPORTED      # bf16 d_head not a whole number of vectors
+    assert gat_fwd(2, 24, 1) == L.SAG_E_UNSUPPORTED      # 3 vectors: not a power of two
+    assert gat_fwd(65, 8, 1) == L.SAG_E_UNSUPPORTED
+    assert gat_fwd(2, 8, 5) == L.SAG_E_INVALID
+    assert gat_fwd(0, 8, 1) == L.SAG_E_INVALID
+    assert gat_fwd(2, 8, 1, float("nan")) == L.SAG_E_INVALID
+    BT = L.SagCsr()
+    BT.n_rows, BT.n_cols, BT.nnz = 12, 10, 6
+    BT.indptr = BT.indices = fake
+    assert lib.sag_gat_layer_backward(ctypes.byref(B), ctypes.byref(BT), fake, 16, 16, fake, fake, fake, 2, 8,
+                                      f32(0.2), 1, fake, fake, 16, fake, fake, fake, fake, fake, 16, 1, fake,
+                                      1 << 30, fake, 1 << 30, None) == L.SAG_E_INVALID
 
 
 def test_workspace_queries_are_host_only():
@@ -119,3 +141,7 @@ def test_workspace_queries_are_host_only():
     assert lib.sag_gcn_save_bytes(100, 64, 16, 0) == 0              # transform first: nothing
     assert lib.sag_sage_save_bytes(100, 100, 256, 1) == 100 * 128 * 2   # rows padded to 128-B lines
     assert lib.sag_gemm_tn_workspace_bytes(10000, 512, 256, 1) > 0
+    # GAT save: Wh (64-B bf16 rows), then el, er [n_ext, heads] and lse [n_local, heads], 256-B aligned
+    assert lib.sag_gat_save_bytes(100, 150, 4, 8, 1) == 9728 + 2560 + 2560 + 1792
+    assert lib.sag_gat_save_bytes(100, 150, 4, 12, 1) == 0
+    assert lib.sag_gat_forward_workspace_bytes(ctypes.byref(A), 64, 4, 8, 1) > 0

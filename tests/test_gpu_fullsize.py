@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import gen
-from oracle import csr as ocsr, layers as olay
+from oracle import csr as ocsr, gat as ogat, layers as olay
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -115,17 +115,26 @@ def _release():
 
 
 # (workload, layer): layer None is the build check; each workload's cases are
-# consecutive so its graph is drawn and built once
-CASES = [(2, None), (2, 0), (2, 1), (3, None), (3, 0), (4, None), (4, 0), (4, 1), (4, 2), (5, None), (5, 0)]
+# consecutive so its graph is drawn and built once; "gat" runs a graph-
+# attention layer on the same graph (its pattern only)
+CASES = [(2, None), (2, 0), (2, 1), (3, None), (3, 0), (4, None), (4, 0), (4, 1), (4, 2), (4, "gat"),
+         (5, None), (5, 0), (5, "gat")]
+# graph-attention layer per workload: (d_in, heads, d_head)
+GAT = {4: (256, 4, 64), 5: (128, 4, 32)}
 
 
-@pytest.mark.parametrize("cfg,layer", CASES,
-                         ids=[f"workload{c}-" + ("build" if l is None else f"layer{l}") for c, l in CASES])
+def _case_id(c, l):
+    return f"workload{c}-" + ("build" if l is None else (l if isinstance(l, str) else f"layer{l}"))
+
+
+@pytest.mark.parametrize("cfg,layer", CASES, ids=[_case_id(c, l) for c, l in CASES])
 def test_full_size(cfg, layer):
     full = _full(cfg)
-    assert full.w.n_layers == max(l for c, l in CASES if c == cfg and l is not None) + 1
+    assert full.w.n_layers == max(l for c, l in CASES if c == cfg and isinstance(l, int)) + 1
     if layer is None:
         check_build(full)
+    elif layer == "gat":
+        check_gat(full, *GAT[cfg])
     else:
         check_layer(full, layer)
 
@@ -245,6 +254,90 @@ def check_layer(full, layer):
     gi = full.gpu_row(uniq)
     e_dh = np.max(np.abs(got[gi] - ref) / (den + 1e-30))
     assert e_dh <= tol(dt), f"dH err {e_dh:.2e}"
+    others = np.ones(got.shape[0], bool)
+    others[gi] = False
+    assert np.all(got[others] == 0.0), "rows outside the sampled neighbourhoods must be zero"
+
+
+def check_gat(full, d_in, heads, dh):
+    """The graph-attention layer over the whole partition; the forward on
+    sampled rows, the backward with an upstream gradient supported on a
+    second row sample (its exact references come from the small CSR of
+    those rows and their neighbours: entries of other rows carry zero
+    gradient and contribute nothing)."""
+    w = full.w
+    dt = w.dtype
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    F = heads * dh
+    g = np.random.default_rng(1000 + w.cfg)
+    n_l, n_h = full.n_l, full.halo.size
+    say(f"full-size GAT layer of workload {w.cfg}: {d_in} -> {heads} x {dh} {dt}")
+    feats = _bits_or_f32(g.standard_normal((n_l, d_in), dtype=np.float32), dt)
+    stale = _bits_or_f32(g.standard_normal((max(w.stale_rows, 1), d_in), dtype=np.float32), dt) \
+        if n_h else None
+    lim = np.sqrt(6.0 / (d_in + F))
+    W = _bits_or_f32(g.uniform(-lim, lim, (d_in, F)), dt)
+    la = np.sqrt(6.0 / (dh + 1))
+    a_src = g.uniform(-la, la, (heads, dh)).astype(np.float32)
+    a_dst = g.uniform(-la, la, (heads, dh)).astype(np.float32)
+    b = g.uniform(-0.1, 0.1, F).astype(np.float32)
+
+    H_ext = sag.empty_dense(n_l + n_h, d_in, tdt, DEV)
+    H_ext[:n_l].copy_(to_dev_dense(feats, dt))
+    if n_h:
+        sag.halo_gather(to_dev_dense(stale, dt), full.gb.halo_gid, H_ext[n_l:], row_base=w.stale_base)
+    Out, ctx = sag.gat_layer_forward(full.gb.A, H_ext, to_dev_dense(W, dt).contiguous(), to_dev(a_src),
+                                     to_dev(a_dst), to_dev(b), heads=heads, relu=True)
+
+    def h_of(gid):
+        gid = np.asarray(gid, np.int64)
+        local = (gid >= w.lo) & (gid < w.hi)
+        out = np.empty((gid.size, d_in), np.float64)
+        out[local] = olay.as_f64(feats[gid[local] - w.lo], dt)
+        if (~local).any():
+            out[~local] = olay.as_f64(stale[gid[~local] - w.stale_base], dt)
+        return out
+
+    W64 = olay.as_f64(W, dt)
+    rows = full.sample(300, seed=31)
+    A_s, ext = full.mini(rows)
+    H_s = h_of(ext)
+    f = ogat.gat_forward(A_s, H_s, W64, a_src, a_dst, b, heads, 0.2, True, store=dt)
+    sw = (d_in + dh + 8) * 2.0 ** -24 / tol(dt)     # rounding of the softmax weights' exponent
+    Yd = ogat.gat_forward_den(A_s, f, b, heads, H_s, W64, a_src, a_dst, sw)
+    e_out = np.max(np.abs(f64(Out)[rows - w.lo] - f["Out"]) / (Yd + 1e-30))
+    say(f"  forward err {e_out:.1e}")
+    assert e_out <= tol(dt), f"forward err {e_out:.2e}"
+
+    rows_b = full.sample(120, seed=41, n_extreme=2)
+    A_b, ext_b = full.mini(rows_b)
+    H_b = h_of(ext_b)
+    fb = ogat.gat_forward(A_b, H_b, W64, a_src, a_dst, b, heads, 0.2, True, store=dt)
+    Gb = _bits_or_f32(g.standard_normal((len(rows_b), F), dtype=np.float32), dt)
+    Ymask = round_to(fb["Y"], dt)
+    G_full = np.zeros((n_l, F), np.uint16 if dt == "bf16" else np.float32)
+    Y_full = np.zeros_like(G_full)
+    G_full[rows_b - w.lo] = Gb
+    Y_full[rows_b - w.lo] = Ymask
+    dW, da_src, da_dst, db, dH = sag.gat_layer_backward(ctx, full.gb.A, full.gb.AT, to_dev_dense(Y_full, dt),
+                                                        to_dev_dense(G_full, dt))
+    Ym64, G64 = olay.as_f64(Ymask, dt), olay.as_f64(Gb, dt)
+    r = ogat.gat_backward(A_b, H_b, W64, a_src, a_dst, heads, 0.2, True, fb, Ym64, G64, store=dt)
+    d = ogat.gat_backward_den(A_b, H_b, W64, a_src, a_dst, heads, 0.2, True, fb, Ym64, G64, sw)
+    errs = {k: float(np.max(np.abs(f64(v) - r[k]) / (d[k] + 1e-30)))
+            for k, v in (("dW", dW), ("da_src", da_src), ("da_dst", da_dst), ("db", db))}
+    # dH_ext by global id (a sampled row is also a column of the small CSR)
+    uniq, inv = np.unique(ext_b, return_inverse=True)
+    ref = np.zeros((uniq.size, d_in))
+    den = np.zeros((uniq.size, d_in))
+    np.add.at(ref, inv, r["dH_ext"])
+    np.add.at(den, inv, d["dH_ext"])
+    got = f64(dH)
+    gi = full.gpu_row(uniq)
+    errs["dH_ext"] = float(np.max(np.abs(got[gi] - ref) / (den + 1e-30)))
+    say("  backward errors: " + " ".join(f"{k} {e:.1e}" for k, e in errs.items()))
+    for k, e in errs.items():
+        assert e <= tol(dt), f"{k} err {e:.2e}"
     others = np.ones(got.shape[0], bool)
     others[gi] = False
     assert np.all(got[others] == 0.0), "rows outside the sampled neighbourhoods must be zero"

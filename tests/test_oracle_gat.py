@@ -162,5 +162,5 @@ def test_backward_den_bounds_terms():
     d = gat.gat_backward_den(A, H, W, a_src, a_dst, 2, 0.2, True, f, f["Y"], G)
     for k in ("dWh", "da_src", "da_dst", "db", "dW", "dH_ext", "der", "dl"):
         assert np.all(np.abs(r[k]) <= d[k] * (1 + 1e-12) + 1e-300), k
-    yd = gat.gat_forward_den(A, f, bias, 2)
+    yd = gat.gat_forward_den(A, f, bias, 2, H, W, a_src, a_dst)
     assert np.all(np.abs(f["Y"]) <= yd * (1 + 1e-12))
