@@ -58,6 +58,8 @@ def parse():
     p.add_argument("--scale", type=float, default=1.0)
     p.add_argument("--seg-len", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--fusion", action="store_true",
+                   help="layers use the fused aggregate -> transform kernel where it applies")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU baseline sample (0: auto)")
     p.add_argument("--copy-calib", action="store_true",
                    help="run one 1 GiB identity row gather before the steps (a copy kernel of known "
@@ -389,6 +391,51 @@ def halo_messages(sag, torch, np, n_store=4_000_000, n_halo=3_800_000, d=128, re
                                       "sample": f"{cpu_rows} rows x {d}, 1-bit, numpy, scaled to {n_halo} rows"}}
 
 
+def fused_vs_separate(m, sag, torch, reps=5):
+    """The fused aggregate -> transform kernel against the separate SpMM and
+    MFMA product, at every layer of the workload that aggregates first
+    (same inputs, HIP events around `reps` calls of each)."""
+    w, dev = m.w, m.dev
+    A = m.built.A
+    out = []
+    for l in range(w.n_layers):
+        d_in, d_out = w.dims[l], w.dims[l + 1]
+        self_rows = w.model == "sage"
+        if d_in > d_out:
+            continue
+        H = m.H0 if l == 0 else sag.empty_dense(m.n_ext, d_in, m.tdt, dev, fill=0.5)
+        Wt = m.W[l]
+        Z = sag.empty_dense(m.n_l, d_in, m.tdt, dev)
+        Out = sag.empty_dense(m.n_l, d_out, m.tdt, dev)
+
+        def fused():
+            sag.aggregate_transform(A, H, Wt, m.b[l], self_rows=self_rows, relu=w.relu[l], Out=Out, Z=Z)
+
+        def separate():
+            sag.spmm_csr(A, H, Y=Z)
+            if self_rows:
+                sag.gemm(H[: m.n_l], Wt, A2=Z, bias=m.b[l], relu=w.relu[l])
+            else:
+                sag.gemm(Z, Wt, bias=m.b[l], relu=w.relu[l])
+
+        row = {"layer": l, "d_in": d_in, "d_out": d_out}
+        for name, f in (("fused", fused), ("separate", separate)):
+            for _ in range(2):
+                f()
+            torch.cuda.synchronize()
+            sag.trace_enable(True)
+            for _ in range(reps):
+                f()
+            torch.cuda.synchronize()
+            sag.trace_enable(False)
+            recs = sag.trace_records(clear=True)
+            row[name + "_ms"] = round(sum(r["ms"] for r in recs if not r["name"].startswith("pack")) / reps, 4)
+        out.append(row)
+        del Z, Out
+    torch.cuda.empty_cache()
+    return out
+
+
 def gat_layer(m, sag, torch, np, heads=4, reps=5, cpu_rows=4096):
     """A graph-attention layer over the same partition and CSR pair (its
     pattern only): d -> heads x d / heads with d the workload's hidden width,
@@ -491,6 +538,7 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    sag.set_fusion(args.fusion)
     w = gen.make_config(args.config, args.scale)
     log(f"[bench] workload {w.name} (scale {args.scale}): drawing the graph")
     t0 = time.perf_counter()
@@ -561,8 +609,10 @@ def main():
     A = m.built.A
     conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
-            "seg_len": args.seg_len, "schedule": sag.csr_info(A)}
+            "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion}
     build_ms = m.build_ms
+    log("[bench] fused aggregate -> transform against the separate kernels")
+    fused = fused_vs_separate(m, sag, torch)
     log("[bench] graph-attention layer on the same partition")
     gat = gat_layer(m, sag, torch, np)
     log("[bench] halo messages (pull, low-bit quantize/dequantize, push) at the 100M-graph share's shape")
@@ -585,6 +635,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "halo_messages": halo,
+        "fused_aggregate_transform": fused,
         "gat": gat,
     }
     print(json.dumps(out), flush=True)

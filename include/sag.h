@@ -361,6 +361,34 @@ sag_status sag_sage_layer_backward(const sag_csr* AT_mean, int64_t n_local,
                                    void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * Fused aggregate -> transform (forward).  One kernel computes
+ *   Z = A H_ext  (as sag_spmm_csr, rounded once to dt; stored when Z != NULL)
+ *   Y = Z W + b                 (self = 0, the GCN layer's product)
+ *   Y = [H_ext[:n_local] | Z] W + b   (self = 1, GraphSAGE: W is [2 d_in, d_out])
+ *   Out = relu ? max(Y, 0) : Y  (Y_pre nullable, as for the layers)
+ * with the sum of each 32-row tile kept in LDS and multiplied by W on the
+ * matrix cores in the same kernel, so Z is not read back from HBM (the
+ * CAGNET page's local SpMM followed by the product with W, in one pass).
+ * dt, W, b, H_ext, Out and ld's as for the layers; Z is [n_local, d_in]
+ * (ld ldz).  Supported: d_out <= 256 and d_in up to about 1000 bf16 / 500
+ * fp32 elements (GraphSAGE: half that); else SAG_E_UNSUPPORTED before any
+ * launch.  After sag_set_fusion(1) the GCN and GraphSAGE forward calls use
+ * it by themselves when they aggregate first and the widths fit (off by
+ * default: on the 2.45M-node graph the separate SpMM and product are
+ * faster).  ws: sag_aggregate_transform_workspace_bytes (16-B aligned). */
+size_t sag_aggregate_transform_workspace_bytes(const sag_csr* A, int64_t d_in, int64_t d_out,
+                                               int self, sag_dtype dt);
+sag_status sag_aggregate_transform(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
+                                   const void* W, const float* b, int64_t d_out, int self,
+                                   int relu, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                   void* Z, int64_t ldz, void* ws, size_t ws_bytes, void* stream);
+/* Process-wide switch for the layers' use of the fused kernel (1: use it
+ * where it applies; 0, the default: separate SpMM and product).  Returns
+ * the previous setting.  Not synchronised with calls running on other
+ * host threads. */
+int sag_set_fusion(int enable);
+
+/* ---------------------------------------------------------------------------
  * Graph-attention layer.  The pages name GAT (Velickovic et al., 2018) among
  * the models that partitioned full-graph training serves (Sylvie, first
  * section and results table; DIGEST, evaluation section) without printing

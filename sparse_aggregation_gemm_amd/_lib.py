@@ -66,6 +66,10 @@ SIGNATURES = {
     "sag_sage_backward_workspace_bytes": (sz, [PCSR, i64, i64, i64, cint]),
     "sag_sage_layer_backward": (cint, [PCSR, i64, vp, i64, i64, vp, i64, cint, vp, vp, i64,
                                        vp, vp, vp, i64, cint, vp, sz, vp, sz, vp]),
+    "sag_aggregate_transform_workspace_bytes": (sz, [PCSR, i64, i64, cint, cint]),
+    "sag_aggregate_transform": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, cint, cint, vp, vp, i64,
+                                       vp, i64, vp, sz, vp]),
+    "sag_set_fusion": (cint, [cint]),
     "sag_gat_save_bytes": (sz, [i64, i64, i64, i64, cint]),
     "sag_gat_forward_workspace_bytes": (sz, [PCSR, i64, i64, i64, cint]),
     "sag_gat_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, vp, vp, i64, i64, ctypes.c_float, cint,

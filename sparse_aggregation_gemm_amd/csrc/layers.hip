@@ -29,6 +29,8 @@ namespace {
 inline bool aggregate_first(int64_t d_in, int64_t d_out) { return d_in <= d_out; }
 
 struct LayerWs {
+    void* fz = nullptr;    // fused aggregate -> transform
+    size_t fz_bytes = 0;
     void* Bp = nullptr;
     void* t1 = nullptr;    // dense temporary
     void* t2 = nullptr;    // dense temporary
@@ -40,9 +42,11 @@ struct LayerWs {
 };
 
 // Workspace layout shared by the size queries and the calls.
-LayerWs carve(void* ws, size_t bytes, size_t bp, size_t t1, size_t t2, size_t sp, size_t tn) {
+LayerWs carve(void* ws, size_t bytes, size_t bp, size_t t1, size_t t2, size_t sp, size_t tn, size_t fz = 0) {
     Carver c(ws, bytes);
     LayerWs w;
+    w.fz = c.take<char>(fz);
+    w.fz_bytes = fz;
     w.Bp = c.take<char>(bp);
     w.t1 = c.take<char>(t1);
     w.t2 = c.take<char>(t2);
@@ -72,7 +76,11 @@ sag_status check_layer_common(const char* who, const sag_csr* A, const void* H, 
 
 LayerWs gcn_fwd_ws(const sag_csr& A, int64_t d_in, int64_t d_out, sag_dtype dt, void* ws, size_t bytes) {
     const size_t bp = packed_b_bytes(d_in, 0, d_out, dt);
-    if (aggregate_first(d_in, d_out)) return carve(ws, bytes, bp, 0, 0, spmm_ws_bytes(A, d_in), 0);
+    if (aggregate_first(d_in, d_out)) {
+        const size_t fz = agg_transform_fits(d_in, d_out, false, dt) ? agg_transform_ws_bytes(A, d_in, d_out, false, dt)
+                                                                     : 0;
+        return carve(ws, bytes, bp, 0, 0, spmm_ws_bytes(A, d_in), 0, fz);
+    }
     return carve(ws, bytes, bp, dense_bytes(A.n_cols, d_out, dt), 0, spmm_ws_bytes(A, d_out), 0);
 }
 
@@ -96,8 +104,11 @@ LayerWs gcn_bwd_ws(const sag_csr* AT, int64_t n_local, int64_t d_in, int64_t d_o
 // ---- SAGE ---------------------------------------------------------------------------
 
 LayerWs sage_fwd_ws(const sag_csr& A, int64_t d_in, int64_t d_out, sag_dtype dt, void* ws, size_t bytes) {
-    if (aggregate_first(d_in, d_out))
-        return carve(ws, bytes, packed_b_bytes(d_in, d_in, d_out, dt), 0, 0, spmm_ws_bytes(A, d_in), 0);
+    if (aggregate_first(d_in, d_out)) {
+        const size_t fz = agg_transform_fits(d_in, d_out, true, dt) ? agg_transform_ws_bytes(A, d_in, d_out, true, dt)
+                                                                    : 0;
+        return carve(ws, bytes, packed_b_bytes(d_in, d_in, d_out, dt), 0, 0, spmm_ws_bytes(A, d_in), 0, fz);
+    }
     const int64_t np = ldv(d_out, dt);
     // t1 = [P | T], [n_ext, np + d_out]
     return carve(ws, bytes, packed_b_bytes(d_in, 0, np + d_out, dt), dense_bytes(A.n_cols, np + d_out, dt), 0,
@@ -168,6 +179,9 @@ extern "C" sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext,
     e.pre = Y_pre;
     if (aggregate_first(d_in, d_out)) {
         const int64_t ldz = ldv(d_in, dt);
+        if (fusion_enabled() && w.fz_bytes)
+            return agg_transform_run(*A, H_ext, ldh, d_in, W, b, d_out, false, relu, dt, Y_pre, Out, ldo, save, ldz,
+                                     w.fz, w.fz_bytes, s);
         SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldz, dt, Epilogue{}, w.spmm, w.spmm_bytes, s));
         GemmA a;
         a.a1 = save; a.lda1 = ldz; a.k1 = d_in; a.m1 = n_l;
@@ -316,6 +330,9 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
         nl.n0 = nl.nsplit = d_out;
         SAG_TRY(pack_b(src, d_in, d_in, nl, dt, w.Bp, s));
         const int64_t ldm = ldv(d_in, dt);
+        if (fusion_enabled() && w.fz_bytes)
+            return agg_transform_run(*A, H_ext, ldh, d_in, W, b, d_out, true, relu, dt, Y_pre, Out, ldo, save, ldm,
+                                     w.fz, w.fz_bytes, s);
         SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldm, dt, Epilogue{}, w.spmm, w.spmm_bytes, s));
         GemmA a;
         a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = n_l;

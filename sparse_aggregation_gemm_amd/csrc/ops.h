@@ -36,6 +36,21 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
                     int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, size_t ws_bytes,
                     hipStream_t s);
 sag_status check_csr(const char* name, const sag_csr* A);
+// Only the long rows of a scheduled A (nothing without a schedule): row j of
+// the long bin's sum goes to Y row j (compact), with no epilogue.
+sag_status spmm_long_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype dt, int64_t d, void* Y,
+                         int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
+
+// ---- fused aggregate -> transform ------------------------------------------------
+// Out = act(Z W + b) (self false) or act([H_ext[:n_rows] | Z] W + b) (self
+// true) with Z = A H_ext summed in LDS (Z stored when non-null).
+bool agg_transform_fits(int64_t d_in, int64_t d_out, bool self, sag_dtype dt);
+size_t agg_transform_ws_bytes(const sag_csr& A, int64_t d_in, int64_t d_out, bool self, sag_dtype dt);
+sag_status agg_transform_run(const sag_csr& A, const void* H_ext, int64_t ldh, int64_t d_in, const void* W,
+                             const float* b, int64_t d_out, bool self, int relu, sag_dtype dt, void* Y_pre, void* Out,
+                             int64_t ldo, void* Z, int64_t ldz, void* ws, size_t ws_bytes, hipStream_t s);
+// Whether the layers use the fused kernel where it applies (sag_set_fusion).
+bool fusion_enabled();
 
 // ---- dense products (MFMA) -------------------------------------------------------
 // Operand A of a GEMM: up to two column blocks along K, each [rows, K_i].

@@ -19,10 +19,13 @@
 // several independent 16-byte loads in flight.  Accumulation is fp32 in a
 // fixed order, so results are bitwise reproducible.
 #include "ops.h"
+#include "rowsum.h"
 #include "trace.h"
 
 namespace sag {
 namespace {
+
+using namespace rowsum;
 
 constexpr int kWaves = 4;
 
@@ -55,6 +58,7 @@ struct SpArgs {
     const int4* seg;          // segment records (long bin)
     const int32_t* seg0;      // segments per long row, prefix
     float* part;              // fp32 partial rows, ld = C * V
+    int compact_long;         // long rows only: output row j of the long bin at row j
     EpiArgs<YT> e;
 };
 
@@ -109,41 +113,6 @@ __device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int
         const int nq = min(VY, n - q);
         if (nq > 0) store_vals<YT>(e.y + row * e.ldy + col0 + q, a + q, nq);
     }
-}
-
-template <class XT>
-__device__ __forceinline__ uint4 load_x(const XT* X, int64_t ldx, int32_t c, int ch) {
-    return *reinterpret_cast<const uint4*>(X + static_cast<int64_t>(c) * ldx + ch * Vec<XT>::N);
-}
-
-template <class XT, int NV, int U>
-__device__ __forceinline__ void accumulate(const XT* X, int64_t ldx, const int (&ch)[NV],
-                                           const int32_t (&c)[U], const float (&w)[U],
-                                           const bool (&ok)[U], float (&acc)[NV][Vec<XT>::N]) {
-    constexpr int V = Vec<XT>::N;
-    uint4 x[U][NV];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int v = 0; v < NV; ++v) x[u][v] = load_x(X, ldx, c[u], ch[v]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            float f[V];
-            unpack<XT>(x[u][v], f);
-#pragma unroll
-            for (int k = 0; k < V; ++k) {
-                const float t = fmaf(w[u], f[k], acc[v][k]);
-                acc[v][k] = ok[u] ? t : acc[v][k];
-            }
-        }
-    }
-}
-
-__device__ __forceinline__ int64_t rec_start(const int4& r) {
-    return static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(r.z)) |
-                                (static_cast<uint64_t>(static_cast<uint32_t>(r.w)) << 32));
 }
 
 // ---- short rows: one group of G lanes per row -------------------------------
@@ -202,54 +171,6 @@ __device__ __forceinline__ void short_rows(const SpArgs<XT, YT>& p, int64_t bloc
         const int cv = v * G + gl;
         if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v]);
     }
-}
-
-// Sums entries [start, start + len) of one row across the whole wavefront:
-// group g takes entries g, g + P, ...; returns the full sum in group 0.
-template <class XT, int G, int NV>
-__device__ __forceinline__ void wave_row_sum(const XT* X, int64_t ldx, int C,
-                                             const int32_t* idx, const float* val, int64_t start, int len,
-                                             float (&acc)[NV][Vec<XT>::N]) {
-    constexpr int V = Vec<XT>::N;
-    constexpr int P = 64 / G;
-    constexpr int U = NV >= 4 ? 2 : (NV >= 2 ? 4 : 8);
-    const int lane = threadIdx.x & 63;
-    const int gl = lane % G, grp = lane / G;
-    int ch[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) ch[v] = min(v * G + gl, C - 1);
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-#pragma unroll
-        for (int k = 0; k < V; ++k) acc[v][k] = 0.f;
-    for (int j0 = 0; j0 < len; j0 += 64) {
-        const int jj = j0 + lane;
-        const bool mine = jj < len;
-        const int32_t c_my = mine ? idx[start + jj] : 0;
-        const float v_my = mine ? (val ? val[start + jj] : 1.f) : 0.f;
-        const int nh = min(64, len - j0);
-        for (int t = 0; t < nh; t += U * P) {
-            int32_t c[U];
-            float w[U];
-            bool ok[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int src = t + u * P + grp;
-                const int s2 = min(src, 63);
-                c[u] = __shfl(c_my, s2, 64);
-                w[u] = __shfl(v_my, s2, 64);
-                ok[u] = src < nh;
-            }
-            accumulate<XT, NV, U>(X, ldx, ch, c, w, ok, acc);
-        }
-    }
-    // add the P group sums with a fixed butterfly
-#pragma unroll
-    for (int off = G; off < 64; off <<= 1)
-#pragma unroll
-        for (int v = 0; v < NV; ++v)
-#pragma unroll
-            for (int k = 0; k < V; ++k) acc[v][k] += __shfl_xor(acc[v][k], off, 64);
 }
 
 // ---- medium rows: one wavefront per row ----------------------------------------
@@ -331,7 +252,7 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
     const int64_t j = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
     if (j >= p.n_long) return;
     const int lane = threadIdx.x & 63;
-    const int64_t row = p.rec_long[j].x;
+    const int64_t row = p.compact_long ? j : p.rec_long[j].x;
     const int32_t s0 = p.seg0[j], s1 = p.seg0[j + 1];
     const int64_t ldp = static_cast<int64_t>(p.C) * V;
     for (int ch = lane; ch < p.C; ch += 64) {
@@ -354,7 +275,7 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
 }
 
 template <class XT, class YT, int G, int NV>
-sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s) {
+sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s, bool long_only) {
     constexpr int P = 64 / G;
     const int4* rec = reinterpret_cast<const int4*>(A.sched);
     if (!rec) {
@@ -370,6 +291,11 @@ sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s) {
         p.seg = rec + A.n_rows;
         p.seg0 = reinterpret_cast<const int32_t*>(rec + A.n_rows + A.n_seg);
         p.n_seg = A.n_long > 0 ? A.n_seg : 0;
+    }
+    if (long_only) {
+        if (!rec) return SAG_OK;
+        p.n_short = p.n_medium = 0;
+        p.compact_long = 1;
     }
     p.nb_seg = cdiv(p.n_seg, kWaves);
     p.nb_medium = cdiv(p.n_medium, kWaves);
@@ -388,7 +314,7 @@ sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s) {
 
 template <class XT, class YT>
 sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, void* Y, int64_t ldy,
-                     const Epilogue& epi, void* ws, hipStream_t s) {
+                     const Epilogue& epi, void* ws, hipStream_t s, bool long_only = false) {
     constexpr int V = Vec<XT>::N;
     SpArgs<XT, YT> p{};
     p.X = static_cast<const XT*>(X);
@@ -408,18 +334,26 @@ sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, vo
     p.e.relu = epi.relu;
     p.e.d = static_cast<int>(d);
     const int C = p.C;
-    if (C <= 4) return launch_bins<XT, YT, 4, 1>(A, p, s);
-    if (C <= 8) return launch_bins<XT, YT, 8, 1>(A, p, s);
-    if (C <= 16) return launch_bins<XT, YT, 16, 1>(A, p, s);
-    if (C <= 32) return launch_bins<XT, YT, 32, 1>(A, p, s);
-    if (C <= 64) return launch_bins<XT, YT, 64, 1>(A, p, s);
-    if (C <= 128) return launch_bins<XT, YT, 64, 2>(A, p, s);
-    if (C <= 192) return launch_bins<XT, YT, 64, 3>(A, p, s);
-    if (C <= 256) return launch_bins<XT, YT, 64, 4>(A, p, s);
+    if (C <= 4) return launch_bins<XT, YT, 4, 1>(A, p, s, long_only);
+    if (C <= 8) return launch_bins<XT, YT, 8, 1>(A, p, s, long_only);
+    if (C <= 16) return launch_bins<XT, YT, 16, 1>(A, p, s, long_only);
+    if (C <= 32) return launch_bins<XT, YT, 32, 1>(A, p, s, long_only);
+    if (C <= 64) return launch_bins<XT, YT, 64, 1>(A, p, s, long_only);
+    if (C <= 128) return launch_bins<XT, YT, 64, 2>(A, p, s, long_only);
+    if (C <= 192) return launch_bins<XT, YT, 64, 3>(A, p, s, long_only);
+    if (C <= 256) return launch_bins<XT, YT, 64, 4>(A, p, s, long_only);
     return fail(SAG_E_UNSUPPORTED, "spmm: row width above 256 vectors of 16 bytes");
 }
 
 }  // namespace
+
+sag_status spmm_long_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype dt, int64_t d, void* Y, int64_t ldy,
+                         void* ws, size_t ws_bytes, hipStream_t s) {
+    if (!A.sched || A.n_long == 0 || d == 0) return SAG_OK;
+    if (ws_bytes < spmm_ws_bytes(A, d) || !ws) return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
+    if (dt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, Epilogue{}, ws, s, true);
+    return run_typed<float, float>(A, X, ldx, d, Y, ldy, Epilogue{}, ws, s, true);
+}
 
 sag_status check_csr(const char* name, const sag_csr* A) {
     const std::string n(name);

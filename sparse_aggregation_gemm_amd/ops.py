@@ -373,6 +373,43 @@ def sage_layer_backward(ctx, AT, n_local, Y, G_out, want_dH=True, want_db=True, 
     return _layer_backward(ctx, AT, n_local, Y, G_out, want_dH, want_db, **kw)
 
 
+def aggregate_transform(A: Csr, H_ext, W, b=None, self_rows=False, relu=True, want_pre=False, want_z=True,
+                        Out=None, Z=None, ws=None):
+    """sag_aggregate_transform: Out = act(Z W + b) or act([H_local | Z] W + b)
+    with Z = A H_ext summed and multiplied in one kernel.  Returns
+    (Out, Y_pre, Z)."""
+    lib = L.lib()
+    dt = dtype_code(H_ext.dtype)
+    d_in = H_ext.shape[1]
+    d_out = W.shape[1]
+    dev = H_ext.device
+    W = W.contiguous()
+    if Out is None:
+        Out = empty_dense(A.n_rows, d_out, H_ext.dtype, dev)
+    Y_pre = empty_dense(A.n_rows, d_out, H_ext.dtype, dev) if want_pre else None
+    if want_pre and _ld(Y_pre) != _ld(Out):
+        raise ValueError("Y_pre and Out must share their leading dimension")
+    if want_z and Z is None:
+        Z = empty_dense(A.n_rows, d_in, H_ext.dtype, dev)
+    if not want_z:
+        Z = None
+    nws = lib.sag_aggregate_transform_workspace_bytes(A.ref, d_in, d_out, int(bool(self_rows)), dt)
+    if ws is None or ws.numel() < nws:
+        ws = _ws(nws, dev)
+    st = lib.sag_aggregate_transform(A.ref, _ptr(H_ext), _ld(H_ext), d_in, _ptr(W), _ptr(b), d_out,
+                                     int(bool(self_rows)), int(relu), dt, _ptr(Y_pre), _ptr(Out), _ld(Out),
+                                     _ptr(Z), _ld(Z) if Z is not None else 0, _ptr(ws), ws.numel(),
+                                     _stream(dev))
+    L.check("sag_aggregate_transform", st)
+    return Out, Y_pre, Z
+
+
+def set_fusion(enable: bool) -> bool:
+    """sag_set_fusion: whether the layers use the fused kernel; returns the
+    previous setting."""
+    return bool(L.lib().sag_set_fusion(int(bool(enable))))
+
+
 @dataclass
 class GatCtx:
     """What the GAT forward hands to its backward."""
