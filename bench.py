@@ -391,6 +391,107 @@ def halo_messages(sag, torch, np, n_store=4_000_000, n_halo=3_800_000, d=128, re
                                       "sample": f"{cpu_rows} rows x {d}, 1-bit, numpy, scaled to {n_halo} rows"}}
 
 
+class TwoLayerShare:
+    """DIGEST on one GPU's share of the 100M-node graph: a 2-layer GCN
+    (128 -> 128 -> 128, bf16, ReLU) whose layer inputs take their halo rows
+    from per-layer stale stores (pull), whose fresh local rows go back into
+    the layer-1 store (push), and whose halo input gradients are added into
+    a gradient store (accumulating push).  `step(overlap)` runs forward and
+    backward either on one stream or with the pulls and the push on a second
+    stream: the layer-1 pull runs beside layer 0's forward and the push
+    beside layer 1, with events ordering every buffer they share."""
+
+    def __init__(self, sag, torch, np, scale, seed=3):
+        import gen
+        self.sag, self.torch = sag, torch
+        dev = torch.device("cuda:0")
+        w = gen.make_config(5, scale)
+        src, dst = w.edges
+        gb = sag.csr_build_normalize(torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), w.n_global,
+                                     w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
+        sag.csr_schedule(gb.A, 1024)
+        sag.csr_schedule(gb.AT, 1024)
+        self.gb, self.w = gb, w
+        n_l, n_h = gb.n_local, gb.n_halo
+        self.n_l, self.n_h = n_l, n_h
+        d = 128
+        bf = torch.bfloat16
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+
+        def dense(rows, fill_random=True):
+            t = sag.empty_dense(rows, d, bf, dev, fill=0.0)
+            if fill_random:
+                t.copy_(torch.randn(rows, d, device=dev, generator=g))
+            return t
+        # stale stores over all global ids of the share (local, then remote)
+        self.stores = [dense(w.n_global), dense(w.n_global)]
+        self.grad_store = dense(w.n_global, False)
+        self.H = [dense(n_l + n_h), dense(n_l + n_h, False)]
+        lim = (6.0 / (2 * d)) ** 0.5
+        self.W = [((torch.rand(d, d, device=dev, generator=g) * 2 - 1) * lim).to(bf).contiguous() for _ in range(2)]
+        self.b = [torch.rand(d, device=dev, generator=g) * 0.2 - 0.1 for _ in range(2)]
+        self.G = dense(n_l)
+        self.Out = dense(n_l, False)
+        self.local_ids = torch.arange(w.lo, w.hi, dtype=torch.int32, device=dev)
+        self.s1 = torch.cuda.Stream(device=dev)
+        self.e_end = torch.cuda.Event()
+        self.e_end.record()
+        self.grads = None
+
+    def step(self, overlap):
+        sag, torch = self.sag, self.torch
+        gb, n_l = self.gb, self.n_l
+        halo = gb.halo_gid
+        s0 = torch.cuda.current_stream()
+        s1 = self.s1 if overlap else s0
+        e0, e1, ef0, epush = (torch.cuda.Event() for _ in range(4))
+        with torch.cuda.stream(s1):
+            s1.wait_event(self.e_end)
+            sag.halo_gather(self.stores[0], halo, self.H[0][n_l:])
+            e0.record(s1)
+            sag.halo_gather(self.stores[1], halo, self.H[1][n_l:])
+            e1.record(s1)
+        s0.wait_event(e0)
+        _, _, ctx0 = sag.gcn_layer_forward(gb.A, self.H[0], self.W[0], self.b[0], relu=True, Out=self.H[1][:n_l])
+        ef0.record(s0)
+        with torch.cuda.stream(s1):
+            s1.wait_event(ef0)
+            sag.halo_push(self.H[1][:n_l], self.local_ids, self.stores[1])
+            epush.record(s1)
+        s0.wait_event(e1)
+        _, _, ctx1 = sag.gcn_layer_forward(gb.A, self.H[1], self.W[1], self.b[1], relu=True, Out=self.Out)
+        dW1, db1, dH1 = sag.gcn_layer_backward(ctx1, gb.AT, n_l, self.Out, self.G)
+        sag.halo_push(dH1[n_l:], halo, self.grad_store, accumulate=True)
+        dW0, db0, _ = sag.gcn_layer_backward(ctx0, gb.AT, n_l, self.H[1][:n_l], dH1[:n_l], want_dH=False)
+        s0.wait_event(epush)
+        self.e_end.record(s0)
+        self.grads = (dW0, db0, dW1, db1)
+
+
+def overlapped_pull(sag, torch, np, scale=0.25, steps=10):
+    """ms per step of TwoLayerShare with the pulls and the push on the
+    compute stream and on a second stream (HIP events around `steps` steps,
+    after two warmup steps of each)."""
+    net = TwoLayerShare(sag, torch, np, scale)
+    out = {"workload": f"2-layer GCN 128 -> 128 -> 128 bf16 on the 100M-graph share at scale {scale}",
+           "n_local": net.n_l, "n_halo": net.n_h, "nnz": net.gb.A.nnz}
+    for overlap in (False, True, False, True):
+        for _ in range(2):
+            net.step(overlap)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            net.step(overlap)
+        b.record()
+        torch.cuda.synchronize()
+        out["overlapped_ms" if overlap else "one_stream_ms"] = round(a.elapsed_time(b) / steps, 3)
+    del net
+    torch.cuda.empty_cache()
+    return out
+
+
 def fused_vs_separate(m, sag, torch, reps=5):
     """The fused aggregate -> transform kernel against the separate SpMM and
     MFMA product, at every layer of the workload that aggregates first
@@ -611,6 +712,8 @@ def main():
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
             "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion}
     build_ms = m.build_ms
+    log("[bench] DIGEST pull overlapped with compute (2-layer GCN on the 100M-graph share, scale 0.25)")
+    overlap = overlapped_pull(sag, torch, np)
     log("[bench] fused aggregate -> transform against the separate kernels")
     fused = fused_vs_separate(m, sag, torch)
     log("[bench] graph-attention layer on the same partition")
@@ -636,6 +739,7 @@ def main():
         "cpu_baseline": cpu,
         "halo_messages": halo,
         "fused_aggregate_transform": fused,
+        "overlapped_pull": overlap,
         "gat": gat,
     }
     print(json.dumps(out), flush=True)
