@@ -41,7 +41,7 @@ CALIB_KERNEL = "gather_rows<32>"   # the 512-byte-row instance
 CSRC = os.path.join(ROOT, "sparse_aggregation_gemm_amd", "csrc")
 # sources whose text decides each op family's kernels (a counter summary is
 # valid only for the sources it was taken on)
-OP_SOURCES = {"spmm": ["spmm.hip", "common.h", "ops.h"], "gemm_nn": ["gemm.hip", "common.h", "ops.h"],
+OP_SOURCES = {"spmm": ["spmm.hip", "rowsum.h", "common.h", "ops.h"], "gemm_nn": ["gemm.hip", "common.h", "ops.h"],
               "gemm_tn": ["gemm.hip", "common.h", "ops.h"], "gather": ["gather.hip", "common.h"]}
 
 
@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--scale", type=float, default=1.0)
     p.add_argument("--seg-len", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="time the step only (skip the overlapped-pull, fused-kernel, GAT and halo-message "
+                        "sections), e.g. for hardware-counter passes")
     p.add_argument("--fusion", action="store_true",
                    help="layers use the fused aggregate -> transform kernel where it applies")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU baseline sample (0: auto)")
@@ -712,16 +715,19 @@ def main():
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
             "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion}
     build_ms = m.build_ms
-    log("[bench] DIGEST pull overlapped with compute (2-layer GCN on the 100M-graph share, scale 0.25)")
-    overlap = overlapped_pull(sag, torch, np)
-    log("[bench] fused aggregate -> transform against the separate kernels")
-    fused = fused_vs_separate(m, sag, torch)
-    log("[bench] graph-attention layer on the same partition")
-    gat = gat_layer(m, sag, torch, np)
-    log("[bench] halo messages (pull, low-bit quantize/dequantize, push) at the 100M-graph share's shape")
+    overlap = fused = gat = halo = None
+    if not args.no_extras:
+        log("[bench] DIGEST pull overlapped with compute (2-layer GCN on the 100M-graph share, scale 0.25)")
+        overlap = overlapped_pull(sag, torch, np)
+        log("[bench] fused aggregate -> transform against the separate kernels")
+        fused = fused_vs_separate(m, sag, torch)
+        log("[bench] graph-attention layer on the same partition")
+        gat = gat_layer(m, sag, torch, np)
     del m, A
     torch.cuda.empty_cache()
-    halo = halo_messages(sag, torch, np)
+    if not args.no_extras:
+        log("[bench] halo messages (pull, low-bit quantize/dequantize, push) at the 100M-graph share's shape")
+        halo = halo_messages(sag, torch, np)
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle on a row sample)")
