@@ -502,6 +502,263 @@ __global__ __launch_bounds__(kNnWaves * 64, 1) void gemm_nn(AOperand<T> A, const
     }
 }
 
+// ---- NN with the weights in registers (bf16) -----------------------------------------
+// When K times the columns of a wavefront is at most 512 bf16 (K <= 512 and
+// N <= 256, or K <= 256 and N <= 512), each of the eight wavefronts keeps
+// the packed-B fragments of its output column blocks (blocks w and w + 8) in
+// registers for the whole kernel: 16 bytes per lane per k-step and block.
+// The workgroup then needs one LDS copy of a 32-row A tile for all N
+// columns, so A is read from HBM once (the LDS-resident kernel above reads
+// each A tile once per 128-column block).  Workgroups are persistent and
+// walk the tiles: the whole-line loads of the next PF tiles sit in
+// registers, the A tile is double-buffered in LDS (one barrier per tile),
+// and each wavefront stages and stores its own 32 x 32 output blocks with no
+// workgroup barrier.  Operand layout and epilogue as in gemm_nn (no addend).
+constexpr int kRwWaves = 8;
+constexpr int kRwRows = 32;
+constexpr int kRwStage = 32 * (64 + 16);          // bytes of one wavefront's staged 32 x 32 block
+
+template <int KS> constexpr int rw_atile() { return kRwRows * (KS * 32 + 16); }
+
+template <int KS, int NBW, bool MASK, int PF, int OCC>
+__global__ __launch_bounds__(kRwWaves * 64, OCC) void gemm_nn_rw(AOperand<uint16_t> A,
+                                                               const uint16_t* __restrict__ Bp, int64_t Kt,
+                                                               int64_t N, int NB, int64_t n_tiles,
+                                                               EpiT<uint16_t> e, const float* __restrict__ bias) {
+    using T = uint16_t;
+    constexpr int KU = KS * 2;                        // 16-byte units of a tile row
+    constexpr int UNITS = kRwRows * KU;
+    constexpr int NT = kRwWaves * 64;
+    constexpr int UPT = (UNITS + NT - 1) / NT;        // units per thread
+    constexpr int PITCH = KU * 16 + 16;               // tile row pitch (bytes)
+    constexpr int ATILE = rw_atile<KS>();
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds_raw[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, l32 = lane & 31;
+    unsigned char* stage = lds_raw + 2 * ATILE + wave * NBW * kRwStage;
+    const int64_t G = gridDim.x;
+    int64_t t = blockIdx.x;
+    if (t >= n_tiles) return;
+
+    uint4 w[NBW][KS];
+    bool has[NBW];
+#pragma unroll
+    for (int j = 0; j < NBW; ++j) {
+        const int nb = wave + kRwWaves * j;
+        has[j] = nb < NB;
+        const T* col = Bp + static_cast<int64_t>(nb * 32 + l32) * Kt + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            w[j][ks] = has[j] ? *reinterpret_cast<const uint4*>(col + ks * 16) : make_uint4(0, 0, 0, 0);
+    }
+
+    uint4 ra[PF][UPT], rm[MASK ? PF : 1][UPT];
+    auto issue = [&](auto slot_c, int64_t tile) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
+        if (tile >= n_tiles) return;
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int u = tid + i * NT;
+            if (UNITS % NT != 0 && u >= UNITS) continue;
+            const int64_t row = tile * kRwRows + u / KU;
+            const int64_t k0 = static_cast<int64_t>(u % KU) * 8;
+            ra[slot][i] = *A.addr(row, k0);
+            if constexpr (MASK) rm[slot][i] = *A.mask_addr(row, k0);
+        }
+    };
+    auto stash = [&](auto slot_c, int64_t tile, unsigned char* buf) __attribute__((always_inline)) {
+        constexpr int slot = decltype(slot_c)::value;
+        if (tile >= n_tiles) return;
+#pragma unroll
+        for (int i = 0; i < UPT; ++i) {
+            const int u = tid + i * NT;
+            if (UNITS % NT != 0 && u >= UNITS) continue;
+            const int r = u / KU, c = u % KU;
+            const int64_t row = tile * kRwRows + r;
+            uint4 v;
+            if constexpr (MASK) v = A.fix_masked(ra[slot][i], rm[slot][i], row, static_cast<int64_t>(c) * 8);
+            else v = A.fix(ra[slot][i], row, static_cast<int64_t>(c) * 8);
+            *reinterpret_cast<uint4*>(buf + r * PITCH + c * 16) = v;
+        }
+    };
+    auto compute = [&](int64_t tile, const unsigned char* buf) __attribute__((always_inline)) {
+        f32x16_t acc[NBW];
+#pragma unroll
+        for (int j = 0; j < NBW; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+        const unsigned char* arow = buf + l32 * PITCH + h * 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const uint4 a = *reinterpret_cast<const uint4*>(arow + ks * 32);
+#pragma unroll
+            for (int j = 0; j < NBW; ++j)
+                if (has[j])
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w[j][ks]),
+                                                                      __builtin_bit_cast(bf16x8_t, a), acc[j], 0, 0,
+                                                                      0);
+        }
+        // this wavefront's blocks: bias, one rounding, staged as row l32,
+        // columns 8q + 4h .. +3 of the block, then stored as 64-byte row pieces
+#pragma unroll
+        for (int j = 0; j < NBW; ++j) {
+            if (!has[j]) continue;
+            const int nb = wave + kRwWaves * j;
+            unsigned char* st = stage + j * kRwStage;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t c0 = nb * 32 + 8 * q + 4 * h;
+                float y[4];
+#pragma unroll
+                for (int t4 = 0; t4 < 4; ++t4)
+                    y[t4] = acc[j][4 * q + t4] + ((bias && c0 + t4 < N) ? bias[c0 + t4] : 0.f);
+                *reinterpret_cast<uint2*>(st + l32 * 80 + (8 * q + 4 * h) * 2) =
+                    make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            }
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = (lane >> 2) + 16 * i, c = lane & 3;
+                const int64_t grow = tile * kRwRows + r;
+                const int64_t col = static_cast<int64_t>(nb) * 32 + c * 8;
+                if (grow >= A.M || col >= N) continue;
+                uint4 v = *reinterpret_cast<const uint4*>(st + r * 80 + c * 16);
+                const int n = static_cast<int>(N - col < 8 ? N - col : 8);
+#pragma unroll
+                for (int pass = 0; pass < 2; ++pass) {
+                    T* dst;
+                    if (pass == 0) {
+                        if (!e.pre) continue;
+                        dst = e.pre;
+                    } else {
+                        dst = e.c;
+                        if (e.relu) {
+                            uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) {
+                                // zero negative values (not -0 or NaN, as max(y, 0) on the fp32 value)
+                                const uint32_t b = (q & 1) ? (wv[q / 2] >> 16) : (wv[q / 2] & 0xffffu);
+                                const uint32_t mag = b & 0x7fffu;
+                                if ((b & 0x8000u) && mag != 0u && mag <= 0x7f80u)
+                                    wv[q / 2] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
+                            }
+                            v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                        }
+                    }
+                    T* p = dst + grow * e.ldc + col;
+                    if (n == 8) {
+                        *reinterpret_cast<uint4*>(p) = v;
+                    } else {
+                        // a ragged last unit: whole 4-byte pairs, then the odd element
+                        const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int q = 0; q < 3; ++q)
+                            if (2 * q + 1 < n) reinterpret_cast<uint32_t*>(p)[q] = wv[q];
+                        if (n & 1) p[n - 1] = static_cast<T>(wv[n / 2] & 0xffffu);
+                    }
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+        }
+    };
+
+    // Register slot s holds tile t + s*G at the start.  Step k computes tile
+    // t_k from LDS buffer k % 2 after moving tile t_{k+1} into the other
+    // buffer and refilling its slot with tile t_{k+1+PF}; one barrier ends
+    // the step (every wavefront is then done with buffer k % 2 and tile
+    // t_{k+1} is complete in the other).
+    static_for<0, PF>([&](auto sc) __attribute__((always_inline)) { issue(sc, t + decltype(sc)::value * G); });
+    stash(std::integral_constant<int, 0>{}, t, lds_raw);
+    __syncthreads();
+    issue(std::integral_constant<int, 0>{}, t + PF * G);
+    int cur = 0;
+    bool done = false;
+    while (!done) {
+        static_for<0, PF>([&](auto sc) __attribute__((always_inline)) {
+            if (done) return;
+            constexpr int nx = (decltype(sc)::value + 1) % PF;
+            unsigned char* nbuf = lds_raw + (cur ^ 1) * ATILE;
+            stash(std::integral_constant<int, nx>{}, t + G, nbuf);
+            issue(std::integral_constant<int, nx>{}, t + (PF + 1) * G);
+            compute(t, lds_raw + cur * ATILE);
+            __syncthreads();
+            cur ^= 1;
+            t += G;
+            if (t >= n_tiles) done = true;
+        });
+    }
+}
+
+int device_cus();
+
+// Tiles in flight per workgroup and workgroups per CU: as many as the
+// registers allow next to the weight fragments.
+template <int KS, int NBW, bool MASK>
+constexpr int rw_pf() { return KS * NBW >= 32 ? (MASK ? 2 : 3) : (KS * NBW >= 16 ? (MASK ? 3 : 4) : 6); }
+template <int KS, int NBW, bool MASK>
+constexpr int rw_occ() { return KS * NBW <= 8 && !MASK ? 2 : 1; }
+
+template <int KS, int NBW, bool MASK>
+sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt, int64_t N,
+                        const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
+    constexpr int PF = rw_pf<KS, NBW, MASK>(), OCC = rw_occ<KS, NBW, MASK>();
+    const int NB = static_cast<int>(cdiv(N, 32));
+    const size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage;
+    static bool attr_set = false;
+    if (!attr_set) {
+        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, OCC>),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, 131072));
+        attr_set = true;
+    }
+    // persistent workgroups: exactly as many as are resident at once
+    static int per_cu = 0;
+    if (per_cu == 0) {
+        int nb = 0;
+        SAG_CHECK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &nb, reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, OCC>), kRwWaves * 64, lds));
+        per_cu = nb > 0 ? nb : 1;
+    }
+    const int64_t n_tiles = cdiv(ao.M, kRwRows);
+    int64_t grid = static_cast<int64_t>(device_cus()) * per_cu;
+    if (grid > n_tiles) grid = n_tiles;
+    gemm_nn_rw<KS, NBW, MASK, PF, OCC><<<dim3(static_cast<unsigned>(grid)), kRwWaves * 64, lds, s>>>(
+        ao, B, Kt, N, NB, n_tiles, e, bias);
+    SAG_LAUNCH_CHECK();
+    return SAG_OK;
+}
+
+// The register-resident kernel for bf16 without an addend when N > 128 and
+// K * (columns per wavefront) <= 512; returns SAG_E_UNSUPPORTED otherwise
+// (the caller then takes the LDS-resident kernel).
+sag_status try_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt, int64_t N,
+                     const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
+    if (e.add) return SAG_E_UNSUPPORTED;
+    const int64_t NB = cdiv(N, 32);
+    // up to 128 columns the LDS-resident kernel reads A once as well, and
+    // is faster (measured at 256 -> 111: 0.60 against 0.75 ms)
+    if (NB <= 4) return SAG_E_UNSUPPORTED;
+    const int nbw = NB <= kRwWaves ? 1 : (NB <= 2 * kRwWaves ? 2 : 0);
+    const bool m = ao.mask != nullptr;
+    if (nbw == 1) {
+        switch (Kt) {
+            case 128: return m ? launch_nn_rw<8, 1, true>(ao, B, Kt, N, e, bias, s) : launch_nn_rw<8, 1, false>(ao, B, Kt, N, e, bias, s);
+            case 256: return m ? launch_nn_rw<16, 1, true>(ao, B, Kt, N, e, bias, s) : launch_nn_rw<16, 1, false>(ao, B, Kt, N, e, bias, s);
+            // (a mask at K = 512 would spill the weight fragments)
+            case 512: return m ? SAG_E_UNSUPPORTED : launch_nn_rw<32, 1, false>(ao, B, Kt, N, e, bias, s);
+            default: return SAG_E_UNSUPPORTED;
+        }
+    }
+    if (nbw == 2) {
+        switch (Kt) {
+            case 128: return m ? launch_nn_rw<8, 2, true>(ao, B, Kt, N, e, bias, s) : launch_nn_rw<8, 2, false>(ao, B, Kt, N, e, bias, s);
+            case 256: return m ? launch_nn_rw<16, 2, true>(ao, B, Kt, N, e, bias, s) : launch_nn_rw<16, 2, false>(ao, B, Kt, N, e, bias, s);
+            default: return SAG_E_UNSUPPORTED;
+        }
+    }
+    return SAG_E_UNSUPPORTED;
+}
+
 // ---- TN (weight gradient) -----------------------------------------------------------
 // C[k, n] = sum over a chunk of rows m of A[m, k] B[m, n].  Tile: KT rows of C
 // (K up to 512 in one tile) by BNT columns; 8 wavefronts, WK along K by WN
@@ -918,6 +1175,12 @@ inline size_t nn_lds_bytes(int64_t bn, int64_t Kt, sag_dtype dt) {
     return static_cast<size_t>(bn) * Kt * elt_size(dt) + static_cast<size_t>(kNnWaves) * kNnTile;
 }
 
+#ifndef SAG_NN_RW
+#define SAG_NN_RW 1
+#endif
+int g_nn_rw = SAG_NN_RW;
+bool nn_rw_enabled() { return g_nn_rw != 0; }
+
 template <class T>
 sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dtype dt, void* C, int64_t ldc,
                     const Epilogue& epi, hipStream_t s) {
@@ -926,6 +1189,12 @@ sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dt
     EpiT<T> e{static_cast<T*>(C), ldc, static_cast<T*>(epi.pre), static_cast<const T*>(epi.addend),
               epi.ld_add, epi.addend ? epi.n_add : 0, epi.bias, epi.relu};
     const T* B = static_cast<const T*>(Bp);
+    if constexpr (sizeof(T) == 2) {
+        if (nn_rw_enabled()) {
+            const sag_status st = try_nn_rw(ao, B, Kt, N, e, epi.bias, s);
+            if (st != SAG_E_UNSUPPORTED) return st;
+        }
+    }
     // widest column block whose slice of B fits in LDS beside the tiles
     const size_t lds = max_lds_per_block();
     const int64_t n32 = round_up(N, 32);
