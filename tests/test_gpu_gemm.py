@@ -64,10 +64,38 @@ def test_gemm_two_blocks_mask_addend_transposed(dt):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_gemm_exact_integers(dt):
+@pytest.mark.parametrize("K1,K2,N,masked", [(256, 256, 256, False), (100, 100, 256, False), (256, 0, 512, True),
+                                            (47, 47, 150, False), (200, 0, 300, True)])
+def test_gemm_wide_outputs(dt, K1, K2, N, masked):
+    """Outputs wider than 128 columns (bf16 takes the kernel that keeps the
+    weight fragments in registers): two K blocks, the ReLU mask, ragged M
+    and N, pre-activation and output."""
+    g = np.random.default_rng(K1 + K2 + N)
+    M = 1031
+    _, A1 = _mat(g, (M, K1), dt)
+    A2 = _mat(g, (M, K2), dt)[1] if K2 else None
+    Mk = _mat(g, (M, K1), dt)[1] if masked else None
+    _, W = _mat(g, (K1 + K2, N), dt)
+    W = W.contiguous()
+    b = g.uniform(-0.1, 0.1, N).astype(np.float32)
+    say(f"gemm wide dt={dt} K={K1}+{K2} N={N} masked={masked}")
+    C, pre = sag.gemm(A1, W, A2=A2, mask=Mk, bias=to_dev(b), relu=True, want_pre=True)
+    A64 = f64(A1) * (f64(Mk) > 0) if masked else f64(A1)
+    if K2:
+        A64 = np.concatenate([A64, f64(A2)], 1)
+    W64 = f64(W)
+    ref = A64 @ W64 + b
+    den = np.abs(A64) @ np.abs(W64) + np.abs(b)
+    assert _err(f64(pre), ref, den) <= tol(dt)
+    assert _err(f64(C), np.maximum(ref, 0), den) <= tol(dt)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [80, 300])
+def test_gemm_exact_integers(dt, N):
     g = np.random.default_rng(4)
     _, A = _mat(g, (300, 96), dt, integers=True)
-    _, W = _mat(g, (96, 80), dt, integers=True)
+    _, W = _mat(g, (96, N), dt, integers=True)
     W = W.contiguous()
     say(f"gemm exact dt={dt}")
     C = sag.gemm(A, W)
