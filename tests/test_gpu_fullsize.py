@@ -117,8 +117,10 @@ def _release():
 # (workload, layer): layer None is the build check; each workload's cases are
 # consecutive so its graph is drawn and built once; "gat" runs a graph-
 # attention layer on the same graph (its pattern only)
-CASES = [(2, None), (2, 0), (2, 1), (3, None), (3, 0), (4, None), (4, 0), (4, 1), (4, 2), (4, "gat"),
-         (5, None), (5, 0), (5, "gat")]
+CASES = [(2, None), (2, 0), (2, 1), (3, None), (3, 0), (4, None), (4, 0), (4, 1), (4, 2), (4, "fused"),
+         (4, "gat"), (5, None), (5, 0), (5, "fused"), (5, "gat")]
+# "fused" runs the fused aggregate -> transform kernel at the widest
+# aggregate-first layer of the workload
 # graph-attention layer per workload: (d_in, heads, d_head)
 GAT = {4: (256, 4, 64), 5: (128, 4, 32)}
 
@@ -135,6 +137,8 @@ def test_full_size(cfg, layer):
         check_build(full)
     elif layer == "gat":
         check_gat(full, *GAT[cfg])
+    elif layer == "fused":
+        check_fused(full)
     else:
         check_layer(full, layer)
 
@@ -341,3 +345,56 @@ def check_gat(full, d_in, heads, dh):
     others = np.ones(got.shape[0], bool)
     others[gi] = False
     assert np.all(got[others] == 0.0), "rows outside the sampled neighbourhoods must be zero"
+
+
+def check_fused(full):
+    """The fused aggregate -> transform kernel over the whole partition at the
+    workload's widest aggregate-first layer; Out and the stored Z on ~300
+    sampled rows against the oracle's layer on the small CSR of those rows."""
+    w = full.w
+    shapes = [(l, d_in, d_out, relu) for l, d_in, d_out, relu in _layer_shapes(w) if d_in <= d_out]
+    _, d_in, d_out, relu = max(shapes, key=lambda t: t[1])
+    self_rows = w.model == "sage"
+    dt = w.dtype
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    g = np.random.default_rng(2000 + w.cfg)
+    n_l, n_h = full.n_l, full.halo.size
+    say(f"full-size fused aggregate -> transform, workload {w.cfg}: {d_in} -> {d_out} {dt}")
+    feats = _bits_or_f32(g.standard_normal((n_l, d_in), dtype=np.float32), dt)
+    stale = _bits_or_f32(g.standard_normal((max(w.stale_rows, 1), d_in), dtype=np.float32), dt) \
+        if n_h else None
+    w_rows = 2 * d_in if self_rows else d_in
+    lim = np.sqrt(6.0 / (w_rows + d_out))
+    W = _bits_or_f32(g.uniform(-lim, lim, (w_rows, d_out)), dt)
+    b = g.uniform(-0.1, 0.1, d_out).astype(np.float32)
+    H_ext = sag.empty_dense(n_l + n_h, d_in, tdt, DEV)
+    H_ext[:n_l].copy_(to_dev_dense(feats, dt))
+    if n_h:
+        sag.halo_gather(to_dev_dense(stale, dt), full.gb.halo_gid, H_ext[n_l:], row_base=w.stale_base)
+    Out, _, Z = sag.aggregate_transform(full.gb.A, H_ext, to_dev_dense(W, dt).contiguous(), to_dev(b),
+                                        self_rows=self_rows, relu=relu)
+
+    def h_of(gid):
+        gid = np.asarray(gid, np.int64)
+        local = (gid >= w.lo) & (gid < w.hi)
+        out = np.empty((gid.size, d_in), np.float64)
+        out[local] = olay.as_f64(feats[gid[local] - w.lo], dt)
+        if (~local).any():
+            out[~local] = olay.as_f64(stale[gid[~local] - w.stale_base], dt)
+        return out
+
+    W64 = olay.as_f64(W, dt)
+    rows = full.sample(300, seed=51)
+    A_s, ext = full.mini(rows)
+    H_s = h_of(ext)
+    if self_rows:
+        Zr, _, Or = olay.sage_forward(A_s, H_s, len(rows), W64, b, relu)
+        Zd, Yd = olay.sage_forward_den(A_s, H_s, len(rows), W64, b)
+    else:
+        Zr, _, Or = olay.gcn_forward(A_s, H_s, W64, b, relu)
+        Zd, Yd = olay.gcn_forward_den(A_s, H_s, W64, b)
+    li = rows - w.lo
+    e_out = np.max(np.abs(f64(Out)[li] - Or) / (Yd + 1e-30))
+    e_z = np.max(np.abs(f64(Z)[li] - Zr) / (Zd + 1e-30))
+    say(f"  errors: out {e_out:.1e} Z {e_z:.1e}")
+    assert e_out <= tol(dt) and e_z <= tol(dt), f"fused err out {e_out:.2e} Z {e_z:.2e}"
