@@ -18,14 +18,18 @@
 //   [u local] der[u] a_dst;  dW = H_ext^T dWh;  dH_ext = dWh W^T;
 //   da_src = sum_u del[u] Wh[u];  da_dst = sum_v der[v] Wh[v];  db = colsum G_Y.
 //
-// No per-entry array is ever stored: every pass recomputes alpha_vu from
-// el, er and lse (12 bytes per row and head) instead of keeping nnz * heads
-// floats.  Four sweeps over the entries share the SpMM's degree-binned
-// schedule and its lane layout (a group of G lanes covers one 16-byte-vector
-// row; short rows one group each, medium rows one wavefront, long rows cut
-// into segments whose fp32 partials a second kernel combines in order):
-//   lse  over A  : the row's softmax normaliser, merged online (max, sum);
-//   fwd  over A  : Out, gathering rows of Wh;
+// No per-entry array is ever stored: the backward sweeps recompute alpha_vu
+// from el, er and lse (12 bytes per row and head) instead of keeping
+// nnz * heads floats.  Three sweeps over the entries share the SpMM's
+// degree-binned schedule and its lane layout (a group of G lanes covers one
+// 16-byte-vector row; short rows one group each, medium rows one wavefront,
+// long rows cut into segments whose fp32 partials a second kernel combines
+// in order):
+//   fwd  over A  : Out and lse, gathering rows of Wh, with the softmax taken
+//                  online (a running max m, the sum s of exp(e - m) and the
+//                  accumulator, rescaled when m grows; partial states merge
+//                  by rescaling to the larger max), so no separate pass
+//                  computes the normalisers;
 //   bwa  over A  : c and der, gathering rows of Wh against the row's own G_Y;
 //   bwt  over AT : dWh and del of each row u of [local | halo], gathering
 //                  rows of G_Y and one 16-byte record {er, lse, c} per head.
@@ -41,7 +45,7 @@ namespace sag {
 namespace {
 
 constexpr int kWaves = 4;
-enum { M_LSE = 0, M_FWD = 1, M_BWA = 2, M_BWT = 3 };
+enum { M_FWD = 1, M_BWA = 2, M_BWT = 3 };
 
 struct GatArgs {
     const int64_t* indptr;
@@ -53,9 +57,9 @@ struct GatArgs {
     const int32_t* seg0;
     int64_t n_short, n_medium, n_long, n_seg;
     int64_t nb_seg, nb_medium;
-    int C;          // 16-byte vectors per row (the lse pass: one per head)
+    int C;          // 16-byte vectors per row
     int H;          // heads
-    int hshift;     // log2(vectors per head); 0 for the lse pass
+    int hshift;     // log2(vectors per head)
     float slope;
     const void* X;  // gathered rows: Wh (fwd, bwa) or G_Y (bwt)
     int64_t ldx;
@@ -96,14 +100,8 @@ __device__ __forceinline__ uint4 load_row_vec(const T* X, int64_t ld, int64_t r,
     return *reinterpret_cast<const uint4*>(X + r * ld + ch * Vec<T>::N);
 }
 
-// Online merge of (max, sum of exp(e - max)) pairs; an empty side is
-// (-inf, 0).
-__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
-    const float mn = fmaxf(m, m2);
-    if (mn == -INFINITY) return;
-    s = s * __expf(m - mn) + s2 * __expf(m2 - mn);
-    m = mn;
-}
+// exp(a - b) for a running max b >= a; an empty side (a = -inf) gives 0.
+__device__ __forceinline__ float rescale(float a, float b) { return a == -INFINITY ? 0.f : __expf(a - b); }
 
 // Per-lane state of one row sweep.
 template <int MODE, class T, int NV>
@@ -113,8 +111,8 @@ struct Lane {
     int hd[NV];        // head of that vector
     float acc[NV][V];  // fwd, bwt
     float own[NV][V];  // bwa: G_Y[v]; bwt: Wh[u]
-    float r0[NV], r1[NV];       // lse: er; fwd, bwa: er, lse; bwt: el
-    float s0[NV], s1[NV], s2[NV];  // lse: max, sum; bwa: c, P, Q; bwt: del
+    float r0[NV], r1[NV];       // fwd: er; bwa: er, lse; bwt: el
+    float s0[NV], s1[NV], s2[NV];  // fwd: running max, sum; bwa: c, P, Q; bwt: del
 };
 
 template <int MODE, class T, int NV>
@@ -124,7 +122,7 @@ __device__ __forceinline__ void lane_init(Lane<MODE, T, NV>& L, const GatArgs& p
         L.ch[v] = min(v * G + gl, p.C - 1);
         L.hd[v] = L.ch[v] >> p.hshift;
         L.r0[v] = L.r1[v] = 0.f;
-        L.s0[v] = MODE == M_LSE ? -INFINITY : 0.f;
+        L.s0[v] = MODE == M_FWD ? -INFINITY : 0.f;
         L.s1[v] = L.s2[v] = 0.f;
 #pragma unroll
         for (int k = 0; k < Lane<MODE, T, NV>::V; ++k) L.acc[v][k] = L.own[v][k] = 0.f;
@@ -138,9 +136,9 @@ __device__ __forceinline__ void lane_row(Lane<MODE, T, NV>& L, const GatArgs& p,
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int64_t rh = row * p.H + L.hd[v];
-        if constexpr (MODE == M_LSE) {
+        if constexpr (MODE == M_FWD) {
             L.r0[v] = p.er[rh];
-        } else if constexpr (MODE == M_FWD || MODE == M_BWA) {
+        } else if constexpr (MODE == M_BWA) {
             L.r0[v] = p.er[rh];
             L.r1[v] = p.lse[rh];
         } else {
@@ -182,33 +180,57 @@ __device__ __forceinline__ void lane_entries(Lane<MODE, T, NV>& L, const GatArgs
     for (int u = 0; u < U; ++u)
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            if constexpr (MODE != M_LSE) x[u][v] = load_row_vec(X, p.ldx, c[u], L.ch[v]);
+            x[u][v] = load_row_vec(X, p.ldx, c[u], L.ch[v]);
             if constexpr (MODE == M_BWT)
                 ri[u][v] = p.rinfo[static_cast<int64_t>(c[u]) * p.H + L.hd[v]];
             else
                 sc[u][v] = p.el[static_cast<int64_t>(c[u]) * p.H + L.hd[v]];
         }
+    if constexpr (MODE == M_FWD) {
+        // the batch's scores, one rescale of the state to the new max, then
+        // the entries' terms
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            float ev[U];
+            float bm = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const float xx = L.r0[v] + sc[u][v];
+                ev[u] = ok[u] ? xx * (xx > 0.f ? 1.f : p.slope) : -INFINITY;
+                bm = fmaxf(bm, ev[u]);
+            }
+            const float mn = fmaxf(L.s0[v], bm);
+            if (mn != -INFINITY) {
+                const float f = rescale(L.s0[v], mn);
+                L.s1[v] *= f;
+#pragma unroll
+                for (int k = 0; k < V; ++k) L.acc[v][k] *= f;
+                L.s0[v] = mn;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const float a = rescale(ev[u], mn);
+                    float f2[V];
+                    unpack<T>(x[u][v], f2);
+                    L.s1[v] += a;
+                    // (a select, not a zero weight: a dead entry reads row 0,
+                    // whatever it holds)
+#pragma unroll
+                    for (int k = 0; k < V; ++k) {
+                        const float t2 = fmaf(a, f2[k], L.acc[v][k]);
+                        L.acc[v][k] = ok[u] ? t2 : L.acc[v][k];
+                    }
+                }
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             float f[V];
-            if constexpr (MODE != M_LSE) unpack<T>(x[u][v], f);
-            if constexpr (MODE == M_LSE) {
-                const float xx = L.r0[v] + sc[u][v];
-                const float e = xx * (xx > 0.f ? 1.f : p.slope);
-                float m = L.s0[v], s = L.s1[v];
-                const float mn = fmaxf(m, e);
-                s = s * __expf(m - mn) + __expf(e - mn);
-                L.s0[v] = ok[u] ? mn : L.s0[v];
-                L.s1[v] = ok[u] ? s : L.s1[v];
-            } else if constexpr (MODE == M_FWD) {
-                const float xx = L.r0[v] + sc[u][v];
-                const float e = xx * (xx > 0.f ? 1.f : p.slope);
-                const float a = ok[u] ? __expf(e - L.r1[v]) : 0.f;
-#pragma unroll
-                for (int k = 0; k < V; ++k) L.acc[v][k] = fmaf(a, f[k], L.acc[v][k]);
-            } else {
+            unpack<T>(x[u][v], f);
+            {
                 float part = 0.f;
 #pragma unroll
                 for (int k = 0; k < V; ++k) part = fmaf(L.own[v][k], f[k], part);
@@ -218,16 +240,20 @@ __device__ __forceinline__ void lane_entries(Lane<MODE, T, NV>& L, const GatArgs
                     const float lam = xx > 0.f ? 1.f : p.slope;
                     const float a = ok[u] ? __expf(xx * lam - L.r1[v]) : 0.f;
                     const float al = a * lam;
-                    L.s0[v] = fmaf(a, dot, L.s0[v]);
-                    L.s1[v] = fmaf(al, dot, L.s1[v]);
+                    // (selects: a dead entry reads row 0, whatever it holds)
+                    L.s0[v] = ok[u] ? fmaf(a, dot, L.s0[v]) : L.s0[v];
+                    L.s1[v] = ok[u] ? fmaf(al, dot, L.s1[v]) : L.s1[v];
                     L.s2[v] += al;
                 } else {
                     const float xx = ri[u][v].x + L.r0[v];
                     const float lam = xx > 0.f ? 1.f : p.slope;
                     const float a = ok[u] ? __expf(xx * lam - ri[u][v].y) : 0.f;
-                    L.s0[v] = fmaf(a * lam, dot - ri[u][v].z, L.s0[v]);
+                    L.s0[v] = ok[u] ? fmaf(a * lam, dot - ri[u][v].z, L.s0[v]) : L.s0[v];
 #pragma unroll
-                    for (int k = 0; k < V; ++k) L.acc[v][k] = fmaf(a, f[k], L.acc[v][k]);
+                    for (int k = 0; k < V; ++k) {
+                        const float t2 = fmaf(a, f[k], L.acc[v][k]);
+                        L.acc[v][k] = ok[u] ? t2 : L.acc[v][k];
+                    }
                 }
             }
         }
@@ -291,11 +317,19 @@ __device__ __forceinline__ void sweep_wave(Lane<MODE, T, NV>& L, const GatArgs& 
     for (int off = G; off < 64; off <<= 1) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            if constexpr (MODE == M_LSE) {
+            if constexpr (MODE == M_FWD) {
                 const float m2 = __shfl_xor(L.s0[v], off, 64), s2 = __shfl_xor(L.s1[v], off, 64);
-                lse_merge(L.s0[v], L.s1[v], m2, s2);
+                const float mn = fmaxf(L.s0[v], m2);
+                const float f1 = rescale(L.s0[v], mn), f2 = rescale(m2, mn);
+                L.s1[v] = L.s1[v] * f1 + s2 * f2;
+#pragma unroll
+                for (int k = 0; k < V; ++k) {
+                    const float o = __shfl_xor(L.acc[v][k], off, 64);
+                    L.acc[v][k] = L.acc[v][k] * f1 + o * f2;
+                }
+                L.s0[v] = mn;
             } else {
-                if constexpr (MODE == M_FWD || MODE == M_BWT) {
+                if constexpr (MODE == M_BWT) {
 #pragma unroll
                     for (int k = 0; k < V; ++k) L.acc[v][k] += __shfl_xor(L.acc[v][k], off, 64);
                 }
@@ -318,17 +352,18 @@ __device__ __forceinline__ void row_out(const Lane<MODE, T, NV>& L, const GatArg
     const int hd = L.hd[v];
     const int64_t rh = row * p.H + hd;
     const bool head_lead = (cv & ((1 << p.hshift) - 1)) == 0;
-    if constexpr (MODE == M_LSE) {
-        p.o_lse[rh] = L.s1[v] > 0.f ? L.s0[v] + __logf(L.s1[v]) : -INFINITY;
-    } else if constexpr (MODE == M_FWD) {
+    if constexpr (MODE == M_FWD) {
+        const float s = L.s1[v];
+        const float inv = s > 0.f ? 1.f / s : 0.f;
         float a[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) {
-            float t = L.acc[v][k];
+            float t = L.acc[v][k] * inv;
             if (p.bias) t += p.bias[cv * V + k];
             a[k] = p.relu && t < 0.f ? 0.f : t;
         }
         store_vals<T>(static_cast<T*>(p.y) + row * p.ldy + cv * V, a, V);
+        if (head_lead) p.o_lse[rh] = s > 0.f ? L.s0[v] + __logf(s) : -INFINITY;
     } else if constexpr (MODE == M_BWA) {
         if (head_lead) {
             p.o_rinfo[rh] = make_float4(L.r0[v], L.r1[v], L.s0[v], 0.f);
@@ -465,15 +500,20 @@ __global__ __launch_bounds__(256) void gat_long_reduce(GatArgs p) {
         Lane<MODE, T, 1> L;
         L.ch[0] = cv;
         L.hd[0] = cv >> p.hshift;
-        L.s0[0] = MODE == M_LSE ? -INFINITY : 0.f;
+        L.s0[0] = MODE == M_FWD ? -INFINITY : 0.f;
         L.s1[0] = L.s2[0] = 0.f;
 #pragma unroll
         for (int k = 0; k < V; ++k) L.acc[0][k] = 0.f;
         for (int32_t s = s0; s < s1; ++s) {
             const float* src = p.part + static_cast<int64_t>(s) * p.ldp;
             const float* st = src + p.soff + L.hd[0] * 3;
-            if constexpr (MODE == M_LSE) {
-                lse_merge(L.s0[0], L.s1[0], st[0], st[1]);
+            float f1 = 1.f, f2 = 1.f;
+            if constexpr (MODE == M_FWD) {
+                const float mn = fmaxf(L.s0[0], st[0]);
+                f1 = rescale(L.s0[0], mn);
+                f2 = rescale(st[0], mn);
+                L.s1[0] = L.s1[0] * f1 + st[1] * f2;
+                L.s0[0] = mn;
             } else {
                 L.s0[0] += st[0];
                 L.s1[0] += st[1];
@@ -483,10 +523,10 @@ __global__ __launch_bounds__(256) void gat_long_reduce(GatArgs p) {
 #pragma unroll
                 for (int q = 0; q < V; q += 4) {
                     const float4 t = *reinterpret_cast<const float4*>(src + cv * V + q);
-                    L.acc[0][q] += t.x;
-                    L.acc[0][q + 1] += t.y;
-                    L.acc[0][q + 2] += t.z;
-                    L.acc[0][q + 3] += t.w;
+                    L.acc[0][q] = L.acc[0][q] * f1 + t.x * f2;
+                    L.acc[0][q + 1] = L.acc[0][q + 1] * f1 + t.y * f2;
+                    L.acc[0][q + 2] = L.acc[0][q + 2] * f1 + t.z * f2;
+                    L.acc[0][q + 3] = L.acc[0][q + 3] * f1 + t.w * f2;
                 }
             }
         }
@@ -676,11 +716,9 @@ sag_status launch_pass(const sag_csr& A, GatArgs p, hipStream_t s) {
     if (C <= 16) return launch_g<MODE, T, 16, 1>(p, s);
     if (C <= 32) return launch_g<MODE, T, 32, 1>(p, s);
     if (C <= 64) return launch_g<MODE, T, 64, 1>(p, s);
-    if constexpr (MODE != M_LSE) {
-        if (C <= 128) return launch_g<MODE, T, 64, 2>(p, s);
-        if (C <= 192) return launch_g<MODE, T, 64, 3>(p, s);
-        if (C <= 256) return launch_g<MODE, T, 64, 4>(p, s);
-    }
+    if (C <= 128) return launch_g<MODE, T, 64, 2>(p, s);
+    if (C <= 192) return launch_g<MODE, T, 64, 3>(p, s);
+    if (C <= 256) return launch_g<MODE, T, 64, 4>(p, s);
     return fail(SAG_E_UNSUPPORTED, "gat: row too wide");
 }
 
@@ -812,24 +850,12 @@ sag_status forward_typed(const sag_csr& A, const Heads& h, const Saved& sv, int6
     p.er = sv.er;
     p.part = part;
     p.ldp = partial_floats(h, dt);
-    {
-        // the softmax normalisers: one "vector" per head
-        GatArgs q = p;
-        q.C = p.H;
-        q.hshift = 0;
-        q.soff = 0;
-        q.o_lse = sv.lse;
-        const int64_t bytes = 8 * (n_l + 1) + 4 * A.nnz + 4 * h.H * (n_ext + 2 * n_l);
-        TraceScope trace(trace_enabled() ? shape_name("gat_lse", "f32", n_l, A.nnz, h.H) : std::string(), s, bytes,
-                         0);
-        SAG_TRY((launch_pass<M_LSE, T>(A, q, s)));
-    }
     p.C = h.C;
     p.hshift = h.hshift;
     p.soff = h.C * static_cast<int>(vec_elems(dt));
     p.X = sv.Wh;
     p.ldx = ldwh;
-    p.lse = sv.lse;
+    p.o_lse = sv.lse;
     p.y = Out;
     p.ldy = ldo;
     p.bias = b;
