@@ -161,9 +161,25 @@ __device__ __forceinline__ void lane_row(Lane<MODE, T, NV>& L, const GatArgs& p,
     }
 }
 
-// Sum of a value over the lanes of one head (d_head / V consecutive lanes).
+// x plus its value in another lane through a DPP lane permutation (one
+// VALU instruction, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum of a value over the lanes of one head (2^hshift consecutive lanes,
+// aligned): swaps within quads (lanes 1 and 2 apart), then mirrors within 8
+// and 16 lanes -- after each step every lane of the group holds the group's
+// sum, so a mirror adds the other half's sum -- then lane shuffles for 32
+// and 64.
 __device__ __forceinline__ float head_sum(float x, int hshift) {
-    for (int off = 1; off < (1 << hshift); off <<= 1) x += __shfl_xor(x, off, 64);
+    if (hshift >= 1) x = dpp_add<0xb1>(x);    // quad_perm [1, 0, 3, 2]
+    if (hshift >= 2) x = dpp_add<0x4e>(x);    // quad_perm [2, 3, 0, 1]
+    if (hshift >= 3) x = dpp_add<0x141>(x);   // row_half_mirror
+    if (hshift >= 4) x = dpp_add<0x140>(x);   // row_mirror
+    if (hshift >= 5) x += __shfl_xor(x, 16, 64);
+    if (hshift >= 6) x += __shfl_xor(x, 32, 64);
     return x;
 }
 
