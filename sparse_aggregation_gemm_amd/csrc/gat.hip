@@ -33,6 +33,9 @@
 //   bwa  over A  : c and der, gathering rows of Wh against the row's own G_Y;
 //   bwt  over AT : dWh and del of each row u of [local | halo], gathering
 //                  rows of G_Y and one 16-byte record {er, lse, c} per head.
+// fwd and bwa take el[u] of a gathered row from the row itself (its dot
+// product with a_src, computed exactly as the score kernel does), so an
+// entry costs the row's cache lines and nothing more.
 // Each lane owns the heads of its vectors; the per-entry dot products are
 // finished with a butterfly over the d_head / V lanes of a head.
 #include <algorithm>
@@ -113,6 +116,7 @@ struct Lane {
     float own[NV][V];  // bwa: G_Y[v]; bwt: Wh[u]
     float r0[NV], r1[NV];       // fwd: er; bwa: er, lse; bwt: el
     float s0[NV], s1[NV], s2[NV];  // fwd: running max, sum; bwa: c, P, Q; bwt: del
+    float as[NV][V];   // fwd, bwa: a_src over the vector's elements
 };
 
 template <int MODE, class T, int NV>
@@ -125,7 +129,10 @@ __device__ __forceinline__ void lane_init(Lane<MODE, T, NV>& L, const GatArgs& p
         L.s0[v] = MODE == M_FWD ? -INFINITY : 0.f;
         L.s1[v] = L.s2[v] = 0.f;
 #pragma unroll
-        for (int k = 0; k < Lane<MODE, T, NV>::V; ++k) L.acc[v][k] = L.own[v][k] = 0.f;
+        for (int k = 0; k < Lane<MODE, T, NV>::V; ++k) {
+            L.acc[v][k] = L.own[v][k] = 0.f;
+            L.as[v][k] = MODE == M_BWT ? 0.f : p.a_src[L.ch[v] * Lane<MODE, T, NV>::V + k];
+        }
     }
 }
 
@@ -197,11 +204,24 @@ __device__ __forceinline__ void lane_entries(Lane<MODE, T, NV>& L, const GatArgs
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             x[u][v] = load_row_vec(X, p.ldx, c[u], L.ch[v]);
-            if constexpr (MODE == M_BWT)
-                ri[u][v] = p.rinfo[static_cast<int64_t>(c[u]) * p.H + L.hd[v]];
-            else
-                sc[u][v] = p.el[static_cast<int64_t>(c[u]) * p.H + L.hd[v]];
+            if constexpr (MODE == M_BWT) ri[u][v] = p.rinfo[static_cast<int64_t>(c[u]) * p.H + L.hd[v]];
         }
+    if constexpr (MODE != M_BWT) {
+        // el of each gathered row, recomputed from the row itself rather than
+        // gathered (one cache line less per entry): the same products, order
+        // and butterfly as the score kernel, so the same bits
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float f[V];
+                unpack<T>(x[u][v], f);
+                float ps = 0.f;
+#pragma unroll
+                for (int k = 0; k < V; ++k) ps = fmaf(f[k], L.as[v][k], ps);
+                sc[u][v] = head_sum(ps, p.hshift);
+            }
+    }
     if constexpr (MODE == M_FWD) {
         // the batch's scores, one rescale of the state to the new max, then
         // the entries' terms
@@ -864,6 +884,7 @@ sag_status forward_typed(const sag_csr& A, const Heads& h, const Saved& sv, int6
     p.slope = slope;
     p.el = sv.el;
     p.er = sv.er;
+    p.a_src = a_src;
     p.part = part;
     p.ldp = partial_floats(h, dt);
     p.C = h.C;
@@ -876,7 +897,7 @@ sag_status forward_typed(const sag_csr& A, const Heads& h, const Saved& sv, int6
     p.ldy = ldo;
     p.bias = b;
     p.relu = relu;
-    const int64_t bytes = 8 * (n_l + 1) + 4 * A.nnz + es * h.F * (n_ext + n_l) + 4 * h.H * (n_ext + 2 * n_l);
+    const int64_t bytes = 8 * (n_l + 1) + 4 * A.nnz + es * h.F * (n_ext + n_l) + 4 * h.H * 2 * n_l;
     TraceScope trace(trace_enabled() ? shape_name("gat_fwd", dt == SAG_BF16 ? "bf16" : "f32", n_l, A.nnz, h.F)
                                      : std::string(),
                      s, bytes, 2 * A.nnz * h.F);
@@ -901,6 +922,7 @@ sag_status backward_typed(const sag_csr& A, const sag_csr& AT, const Heads& h, c
     p.el = sv.el;
     p.er = sv.er;
     p.lse = sv.lse;
+    p.a_src = a_src;
     p.part = w.part;
     p.ldp = partial_floats(h, dt);
     p.soff = h.C * static_cast<int>(vec_elems(dt));
@@ -918,7 +940,7 @@ sag_status backward_typed(const sag_csr& A, const sag_csr& AT, const Heads& h, c
         q.o_rinfo = w.rinfo;
         q.o_der = w.der;
         const int64_t bytes = 8 * (n_l + 1) + 4 * A.nnz + es * h.F * (n_ext + n_l * (relu ? 3 : 1)) +
-                              4 * h.H * (n_ext + 2 * n_l) + 20 * h.H * n_l;
+                              4 * h.H * 2 * n_l + 20 * h.H * n_l;
         TraceScope trace(trace_enabled() ? shape_name("gat_bwd_rows", dt == SAG_BF16 ? "bf16" : "f32", n_l, A.nnz, h.F)
                                          : std::string(),
                          s, bytes, 2 * A.nnz * h.F);
