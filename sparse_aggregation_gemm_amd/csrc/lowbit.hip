@@ -33,47 +33,75 @@ namespace {
 constexpr uint32_t kPhiloxM0 = 0xD2511F53u, kPhiloxM1 = 0xCD9E8D57u;
 constexpr uint32_t kPhiloxW0 = 0x9E3779B9u, kPhiloxW1 = 0xBB67AE85u;
 
-// Philox4x32 with 10 rounds: c is the counter in and the block out.
+// Philox4x32 with 10 rounds: c is the counter in and the block out.  Each
+// round's two 32 x 32 -> 64-bit products are taken whole, so one
+// instruction gives both halves of each.
 __device__ __forceinline__ void philox4x32_10(uint32_t (&c)[4], uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
-        const uint32_t lo0 = kPhiloxM0 * c[0], hi0 = __umulhi(kPhiloxM0, c[0]);
-        const uint32_t lo1 = kPhiloxM1 * c[2], hi1 = __umulhi(kPhiloxM1, c[2]);
-        const uint32_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+        const uint64_t p0 = static_cast<uint64_t>(kPhiloxM0) * c[0];
+        const uint64_t p1 = static_cast<uint64_t>(kPhiloxM1) * c[2];
+        const uint32_t n0 = static_cast<uint32_t>(p1 >> 32) ^ c[1] ^ k0;
+        const uint32_t n2 = static_cast<uint32_t>(p0 >> 32) ^ c[3] ^ k1;
         c[0] = n0;
-        c[1] = lo1;
+        c[1] = static_cast<uint32_t>(p1);
         c[2] = n2;
-        c[3] = lo0;
+        c[3] = static_cast<uint32_t>(p0);
         k0 += kPhiloxW0;
         k1 += kPhiloxW1;
     }
 }
 
-// The eight elements [8g, 8g + 8) of a row as fp32 (elements past d read 0).
+// The eight elements [8g, 8g + 8) of a row as fp32 (elements past d read
+// as 0).  Loads are whole 16-byte vectors: the vector that holds the row's
+// last element lies inside the row's pitch (a multiple of 16 bytes), so only
+// an fp32 vector that starts at or past d is skipped.
 template <class T>
 __device__ __forceinline__ void load8(const T* row, int64_t g, int64_t d, float (&f)[8]) {
     const int64_t j0 = 8 * g;
-    if (j0 + 8 <= d) {
-        if constexpr (sizeof(T) == 2) {
-            unpack<T>(*reinterpret_cast<const uint4*>(row + j0), f);
-        } else {
-            unpack<T>(*reinterpret_cast<const uint4*>(row + j0), f);
+    unpack<T>(*reinterpret_cast<const uint4*>(row + j0), f);
+    if constexpr (sizeof(T) == 4) {
+        if (j0 + 4 < d) {
             unpack<T>(*reinterpret_cast<const uint4*>(row + j0 + 4), f + 4);
-        }
-    } else {
+        } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) f[e] = j0 + e < d ? to_f32(row[j0 + e]) : 0.f;
+            for (int e = 4; e < 8; ++e) f[e] = 0.f;
+        }
+    }
+    if (j0 + 8 > d) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = j0 + e < d ? f[e] : 0.f;
     }
 }
 
-// Writes the b bytes that hold eight b-bit codes.
-__device__ __forceinline__ void store_codes(uint8_t* p, uint64_t packed, int bits) {
-    switch (bits) {
-        case 1: *p = static_cast<uint8_t>(packed); break;
-        case 2: *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(packed); break;
-        case 4: *reinterpret_cast<uint32_t*>(p) = static_cast<uint32_t>(packed); break;
-        default: *reinterpret_cast<uint64_t*>(p) = packed; break;
+// Writes the BITS bytes that hold eight BITS-bit codes.
+template <int BITS>
+__device__ __forceinline__ void store_codes(uint8_t* p, uint64_t packed) {
+    if constexpr (BITS == 1) *p = static_cast<uint8_t>(packed);
+    else if constexpr (BITS == 2) *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(packed);
+    else if constexpr (BITS == 4) *reinterpret_cast<uint32_t*>(p) = static_cast<uint32_t>(packed);
+    else *reinterpret_cast<uint64_t*>(p) = packed;
+}
+
+// The codes of eight elements f (the first `live` of them real; the others
+// get code 0) with the uniform draws in w, packed BITS bits each.
+template <int BITS, bool FULL>
+__device__ __forceinline__ uint64_t code_group(const float (&f)[8], int live, float z, float inv, float B,
+                                               const uint32_t (&w)[4]) {
+    uint32_t part[2] = {0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float t = (f[e] - z) * inv;
+        const float fl = floorf(t);
+        const float fr = t - fl;
+        const float u = static_cast<float>((w[e / 2] >> (16 * (e & 1))) & 0xffffu) * 1.52587890625e-5f;   // 2^-16
+        float q = u < fr ? fl + 1.f : fl;
+        q = q < B ? q : B;
+        uint32_t c = static_cast<uint32_t>(q);
+        if constexpr (!FULL) c = e < live ? c : 0u;
+        part[(BITS * e) / 32] |= c << ((BITS * e) % 32);
     }
+    return static_cast<uint64_t>(part[0]) | (static_cast<uint64_t>(part[1]) << 32);
 }
 
 __device__ __forceinline__ uint64_t load_codes(const uint8_t* p, int bits) {
@@ -100,7 +128,33 @@ struct QArgs {
     float* zero;
 };
 
-template <class T, int G>
+// x from another lane through a DPP lane permutation (one VALU operand
+// modifier, no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Min and max over the G lanes (aligned) of a row: swaps within quads, then
+// mirrors within 8 and 16 lanes (after each step all lanes of the block hold
+// its value, so a mirror brings in the other half's), then lane shuffles.
+template <int G>
+__device__ __forceinline__ void group_minmax(float& mn, float& mx) {
+    if constexpr (G >= 2) { mn = fminf(mn, dpp<0xb1>(mn)); mx = fmaxf(mx, dpp<0xb1>(mx)); }     // quad_perm [1,0,3,2]
+    if constexpr (G >= 4) { mn = fminf(mn, dpp<0x4e>(mn)); mx = fmaxf(mx, dpp<0x4e>(mx)); }     // quad_perm [2,3,0,1]
+    if constexpr (G >= 8) { mn = fminf(mn, dpp<0x141>(mn)); mx = fmaxf(mx, dpp<0x141>(mx)); }   // row_half_mirror
+    if constexpr (G >= 16) { mn = fminf(mn, dpp<0x140>(mn)); mx = fmaxf(mx, dpp<0x140>(mx)); }  // row_mirror
+    if constexpr (G >= 32) {
+        mn = fminf(mn, __shfl_xor(mn, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    }
+    if constexpr (G >= 64) {
+        mn = fminf(mn, __shfl_xor(mn, 32, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    }
+}
+
+template <class T, int G, int BITS>
 __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
     constexpr int kRowsPerBlock = 256 / G;
     const int gl = threadIdx.x % G;
@@ -122,20 +176,17 @@ __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) f0[e] = f[e];
             }
+            const int live = static_cast<int>(a.d - 8 * g < 8 ? a.d - 8 * g : 8);
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (8 * g + e < a.d) {
+                if (live == 8 || e < live) {
                     mn = fminf(mn, f[e]);
                     mx = fmaxf(mx, f[e]);
                 }
         }
     }
-#pragma unroll
-    for (int off = G / 2; off > 0; off >>= 1) {
-        mn = fminf(mn, __shfl_xor(mn, off, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-    }
-    const float B = static_cast<float>((1 << a.bits) - 1);
+    group_minmax<G>(mn, mx);
+    const float B = static_cast<float>((1 << BITS) - 1);
     const float z = ok && a.d > 0 ? mn : 0.f;
     const float R = ok && a.d > 0 ? mx - mn : 0.f;
     const float s = R / B;
@@ -155,19 +206,11 @@ __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
             }
             uint32_t w[4] = {static_cast<uint32_t>(g), node, a.epoch, 0u};
             philox4x32_10(w, a.key0, a.key1);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                if (8 * g + e >= a.d) continue;
-                const float t = (f[e] - z) * inv;
-                const float fl = floorf(t);
-                const float fr = t - fl;
-                const float u = static_cast<float>((w[e / 2] >> (16 * (e & 1))) & 0xffffu) * 1.52587890625e-5f;   // 2^-16
-                float q = u < fr ? fl + 1.f : fl;
-                q = q < B ? q : B;
-                packed |= static_cast<uint64_t>(static_cast<uint32_t>(q)) << (a.bits * e);
-            }
+            const int live = static_cast<int>(a.d - 8 * g < 8 ? a.d - 8 * g : 8);
+            packed = live == 8 ? code_group<BITS, true>(f, 8, z, inv, B, w)
+                               : code_group<BITS, false>(f, live, z, inv, B, w);
         }
-        store_codes(out + g * a.bits, packed, a.bits);
+        store_codes<BITS>(out + g * BITS, packed);
     }
     if (gl == 0) {
         a.scale[k] = s;
@@ -230,12 +273,12 @@ __global__ __launch_bounds__(256) void dequantize_rows(DArgs a) {
     }
 }
 
-template <class T>
+template <class T, int BITS>
 sag_status launch_q(const QArgs& a, hipStream_t s) {
     const int64_t groups = (a.d + 7) / 8;
     auto go = [&](auto gc) {
         constexpr int G = decltype(gc)::value;
-        quantize_rows<T, G><<<dim3(static_cast<unsigned>(cdiv(a.n, 256 / G))), dim3(256), 0, s>>>(a);
+        quantize_rows<T, G, BITS><<<dim3(static_cast<unsigned>(cdiv(a.n, 256 / G))), dim3(256), 0, s>>>(a);
     };
     if (groups <= 4) go(std::integral_constant<int, 4>{});
     else if (groups <= 8) go(std::integral_constant<int, 8>{});
@@ -296,7 +339,16 @@ extern "C" sag_status sag_quantize_rows(const void* src, int64_t ld_src, sag_dty
     TraceScope trace(trace_enabled() ? shape_name("quantize", dt == SAG_BF16 ? "bf16" : "f32", n, d, bits)
                                      : std::string(),
                      s, n * (d * e + (d * bits + 7) / 8 + 8 + (rows ? 4 : 0) + (nodes ? 4 : 0)), 0);
-    return dt == SAG_BF16 ? launch_q<uint16_t>(a, s) : launch_q<float>(a, s);
+    auto go = [&](auto bc) {
+        constexpr int BITS = decltype(bc)::value;
+        return dt == SAG_BF16 ? launch_q<uint16_t, BITS>(a, s) : launch_q<float, BITS>(a, s);
+    };
+    switch (bits) {
+        case 1: return go(std::integral_constant<int, 1>{});
+        case 2: return go(std::integral_constant<int, 2>{});
+        case 4: return go(std::integral_constant<int, 4>{});
+        default: return go(std::integral_constant<int, 8>{});
+    }
 }
 
 extern "C" sag_status sag_dequantize_rows(const uint8_t* codes, int64_t ld_codes, const float* scale,
