@@ -11,7 +11,13 @@ and are reported as build_ms.
 Default workload: the 2.45M-node power-law graph, 3-layer GraphSAGE-mean
 100 -> 256 -> 256 -> 47 in bf16 with fp32 accumulation.
 
-Prints one JSON line on stdout; progress goes to stderr.
+Prints one JSON line on stdout; progress goes to stderr.  Besides the
+headline (K consecutive steps between two synchronisations), the line
+carries per-step p10 / median / p90 from HIP events around each timed step,
+the same for up to five cold steps (each after a 1 GiB write that evicts L2
+and the MALL), per-operation times with algorithmic GB/s, TFLOP/s and their
+fractions of the HBM, MFMA and attainable (min(MFMA peak, intensity x HBM
+peak)) ceilings, and row-length statistics of the graph.
 """
 from __future__ import annotations
 
@@ -204,6 +210,27 @@ def stored_traffic(op: str):
     return None, None
 
 
+def graph_stats(A, n_l, torch):
+    """Row-length statistics of the local CSR (self-loops included) and the
+    share of its entries that fall in halo columns."""
+    if A.n_rows == 0:
+        return {}
+    lens = (A.indptr[1:] - A.indptr[:-1]).to(torch.float64)
+    srt = torch.sort(lens).values
+    p99 = float(srt[min(A.n_rows - 1, int(0.99 * (A.n_rows - 1) + 0.5))])
+    halo = int((A.indices >= n_l).sum()) if A.n_cols > n_l else 0
+    return {"row_len_min": int(srt[0]), "row_len_mean": round(float(lens.mean()), 2), "row_len_p99": int(p99),
+            "row_len_max": int(srt[-1]), "halo_share_of_nnz": round(halo / max(A.nnz, 1), 4)}
+
+
+def pct(xs):
+    """p10 / median / p90 of a list of times (ms)."""
+    import numpy as np
+    a = np.asarray(xs, dtype=np.float64)
+    return {"p10": round(float(np.percentile(a, 10)), 4), "p50": round(float(np.percentile(a, 50)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4)}
+
+
 class Model:
     """Device-resident inputs, weights and buffers of one workload."""
 
@@ -229,6 +256,7 @@ class Model:
         self.n_h = self.n_ext - self.n_l
         log(f"[bench] built: n_local={self.n_l} n_halo={self.n_h} nnz={A.nnz} in {self.build_ms:.1f} ms; "
             f"schedule {sag.csr_info(A)}")
+        self.graph_stats = graph_stats(A, self.n_l, torch)
 
         def dev_dense(x):
             t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16) \
@@ -277,6 +305,26 @@ class Model:
                                 dH=self.dH[l] if want_dH else None, ws=self.ws)
             g = dH[: self.n_l] if want_dH else None
         return x
+
+
+def cold_steps(m, torch, n, flush_bytes=1 << 30):
+    """Times (ms, HIP events around the step only) of n steps, each after
+    writing a 1 GiB buffer so that L2 and the 256 MB MALL hold none of the
+    step's data."""
+    if n <= 0:
+        return []
+    junk = torch.empty(flush_bytes, dtype=torch.uint8, device=m.dev)
+    out = []
+    for i in range(n):
+        junk.fill_(i & 0xff)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        m.step()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    del junk
+    return out
 
 
 def _oracle_sample(w, R: int):
@@ -338,7 +386,23 @@ def cpu_baseline(w, rows_hint: int, target_s: float = 15.0):
         "value": round(ms, 1), "unit": "ms", "cores": native.num_threads(), "kind": "oracle",
         "sample": (f"local rows [0,{R}) of the {n_l}-row graph as a partition ({n_ext - R} halo columns), "
                    f"{w.n_layers}-layer fwd+bwd in float64 took {total:.2f} s, scaled by {scale:.2f}"),
+        "host": host_info(),
     }
+
+
+def host_info():
+    """CPU model and logical CPU count of the host the oracle ran on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
 
 
 def halo_messages(sag, torch, np, n_store=4_000_000, n_halo=3_800_000, d=128, reps=5, cpu_rows=20_000):
@@ -665,15 +729,20 @@ def main():
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     sag.trace_enable(True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    marks[0].record()
+    for i in range(args.steps):
         m.step()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     sag.trace_enable(False)
     recs = sag.trace_records(clear=True)
     ms_step = elapsed * 1e3 / args.steps
+    warm = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    cold = cold_steps(m, torch, min(args.steps, 5))
 
     # per-op statistics from the HIP events of the timed steps
     ops = {}
@@ -684,10 +753,19 @@ def main():
     table = []
     for name, o in ops.items():
         avg = o["ms"] / o["n"]
-        table.append({"op": name, "launches_per_step": o["n"] / args.steps, "avg_ms": round(avg, 4),
-                      "ms_per_step": round(o["ms"] / args.steps, 4),
-                      "GBps": round(o["bytes"] / avg / 1e6, 1) if avg > 0 else None,
-                      "TFLOPs": round(o["flops"] / avg / 1e9, 2) if avg > 0 else None})
+        t = {"op": name, "launches_per_step": o["n"] / args.steps, "avg_ms": round(avg, 4),
+             "ms_per_step": round(o["ms"] / args.steps, 4),
+             "GBps": round(o["bytes"] / avg / 1e6, 1) if avg > 0 else None,
+             "TFLOPs": round(o["flops"] / avg / 1e9, 2) if avg > 0 else None}
+        if avg > 0:
+            t["frac_hbm"] = round(t["GBps"] / HBM_PEAK_GBS, 4)
+            if name.startswith("gemm") and o["flops"] > 0 and o["bytes"] > 0:
+                peak = MFMA_PEAK_TFLOPS["bf16" if "[bf16" in name else "f32"]
+                # the attainable ceiling: min(MFMA peak, arithmetic intensity x HBM peak)
+                attain = min(peak, o["flops"] / o["bytes"] * HBM_PEAK_GBS / 1e3)
+                t["frac_mfma"] = round(t["TFLOPs"] / peak, 4)
+                t["frac_attainable"] = round(t["TFLOPs"] / attain, 4)
+        table.append(t)
     table.sort(key=lambda t: -t["ms_per_step"])
     spmm = [t for t in table if t["op"].startswith("spmm")]
     dom = table[0]
@@ -713,7 +791,8 @@ def main():
     A = m.built.A
     conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
-            "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion}
+            "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion,
+            "graph": m.graph_stats}
     build_ms = m.build_ms
     overlap = fused = gat = halo = None
     if not args.no_extras:
@@ -739,6 +818,8 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": conf,
         "build_ms": round(build_ms, 1),
+        "step_ms": pct(warm),
+        "cold": {"step_ms": pct(cold), "steps": len(cold), "flush_bytes": 1 << 30} if cold else None,
         "spmm": spmm,
         "ops": table,
         "roofline": roof,
