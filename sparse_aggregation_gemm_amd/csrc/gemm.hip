@@ -520,8 +520,8 @@ constexpr int kRwStage = 32 * (64 + 16);          // bytes of one wavefront's st
 
 template <int KS> constexpr int rw_atile() { return kRwRows * (KS * 32 + 16); }
 
-template <int KS, int NBW, bool MASK, int PF, int OCC>
-__global__ __launch_bounds__(kRwWaves * 64, OCC) void gemm_nn_rw(AOperand<uint16_t> A,
+template <int KS, int NBW, bool MASK, int PF, int WPE>
+__global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16_t> A,
                                                                const uint16_t* __restrict__ Bp, int64_t Kt,
                                                                int64_t N, int NB, int64_t n_tiles,
                                                                EpiT<uint16_t> e, const float* __restrict__ bias) {
@@ -692,22 +692,29 @@ __global__ __launch_bounds__(kRwWaves * 64, OCC) void gemm_nn_rw(AOperand<uint16
 
 int device_cus();
 
-// Tiles in flight per workgroup and workgroups per CU: as many as the
-// registers allow next to the weight fragments.
+// Tiles in flight per workgroup: as many as the registers allow next to the
+// weight fragments (deeper prefetch where registers are left over, up to 10
+// tiles at K = 256, measured no faster).  WPE is the minimum of waves per
+// SIMD handed to __launch_bounds__ (HIP's second argument counts waves per
+// execution unit, not workgroups per CU): an 8-wave workgroup is 2 waves per
+// SIMD, so 2 only caps the registers at 256.  The KS * NBW <= 8 kernel needs
+// 113 registers and runs two workgroups per CU, as the occupancy query that
+// sizes the grid reports; the others need 124-253 and run one.  Asking for 4
+// (two workgroups) at K = 256 spills the weight fragments to scratch.
 template <int KS, int NBW, bool MASK>
 constexpr int rw_pf() { return KS * NBW >= 32 ? (MASK ? 2 : 3) : (KS * NBW >= 16 ? (MASK ? 3 : 4) : 6); }
 template <int KS, int NBW, bool MASK>
-constexpr int rw_occ() { return KS * NBW <= 8 && !MASK ? 2 : 1; }
+constexpr int rw_wpe() { return KS * NBW <= 8 && !MASK ? 2 : 1; }
 
 template <int KS, int NBW, bool MASK>
 sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt, int64_t N,
                         const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
-    constexpr int PF = rw_pf<KS, NBW, MASK>(), OCC = rw_occ<KS, NBW, MASK>();
+    constexpr int PF = rw_pf<KS, NBW, MASK>(), WPE = rw_wpe<KS, NBW, MASK>();
     const int NB = static_cast<int>(cdiv(N, 32));
     const size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage;
     static bool attr_set = false;
     if (!attr_set) {
-        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, OCC>),
+        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>),
                                           hipFuncAttributeMaxDynamicSharedMemorySize, 131072));
         attr_set = true;
     }
@@ -716,13 +723,13 @@ sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t
     if (per_cu == 0) {
         int nb = 0;
         SAG_CHECK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, OCC>), kRwWaves * 64, lds));
+            &nb, reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>), kRwWaves * 64, lds));
         per_cu = nb > 0 ? nb : 1;
     }
     const int64_t n_tiles = cdiv(ao.M, kRwRows);
     int64_t grid = static_cast<int64_t>(device_cus()) * per_cu;
     if (grid > n_tiles) grid = n_tiles;
-    gemm_nn_rw<KS, NBW, MASK, PF, OCC><<<dim3(static_cast<unsigned>(grid)), kRwWaves * 64, lds, s>>>(
+    gemm_nn_rw<KS, NBW, MASK, PF, WPE><<<dim3(static_cast<unsigned>(grid)), kRwWaves * 64, lds, s>>>(
         ao, B, Kt, N, NB, n_tiles, e, bias);
     SAG_LAUNCH_CHECK();
     return SAG_OK;
