@@ -537,9 +537,15 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
     const int lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, l32 = lane & 31;
     unsigned char* stage = lds_raw + 2 * ATILE + wave * NBW * kRwStage;
+    // the bias of every column the workgroup writes (0 past N or without a
+    // bias), copied to LDS once: per-lane global loads in the epilogue would
+    // be issued after the next tiles' prefetch, and waiting for them would
+    // drain that prefetch every tile
+    float* bias_s = reinterpret_cast<float*>(lds_raw + 2 * ATILE + kRwWaves * NBW * kRwStage);
     const int64_t G = gridDim.x;
     int64_t t = blockIdx.x;
     if (t >= n_tiles) return;
+    for (int n = tid; n < kRwWaves * NBW * 32; n += kRwWaves * 64) bias_s[n] = bias && n < N ? bias[n] : 0.f;
 
     uint4 w[NBW][KS];
     bool has[NBW];
@@ -608,11 +614,9 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
             unsigned char* st = stage + j * kRwStage;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t c0 = nb * 32 + 8 * q + 4 * h;
-                float y[4];
-#pragma unroll
-                for (int t4 = 0; t4 < 4; ++t4)
-                    y[t4] = acc[j][4 * q + t4] + ((bias && c0 + t4 < N) ? bias[c0 + t4] : 0.f);
+                const float4 bv = *reinterpret_cast<const float4*>(bias_s + nb * 32 + 8 * q + 4 * h);
+                const float y[4] = {acc[j][4 * q] + bv.x, acc[j][4 * q + 1] + bv.y, acc[j][4 * q + 2] + bv.z,
+                                    acc[j][4 * q + 3] + bv.w};
                 *reinterpret_cast<uint2*>(st + l32 * 80 + (8 * q + 4 * h) * 2) =
                     make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
             }
@@ -698,9 +702,9 @@ int device_cus();
 // SIMD handed to __launch_bounds__ (HIP's second argument counts waves per
 // execution unit, not workgroups per CU): an 8-wave workgroup is 2 waves per
 // SIMD, so 2 only caps the registers at 256.  The KS * NBW <= 8 kernel needs
-// 113 registers and runs two workgroups per CU, as the occupancy query that
-// sizes the grid reports; the others need 124-253 and run one.  Asking for 4
-// (two workgroups) at K = 256 spills the weight fragments to scratch.
+// 106 registers and runs two workgroups per CU, as the occupancy query that
+// sizes the grid reports; the others need 132-241 and run one.  Asking for 4
+// (two workgroups) at K = 256 spills to scratch at every prefetch depth.
 template <int KS, int NBW, bool MASK>
 constexpr int rw_pf() { return KS * NBW >= 32 ? (MASK ? 2 : 3) : (KS * NBW >= 16 ? (MASK ? 3 : 4) : 6); }
 template <int KS, int NBW, bool MASK>
@@ -711,7 +715,8 @@ sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t
                         const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
     constexpr int PF = rw_pf<KS, NBW, MASK>(), WPE = rw_wpe<KS, NBW, MASK>();
     const int NB = static_cast<int>(cdiv(N, 32));
-    const size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage;
+    const size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage +
+                       static_cast<size_t>(kRwWaves) * NBW * 32 * sizeof(float);
     static bool attr_set = false;
     if (!attr_set) {
         SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>),
