@@ -560,9 +560,10 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
     }
 
     uint4 ra[PF][UPT], rm[MASK ? PF : 1][UPT];
+    // (no tile bound: rows past M load from a valid address, so every step
+    // issues the same loads and the compiler's wait counts stay exact)
     auto issue = [&](auto slot_c, int64_t tile) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
-        if (tile >= n_tiles) return;
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const int u = tid + i * NT;
@@ -575,7 +576,6 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
     };
     auto stash = [&](auto slot_c, int64_t tile, unsigned char* buf) __attribute__((always_inline)) {
         constexpr int slot = decltype(slot_c)::value;
-        if (tile >= n_tiles) return;
 #pragma unroll
         for (int i = 0; i < UPT; ++i) {
             const int u = tid + i * NT;
@@ -671,16 +671,17 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
     // t_k from LDS buffer k % 2 after moving tile t_{k+1} into the other
     // buffer and refilling its slot with tile t_{k+1+PF}; one barrier ends
     // the step (every wavefront is then done with buffer k % 2 and tile
-    // t_{k+1} is complete in the other).
+    // t_{k+1} is complete in the other).  Steps run in whole rounds of PF
+    // with no exit inside a round; a step past the workgroup's last tile
+    // computes zeros and stores nothing (its rows are >= M).
+    const int64_t steps = (n_tiles - t + G - 1) / G;
     static_for<0, PF>([&](auto sc) __attribute__((always_inline)) { issue(sc, t + decltype(sc)::value * G); });
     stash(std::integral_constant<int, 0>{}, t, lds_raw);
     __syncthreads();
     issue(std::integral_constant<int, 0>{}, t + PF * G);
     int cur = 0;
-    bool done = false;
-    while (!done) {
+    for (int64_t k = 0; k < steps; k += PF) {
         static_for<0, PF>([&](auto sc) __attribute__((always_inline)) {
-            if (done) return;
             constexpr int nx = (decltype(sc)::value + 1) % PF;
             unsigned char* nbuf = lds_raw + (cur ^ 1) * ATILE;
             stash(std::integral_constant<int, nx>{}, t + G, nbuf);
@@ -689,24 +690,26 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
             __syncthreads();
             cur ^= 1;
             t += G;
-            if (t >= n_tiles) done = true;
         });
     }
 }
 
 int device_cus();
 
-// Tiles in flight per workgroup: as many as the registers allow next to the
-// weight fragments (deeper prefetch where registers are left over, up to 10
-// tiles at K = 256, measured no faster).  WPE is the minimum of waves per
+// Tiles in flight per workgroup: as many as the registers hold next to the
+// weight fragments (every slot is live at once: the loop issues the same
+// loads on every step, so the waits count exactly and never drain the
+// prefetch); the masked 16-step kernel with two blocks per wavefront spills
+// 12 bytes even at one tile and is still faster than with conditional
+// loads.  WPE is the minimum of waves per
 // SIMD handed to __launch_bounds__ (HIP's second argument counts waves per
 // execution unit, not workgroups per CU): an 8-wave workgroup is 2 waves per
 // SIMD, so 2 only caps the registers at 256.  The KS * NBW <= 8 kernel needs
-// 106 registers and runs two workgroups per CU, as the occupancy query that
-// sizes the grid reports; the others need 132-241 and run one.  Asking for 4
+// 110 registers and runs two workgroups per CU, as the occupancy query that
+// sizes the grid reports; the others need 138-256 and run one.  Asking for 4
 // (two workgroups) at K = 256 spills to scratch at every prefetch depth.
 template <int KS, int NBW, bool MASK>
-constexpr int rw_pf() { return KS * NBW >= 32 ? (MASK ? 2 : 3) : (KS * NBW >= 16 ? (MASK ? 3 : 4) : 6); }
+constexpr int rw_pf() { return KS * NBW >= 32 ? 1 : (KS * NBW >= 16 ? (MASK ? 2 : 3) : 6); }
 template <int KS, int NBW, bool MASK>
 constexpr int rw_wpe() { return KS * NBW <= 8 && !MASK ? 2 : 1; }
 
