@@ -798,7 +798,7 @@ template <class T, int KT, int BNT> constexpr int tn_stage_bytes() {
            kTnRows * (BNT * static_cast<int>(sizeof(T)) + tn_pad<T>());
 }
 
-template <class T, int KT, int BNT>
+template <class T, int KT, int BNT, bool MASK>
 __global__ __launch_bounds__(kTnThreads, 1) void gemm_tn(AOperand<T> A, const T* __restrict__ B, int64_t ldb,
                                                          const T* __restrict__ mask, int64_t ldmask, int64_t N,
                                                          int64_t n_ktile, int64_t n_ntile, int64_t rows_per_chunk,
@@ -856,29 +856,30 @@ __global__ __launch_bounds__(kTnThreads, 1) void gemm_tn(AOperand<T> A, const T*
             alim[j] = 0;
         }
     }
+    // Every call issues the same loads, whatever the step or the thread: rows
+    // are clamped into the operands and units past a step's tile load a
+    // clamped row too (they are never written to LDS), so the compiler's
+    // wait counts stay exact and a wait for one step never drains the loads
+    // of the steps behind it.
     uint4 ra[2][UA], rb[2][UB], rm[2][UB];
     auto load = [&](auto buf_c, int64_t m0) {
         constexpr int bsel = decltype(buf_c)::value;
 #pragma unroll
         for (int j = 0; j < UA; ++j) {
             const int q = t + j * kTnThreads;
-            if (q < NA) {
-                const int64_t row = m0 + q / UPA;
-                const int64_t rc = row < alim[j] ? row : (alim[j] > 0 ? alim[j] - 1 : 0);
-                ra[bsel][j] = *reinterpret_cast<const uint4*>(abase[j] + rc * ald[j]);
-            }
+            const int64_t row = m0 + q / UPA;
+            const int64_t rc = row < alim[j] ? row : (alim[j] > 0 ? alim[j] - 1 : 0);
+            ra[bsel][j] = *reinterpret_cast<const uint4*>(abase[j] + rc * ald[j]);
         }
 #pragma unroll
         for (int j = 0; j < UB; ++j) {
             const int q = t + j * kTnThreads;
-            if (q < NBU) {
-                int64_t row = m0 + q / UPB;
-                row = row < A.M ? row : A.M - 1;
-                int64_t col = n0 + (q % UPB) * V;
-                col = col < lastn ? col : lastn;
-                rb[bsel][j] = *reinterpret_cast<const uint4*>(B + row * ldb + col);
-                if (mask) rm[bsel][j] = *reinterpret_cast<const uint4*>(mask + row * ldmask + col);
-            }
+            int64_t row = m0 + q / UPB;
+            row = row < A.M ? row : A.M - 1;
+            int64_t col = n0 + (q % UPB) * V;
+            col = col < lastn ? col : lastn;
+            rb[bsel][j] = *reinterpret_cast<const uint4*>(B + row * ldb + col);
+            if constexpr (MASK) rm[bsel][j] = *reinterpret_cast<const uint4*>(mask + row * ldmask + col);
         }
     };
     float cs[UB][V];
@@ -908,7 +909,7 @@ __global__ __launch_bounds__(kTnThreads, 1) void gemm_tn(AOperand<T> A, const T*
             const int q = t + j * kTnThreads;
             if (q < NBU) {
                 uint4 v = rb[bsel][j];
-                if (mask) v = apply_mask<T>(v, rm[bsel][j]);
+                if constexpr (MASK) v = apply_mask<T>(v, rm[bsel][j]);
                 if (tail && m0 + q / UPB >= m_end) v = make_uint4(0, 0, 0, 0);
                 if (do_cs) {
                     float f[V];
@@ -989,25 +990,24 @@ __global__ __launch_bounds__(kTnThreads, 1) void gemm_tn(AOperand<T> A, const T*
     const int64_t nsteps = m_begin < m_end ? (m_end - m_begin + kTnRows - 1) / kTnRows : 0;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
-    if (nsteps > 0) {
-        load(I0{}, m_begin);
-        store(I0{}, 0, m_begin);
-    }
-    if (nsteps > 1) load(I1{}, m_begin + kTnRows);
-    if (nsteps > 2) load(I0{}, m_begin + 2 * kTnRows);
+    load(I0{}, m_begin);
+    store(I0{}, 0, m_begin);
+    load(I1{}, m_begin + kTnRows);
+    load(I0{}, m_begin + 2 * kTnRows);
     __syncthreads();
     // step s: write step s+1 (register buffer (s+1)%2) into stage (s+1)%2,
-    // refill that buffer with step s+3, then multiply stage s%2
+    // refill that buffer with step s+3, then multiply stage s%2.  Steps run
+    // in pairs; past the chunk the stores write zeros and the loads read
+    // clamped rows, and only the multiply is skipped (a uniform branch with
+    // no memory loads in it).
     for (int64_t s0 = 0; s0 < nsteps; s0 += 2) {
         static_for<0, 2>([&](auto dc) {
             constexpr int d = decltype(dc)::value;
             const int64_t s = s0 + d;
-            if (s < nsteps) {
-                if (s + 1 < nsteps) store(std::integral_constant<int, 1 - d>{}, 1 - d, m_begin + (s + 1) * kTnRows);
-                if (s + 3 < nsteps) load(std::integral_constant<int, 1 - d>{}, m_begin + (s + 3) * kTnRows);
-                compute(d);
-                __syncthreads();
-            }
+            store(std::integral_constant<int, 1 - d>{}, 1 - d, m_begin + (s + 1) * kTnRows);
+            load(std::integral_constant<int, 1 - d>{}, m_begin + (s + 3) * kTnRows);
+            if (s < nsteps) compute(d);
+            __syncthreads();
         });
     }
 
@@ -1248,21 +1248,28 @@ TnPlan tn_plan(int64_t M, int64_t Kv, int64_t N, sag_dtype dt) {
     return p;
 }
 
-template <class T, int KT, int BNT>
-void launch_tn(const TnPlan& p, const AOperand<T>& ao, const void* B, int64_t ldb, const void* mask, int64_t ldmask,
-               int64_t N, float* part, float* pcs, hipStream_t s) {
+template <class T, int KT, int BNT, bool MASK>
+void launch_tn_m(const TnPlan& p, const AOperand<T>& ao, const void* B, int64_t ldb, const void* mask,
+                 int64_t ldmask, int64_t N, float* part, float* pcs, hipStream_t s) {
     constexpr size_t lds = 2 * static_cast<size_t>(tn_stage_bytes<T, KT, BNT>());
     static_assert(lds >= static_cast<size_t>(kTnRows) * BNT * 4, "column-sum buffer");
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn<T, KT, BNT>),
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn<T, KT, BNT, MASK>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
         attr_set = true;
     }
     const unsigned grid = static_cast<unsigned>(p.n_chunks * p.n_ktile * p.n_ntile);
-    gemm_tn<T, KT, BNT><<<grid, kTnThreads, lds, s>>>(ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask),
-                                                     ldmask, N, p.n_ktile, p.n_ntile, p.rows_per_chunk, part,
-                                                     p.ldp_k, p.ldp_n, pcs);
+    gemm_tn<T, KT, BNT, MASK><<<grid, kTnThreads, lds, s>>>(
+        ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask), ldmask, N, p.n_ktile, p.n_ntile,
+        p.rows_per_chunk, part, p.ldp_k, p.ldp_n, pcs);
+}
+
+template <class T, int KT, int BNT>
+void launch_tn(const TnPlan& p, const AOperand<T>& ao, const void* B, int64_t ldb, const void* mask, int64_t ldmask,
+               int64_t N, float* part, float* pcs, hipStream_t s) {
+    if (mask) launch_tn_m<T, KT, BNT, true>(p, ao, B, ldb, mask, ldmask, N, part, pcs, s);
+    else launch_tn_m<T, KT, BNT, false>(p, ao, B, ldb, mask, ldmask, N, part, pcs, s);
 }
 
 template <class T>
