@@ -751,8 +751,10 @@ sag_status try_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt
     if (e.add) return SAG_E_UNSUPPORTED;
     const int64_t NB = cdiv(N, 32);
     // up to 128 columns the LDS-resident kernel reads A once as well, and
-    // is faster (measured at 256 -> 111: 0.60 against 0.75 ms)
-    if (NB <= 4) return SAG_E_UNSUPPORTED;
+    // is faster at K = 256 (256 -> 128: 0.44 against 0.49 ms; 256 -> 64: 0.33
+    // against 0.45), but not at K = 128 (128 -> 128: 0.36 against 0.24),
+    // where this kernel runs two workgroups per CU
+    if (NB <= 4 && (Kt != 128 || ao.mask)) return SAG_E_UNSUPPORTED;
     const int nbw = NB <= kRwWaves ? 1 : (NB <= 2 * kRwWaves ? 2 : 0);
     const bool m = ao.mask != nullptr;
     if (nbw == 1) {

@@ -190,7 +190,7 @@ extern "C" sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext,
     const int64_t ldt = ldv(d_out, dt);
     GemmA a;
     a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = A->n_cols;
-    SAG_TRY(gemm_run(A->n_cols, d_out, a, w.Bp, dt, w.t1, ldt, Epilogue{}, s));
+    SAG_TRY(gemm_run(A->n_cols, full_width(ldt), a, w.Bp, dt, w.t1, ldt, Epilogue{}, s));
     return spmm_run(*A, w.t1, ldt, dt, d_out, Out, ldo, dt, e, w.spmm, w.spmm_bytes, s);
 }
 
@@ -251,7 +251,7 @@ extern "C" sag_status sag_gcn_layer_backward(const sag_csr* AT, int64_t n_local,
         SAG_TRY(pack_b(src, d_out, 0, nl, dt, w.Bp, s));
         GemmA g;
         g.a1 = G_out; g.lda1 = ldg; g.k1 = d_out; g.m1 = n_local; g.mask = mask; g.ldmask = ldg;
-        SAG_TRY(gemm_run(n_local, d_in, g, w.Bp, dt, w.t1, ldz, Epilogue{}, s));
+        SAG_TRY(gemm_run(n_local, full_width(ldz), g, w.Bp, dt, w.t1, ldz, Epilogue{}, s));
         return spmm_run(*AT, w.t1, ldz, dt, d_in, dH_ext, ldd, dt, Epilogue{}, w.spmm, w.spmm_bytes, s);
     }
     // transform first: G_Y, S = A^T G_Y, dW = H^T S, db = colsum G_Y, dH = S W^T
@@ -357,7 +357,7 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
     SAG_TRY(pack_b(src, d_in, 0, nl, dt, w.Bp, s));
     GemmA a;
     a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = A->n_cols;
-    SAG_TRY(gemm_run(A->n_cols, np + d_out, a, w.Bp, dt, w.t1, ldpt, Epilogue{}, s));
+    SAG_TRY(gemm_run(A->n_cols, full_width(ldpt), a, w.Bp, dt, w.t1, ldpt, Epilogue{}, s));
     e.addend = static_cast<const char*>(w.t1) + np * es;
     e.ld_add = ldpt;
     e.n_add = n_l;
@@ -429,7 +429,7 @@ extern "C" sag_status sag_sage_layer_backward(const sag_csr* AT, int64_t n_local
         SAG_TRY(pack_b(src, d_out, 0, nl, dt, w.Bp, s));
         GemmA g;
         g.a1 = G_out; g.lda1 = ldg; g.k1 = d_out; g.m1 = n_local; g.mask = mask; g.ldmask = ldg;
-        SAG_TRY(gemm_run(n_local, ip + d_in, g, w.Bp, dt, w.t1, ldx, Epilogue{}, s));
+        SAG_TRY(gemm_run(n_local, full_width(ldx), g, w.Bp, dt, w.t1, ldx, Epilogue{}, s));
         Epilogue e;
         e.addend = w.t1;
         e.ld_add = ldx;

@@ -25,6 +25,11 @@ inline int64_t ldv(int64_t d, sag_dtype dt) {
     const int64_t e = elt_size(dt), bytes = (d > 0 ? d : 1) * e;
     return (bytes > 64 ? round_up(bytes, 128) : round_up(bytes, 16)) / e;
 }
+// A product written into one of the library's own buffers computes the
+// buffer's whole pitch (the packed weight reads zeros past its columns): its
+// rows go out as whole cache lines, with no ragged element stores and no
+// partial-line writes.
+inline int64_t full_width(int64_t ld) { return ld; }
 inline size_t dense_bytes(int64_t rows, int64_t d, sag_dtype dt) {
     return static_cast<size_t>(rows > 0 ? rows : 0) * ldv(d, dt) * elt_size(dt);
 }
