@@ -62,32 +62,44 @@ struct SpArgs {
     EpiArgs<YT> e;
 };
 
-template <class T>
-__device__ __forceinline__ void load_vals(const T* p, float* f, int n) {
-    constexpr int V = Vec<T>::N;
-    if (n == V) {
-        uint4 v = *reinterpret_cast<const uint4*>(p);
-        unpack<T>(v, f);
-    } else {
-        for (int e = 0; e < n; ++e) f[e] = to_f32(p[e]);
+// The addend and bias of V consecutive outputs starting at column ch * V,
+// loaded before the row's gathers so that their latency hides under them
+// (read at the end of the row, they cost a full memory round trip per row).
+// The addend is read as whole 16-byte vectors: the vector that holds the
+// row's last element lies inside its pitch.  The bias has exactly d entries.
+template <class YT, int V>
+struct EpiIn {
+    static constexpr int NU = V * static_cast<int>(sizeof(YT)) / 16;
+    uint4 add[NU];
+    float bias[V];
+};
+
+template <class YT, int V>
+__device__ __forceinline__ void epi_load(const EpiArgs<YT>& e, int64_t row, int ch, bool live, EpiIn<YT, V>& in) {
+    constexpr int VY = Vec<YT>::N;
+    const int col0 = ch * V;
+#pragma unroll
+    for (int q = 0; q < EpiIn<YT, V>::NU; ++q) {
+        in.add[q] = make_uint4(0, 0, 0, 0);
+        if (live && e.add && row < e.n_add && col0 + q * VY < e.d)
+            in.add[q] = *reinterpret_cast<const uint4*>(e.add + row * e.ld_add + col0 + q * VY);
     }
+#pragma unroll
+    for (int k = 0; k < V; ++k) in.bias[k] = live && e.bias && col0 + k < e.d ? e.bias[col0 + k] : 0.f;
 }
 
 // Epilogue and store of V consecutive outputs starting at column ch * V.
 template <class YT, int V>
-__device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int ch, float* a) {
+__device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int ch, float* a,
+                                          const EpiIn<YT, V>& in) {
     const int col0 = ch * V;
     if (col0 >= e.d) return;
     const int n = min(V, e.d - col0);
     constexpr int VY = Vec<YT>::N;
     if (e.add && row < e.n_add) {
         float t[V];
-        const YT* ap = e.add + row * e.ld_add + col0;
 #pragma unroll
-        for (int q = 0; q < V; q += VY) {
-            const int nq = min(VY, n - q);
-            if (nq > 0) load_vals<YT>(ap + q, t + q, nq);
-        }
+        for (int q = 0; q < EpiIn<YT, V>::NU; ++q) unpack<YT>(in.add[q], t + q * VY);
 #pragma unroll
         for (int k = 0; k < V; ++k)
             if (k < n) a[k] += t[k];
@@ -95,7 +107,7 @@ __device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int
     if (e.bias) {
 #pragma unroll
         for (int k = 0; k < V; ++k)
-            if (k < n) a[k] += e.bias[col0 + k];
+            if (k < n) a[k] += in.bias[k];
     }
     if (e.pre) {
 #pragma unroll
@@ -139,6 +151,10 @@ __device__ __forceinline__ void short_rows(const SpArgs<XT, YT>& p, int64_t bloc
     int ch[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) ch[v] = min(v * G + gl, p.C - 1);
+    // (rows of one vector per lane load the epilogue inputs first; wider
+    // rows, with more work per row to hide the latency, at the end)
+    EpiIn<YT, V> ein[NV];
+    if constexpr (NV == 1) epi_load<YT, V>(p.e, row, gl, valid && gl < p.C, ein[0]);
     float acc[NV][V];
 #pragma unroll
     for (int v = 0; v < NV; ++v)
@@ -169,7 +185,8 @@ __device__ __forceinline__ void short_rows(const SpArgs<XT, YT>& p, int64_t bloc
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int cv = v * G + gl;
-        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v]);
+        if constexpr (NV != 1) epi_load<YT, V>(p.e, row, cv, cv < p.C, ein[v]);
+        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v], ein[v]);
     }
 }
 
@@ -191,14 +208,17 @@ __device__ __forceinline__ void medium_rows(const SpArgs<XT, YT>& p, int64_t blo
         start = p.indptr[w];
         len = static_cast<int>(p.indptr[w + 1] - start);
     }
+    const int lane = threadIdx.x & 63;
+    EpiIn<YT, V> ein[NV];
+    if constexpr (NV == 1) epi_load<YT, V>(p.e, row, lane, lane < G && lane < p.C, ein[0]);
     float acc[NV][V];
     wave_row_sum<XT, G, NV>(p.X, p.ldx, p.C, p.idx, p.val, start, len, acc);
-    const int lane = threadIdx.x & 63;
     if (lane >= G) return;
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
         const int cv = v * G + lane;
-        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v]);
+        if constexpr (NV != 1) epi_load<YT, V>(p.e, row, cv, cv < p.C, ein[v]);
+        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v], ein[v]);
     }
 }
 
@@ -256,6 +276,8 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
     const int32_t s0 = p.seg0[j], s1 = p.seg0[j + 1];
     const int64_t ldp = static_cast<int64_t>(p.C) * V;
     for (int ch = lane; ch < p.C; ch += 64) {
+        EpiIn<YT, V> ein;
+        epi_load<YT, V>(p.e, row, ch, true, ein);
         float a[V];
 #pragma unroll
         for (int k = 0; k < V; ++k) a[k] = 0.f;
@@ -270,7 +292,7 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
                 a[q + 3] += t.w;
             }
         }
-        epi_store<YT, V>(p.e, row, ch, a);
+        epi_store<YT, V>(p.e, row, ch, a, ein);
     }
 }
 
