@@ -382,7 +382,8 @@ __device__ __forceinline__ void sweep_wave(Lane<MODE, T, NV>& L, const GatArgs& 
 // Outputs of one row from a combined lane state, for vector v of the lane
 // (cv = its unclamped index).
 template <int MODE, class T, int NV>
-__device__ __forceinline__ void row_out(const Lane<MODE, T, NV>& L, const GatArgs& p, int64_t row, int v, int cv) {
+__device__ __forceinline__ void row_out(const Lane<MODE, T, NV>& L, const GatArgs& p, const float* cvec, int64_t row,
+                                        int v, int cv) {
     constexpr int V = Vec<T>::N;
     if (cv >= p.C) return;
     const int hd = L.hd[v];
@@ -395,7 +396,7 @@ __device__ __forceinline__ void row_out(const Lane<MODE, T, NV>& L, const GatArg
 #pragma unroll
         for (int k = 0; k < V; ++k) {
             float t = L.acc[v][k] * inv;
-            if (p.bias) t += p.bias[cv * V + k];
+            if (p.bias) t += cvec[cv * V + k];
             a[k] = p.relu && t < 0.f ? 0.f : t;
         }
         store_vals<T>(static_cast<T*>(p.y) + row * p.ldy + cv * V, a, V);
@@ -418,7 +419,7 @@ __device__ __forceinline__ void row_out(const Lane<MODE, T, NV>& L, const GatArg
 }
 
 template <int MODE, class T, int G, int NV>
-__device__ __forceinline__ void short_rows(const GatArgs& p, int64_t block) {
+__device__ __forceinline__ void short_rows(const GatArgs& p, const float* cvec, int64_t block) {
     constexpr int P = 64 / G;
     const int lane = threadIdx.x & 63;
     const int gl = lane % G, grp = lane / G;
@@ -441,11 +442,11 @@ __device__ __forceinline__ void short_rows(const GatArgs& p, int64_t block) {
     sweep_group<MODE, T, G, NV>(L, p, start, len, lmax);
     if (!valid) return;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) row_out(L, p, row, v, v * G + gl);
+    for (int v = 0; v < NV; ++v) row_out(L, p, cvec, row, v, v * G + gl);
 }
 
 template <int MODE, class T, int G, int NV>
-__device__ __forceinline__ void medium_rows(const GatArgs& p, int64_t block) {
+__device__ __forceinline__ void medium_rows(const GatArgs& p, const float* cvec, int64_t block) {
     const int64_t w = block * kWaves + (threadIdx.x >> 6);
     if (w >= p.n_medium) return;
     int64_t row, start;
@@ -468,7 +469,7 @@ __device__ __forceinline__ void medium_rows(const GatArgs& p, int64_t block) {
     sweep_wave<MODE, T, G, NV>(L, p, start, len);
     if (lane >= G) return;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) row_out(L, p, row, v, v * G + gl);
+    for (int v = 0; v < NV; ++v) row_out(L, p, cvec, row, v, v * G + gl);
 }
 
 template <int MODE, class T, int G, int NV>
@@ -507,8 +508,25 @@ __device__ __forceinline__ void segments(const GatArgs& p, int64_t block) {
     }
 }
 
+// The forward's bias (zeros without one) copied to LDS once per workgroup:
+// read from global memory at the end of every row it costs a memory round
+// trip per row, and kept in registers it would cost occupancy.  (The column
+// sweep's a_src and a_dst measured no faster this way.)
+template <int MODE, class T>
+__device__ __forceinline__ void load_cvec(const GatArgs& p, float* cvec) {
+    constexpr int V = Vec<T>::N;
+    const int F = p.C * V;
+    for (int i = threadIdx.x; i < F; i += blockDim.x) cvec[i] = p.bias ? p.bias[i] : 0.f;
+    __syncthreads();
+}
+
+template <int MODE>
+constexpr int cvec_count() { return MODE == M_FWD ? 1 : 0; }
+
 template <int MODE, class T, int G, int NV>
 __global__ __launch_bounds__(256) void gat_bins(GatArgs p) {
+    extern __shared__ float cvec[];
+    if constexpr (cvec_count<MODE>() > 0) load_cvec<MODE, T>(p, cvec);
     int64_t b = blockIdx.x;
     if (b < p.nb_seg) {
         segments<MODE, T, G, NV>(p, b);
@@ -516,10 +534,10 @@ __global__ __launch_bounds__(256) void gat_bins(GatArgs p) {
     }
     b -= p.nb_seg;
     if (b < p.nb_medium) {
-        medium_rows<MODE, T, G, NV>(p, b);
+        medium_rows<MODE, T, G, NV>(p, cvec, b);
         return;
     }
-    short_rows<MODE, T, G, NV>(p, b - p.nb_medium);
+    short_rows<MODE, T, G, NV>(p, cvec, b - p.nb_medium);
 }
 
 // Combines the segment partials of each long row in segment order, then
@@ -527,6 +545,8 @@ __global__ __launch_bounds__(256) void gat_bins(GatArgs p) {
 template <int MODE, class T>
 __global__ __launch_bounds__(256) void gat_long_reduce(GatArgs p) {
     constexpr int V = Vec<T>::N;
+    extern __shared__ float cvec[];
+    if constexpr (cvec_count<MODE>() > 0) load_cvec<MODE, T>(p, cvec);
     const int64_t j = static_cast<int64_t>(blockIdx.x) * kWaves + (threadIdx.x >> 6);
     if (j >= p.n_long) return;
     const int lane = threadIdx.x & 63;
@@ -579,7 +599,7 @@ __global__ __launch_bounds__(256) void gat_long_reduce(GatArgs p) {
                 store_vals<T>(static_cast<T*>(p.gy) + row * p.ldgy + cv * V, g, V);
             }
         }
-        row_out(L, p, row, 0, cv);
+        row_out(L, p, cvec, row, 0, cv);
     }
 }
 
@@ -731,12 +751,13 @@ sag_status launch_g(GatArgs p, hipStream_t s) {
     p.nb_seg = cdiv(p.n_seg, kWaves);
     p.nb_medium = cdiv(p.n_medium, kWaves);
     const int64_t blocks = p.nb_seg + p.nb_medium + cdiv(p.n_short, kWaves * P);
+    const size_t lds = static_cast<size_t>(cvec_count<MODE>()) * p.C * Vec<T>::N * sizeof(float);
     if (blocks > 0) {
-        gat_bins<MODE, T, G, NV><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(p);
+        gat_bins<MODE, T, G, NV><<<dim3(static_cast<unsigned>(blocks)), 256, lds, s>>>(p);
         SAG_LAUNCH_CHECK();
     }
     if (p.n_long > 0) {
-        gat_long_reduce<MODE, T><<<dim3(static_cast<unsigned>(cdiv(p.n_long, kWaves))), 256, 0, s>>>(p);
+        gat_long_reduce<MODE, T><<<dim3(static_cast<unsigned>(cdiv(p.n_long, kWaves))), 256, lds, s>>>(p);
         SAG_LAUNCH_CHECK();
     }
     return SAG_OK;
