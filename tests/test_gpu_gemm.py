@@ -23,8 +23,10 @@ def _err(got, ref, den):
     return float(np.max(np.abs(got - ref) / (den + 1e-30))) if ref.size else 0.0
 
 
+# (1031, 128, 111) and (517, 100, 64): bf16 products over a 128-element K
+# with at most 128 columns take the weights-in-registers kernel
 SHAPES = [(1, 1, 1), (5, 3, 7), (130, 64, 16), (257, 100, 256), (1000, 200, 47), (333, 512, 48),
-          (700, 128, 602), (4099, 602, 128), (129, 41, 300)]
+          (700, 128, 602), (4099, 602, 128), (129, 41, 300), (1031, 128, 111), (517, 100, 64)]
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
