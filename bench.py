@@ -151,7 +151,9 @@ def summarize_counters(args):
             b = 32 * v[names[1]] + 64 * v[names[2]] + 128 * v[names[3]]
             rows.append(f"| {label} | {v[names[0]]:.0f} | {v[names[1]]:.0f} | {v[names[2]]:.0f} | "
                         f"{v[names[3]]:.0f} | {b:.4e} |")
-            rec["sized_read_bytes_" + ("calib" if label.startswith("cal") else "kernel")] = int(round(b))
+            tag = "calib" if label.startswith("cal") else "kernel"
+            rec["sized_read_bytes_" + tag] = int(round(b))
+            rec["read_requests_" + tag] = int(round(v[names[0]]))
         sizes = f"""
 Cross-check: read requests by size (one more pass), bytes = 32 n32 + 64 n64 + 128 n128:
 
@@ -197,17 +199,18 @@ Machine-readable record (bench.py reads it while the kernel sources keep this di
     print(json.dumps(rec))
 
 
-def stored_traffic(op: str):
-    """Traffic per launch of `op` from a committed counter summary taken on
-    the current kernel sources, else None."""
+def stored_counters(op: str):
+    """The counter record of `op` from a committed summary taken on the
+    current kernel sources (and the summary's path), else (None, None)."""
     dig = sources_digest(op)
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(f) as fh:
             for m in re.finditer(r"<!-- counters (\{.*\}) -->", fh.read()):
                 rec = json.loads(m.group(1))
                 if rec.get("op") == op and rec.get("sources_sha256_16") == dig:
-                    return rec["traffic_bytes_per_launch"], os.path.relpath(f, ROOT)
+                    return rec, os.path.relpath(f, ROOT)
     return None, None
+
 
 
 def graph_stats(A, n_l, torch):
@@ -781,9 +784,15 @@ def main():
         roof = {"bound": "hbm", "achieved": round(dom_o["bytes"] / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    traffic, tsrc = stored_traffic(dom["op"])
-    roof["traffic"] = traffic
+    crec, tsrc = stored_counters(dom["op"])
+    roof["traffic"] = crec["traffic_bytes_per_launch"] if crec else None
     roof["traffic_source"] = tsrc
+    # L2-miss read requests of one launch (all whole 128-byte lines for the
+    # gathers) and the rate this run achieved: random row gathers on this part
+    # are capped by that rate, not by HBM bytes
+    reqs = crec.get("read_requests_kernel") if crec else None
+    roof["read_requests_per_launch"] = reqs
+    roof["read_request_rate_G_per_s"] = round(reqs / avg_s / 1e9, 2) if reqs else None
     roof["kernel"] = dom["op"]
     roof["alg_bytes_per_launch"] = dom_o["bytes"]
     roof["avg_launch_ms"] = dom["avg_ms"]
