@@ -93,6 +93,24 @@ def test_gemm_wide_outputs(dt, K1, K2, N, masked):
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("M", [1, 33, 97])
+@pytest.mark.parametrize("K,N", [(128, 256), (256, 256), (512, 256), (256, 512), (96, 100)])
+def test_gemm_few_rows(dt, M, K, N):
+    """Fewer row tiles than the persistent kernels' workgroups and their
+    prefetch depth: the steps past a workgroup's last tile must store
+    nothing.  Exact small integers, so any stray or missing store shows."""
+    g = np.random.default_rng(M + K + N)
+    _, A = _mat(g, (M, K), dt, integers=True)
+    _, W = _mat(g, (K, N), dt, integers=True)
+    W = W.contiguous()
+    say(f"gemm few rows dt={dt} M={M} K={K} N={N}")
+    C = sag.gemm(A, W)
+    exact = f64(A) @ f64(W)
+    ref = olay.round_bf16(exact) if dt == "bf16" else exact
+    assert np.array_equal(f64(C), ref)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [80, 300])
 def test_gemm_exact_integers(dt, N):
     g = np.random.default_rng(4)
