@@ -674,6 +674,57 @@ __global__ __launch_bounds__(256) void gat_colsum_part(const T* X, int64_t ldx, 
     }
 }
 
+// Stage 1 of two weighted column sums of the same X in one pass over its
+// rows: part1 over rows [0, n1) with weights w1, part2 over rows [0, n2)
+// with w2 (n1 <= n2), each block and each sum in the order of
+// gat_colsum_part, so the results equal two separate passes.
+template <class T>
+__global__ __launch_bounds__(256) void gat_colsum2_part(const T* X, int64_t ldx, int64_t n1, int64_t n2, int C,
+                                                        int Cp, int H, int hshift, const float* w1,
+                                                        const float* w2, int64_t rows_per_block, int64_t nb1,
+                                                        float* part1, float* part2) {
+    constexpr int V = Vec<T>::N;
+    __shared__ float red[2][256 * V];
+    const int t = threadIdx.x;
+    const int ch = t % Cp, rr = t / Cp, RP = 256 / Cp;
+    const int64_t r0 = static_cast<int64_t>(blockIdx.x) * rows_per_block;
+    const int64_t r1 = min(n2, r0 + rows_per_block), r1a = min(n1, r0 + rows_per_block);
+    float a[V], b[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) a[k] = b[k] = 0.f;
+    if (ch < C) {
+        for (int64_t r = r0 + rr; r < r1; r += RP) {
+            float f[V];
+            unpack<T>(load_row_vec(X, ldx, r, ch), f);
+            const int64_t rh = r * H + (ch >> hshift);
+            const float wb = w2[rh];
+#pragma unroll
+            for (int k = 0; k < V; ++k) b[k] = fmaf(wb, f[k], b[k]);
+            if (r < r1a) {
+                const float wa = w1[rh];
+#pragma unroll
+                for (int k = 0; k < V; ++k) a[k] = fmaf(wa, f[k], a[k]);
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+        red[0][t * V + k] = a[k];
+        red[1][t * V + k] = b[k];
+    }
+    __syncthreads();
+    const int F = C * V;
+    for (int j = t; j < F; j += 256) {
+        float sa = 0.f, sb = 0.f;
+        for (int q = 0; q < RP; ++q) {
+            sa += red[0][q * Cp * V + j];
+            sb += red[1][q * Cp * V + j];
+        }
+        if (blockIdx.x < nb1) part1[static_cast<int64_t>(blockIdx.x) * F + j] = sa;
+        part2[static_cast<int64_t>(blockIdx.x) * F + j] = sb;
+    }
+}
+
 // Stage 2: out[j] = sum over blocks of part[b][j], blocks in order; 64
 // columns per workgroup, four interleaved block ranges added at the end.
 __global__ __launch_bounds__(256) void gat_colsum_final(const float* part, int64_t nb, int F, float* out) {
@@ -825,6 +876,28 @@ sag_status launch_colsum(const Heads& h, const void* X, int64_t ldx, int64_t n, 
     return SAG_OK;
 }
 
+// da_dst (rows [0, n1), weights w1) and da_src (rows [0, n2), weights w2)
+// from one pass over Wh.
+template <class T>
+sag_status launch_colsum2(const Heads& h, const void* X, int64_t ldx, int64_t n1, const float* w1, float* part1,
+                          float* out1, int64_t n2, const float* w2, float* part2, float* out2, hipStream_t s) {
+    const int F = static_cast<int>(h.F);
+    const int64_t nb1 = colsum_blocks(n1), nb2 = colsum_blocks(n2);
+    if (nb2 > 0) {
+        int Cp = 1;
+        while (Cp < h.C) Cp <<= 1;
+        gat_colsum2_part<T><<<dim3(static_cast<unsigned>(nb2)), 256, 0, s>>>(
+            static_cast<const T*>(X), ldx, n1, n2, h.C, Cp, static_cast<int>(h.H), h.hshift, w1, w2, kColsumRows,
+            nb1, part1, part2);
+        SAG_LAUNCH_CHECK();
+    }
+    gat_colsum_final<<<dim3(static_cast<unsigned>(cdiv(F, 64))), 256, 0, s>>>(part1, nb1, F, out1);
+    SAG_LAUNCH_CHECK();
+    gat_colsum_final<<<dim3(static_cast<unsigned>(cdiv(F, 64))), 256, 0, s>>>(part2, nb2, F, out2);
+    SAG_LAUNCH_CHECK();
+    return SAG_OK;
+}
+
 // Saved forward state: Wh [n_ext, ldv(F)], el and er [n_ext, H], lse [n_local, H].
 struct Saved {
     void* Wh = nullptr;
@@ -869,6 +942,7 @@ struct BwdWs {
     float* del = nullptr;
     float* part = nullptr;
     float* cpart = nullptr;
+    float* cpart2 = nullptr;
     void* tn = nullptr;
     size_t tn_bytes = 0;
     size_t total = 0;
@@ -887,6 +961,7 @@ BwdWs carve_bwd(void* base, const sag_csr& A, const sag_csr& AT, int64_t d_in, c
     const int64_t ns = std::max(seg_count(A), seg_count(AT));
     w.part = c.take<float>(static_cast<size_t>(ns) * partial_floats(h, dt));
     w.cpart = c.take<float>(static_cast<size_t>(std::max<int64_t>(colsum_blocks(n_ext), 1)) * h.F);
+    w.cpart2 = c.take<float>(static_cast<size_t>(std::max<int64_t>(colsum_blocks(n_l), 1)) * h.F);
     w.tn_bytes = gemm_tn_ws_bytes(n_ext, ldv(d_in, dt), h.F, dt);
     w.tn = c.take<char>(w.tn_bytes);
     w.total = c.used();
@@ -992,8 +1067,12 @@ sag_status backward_typed(const sag_csr& A, const sag_csr& AT, const Heads& h, c
                                      : std::string(),
                      s, es * h.F * (2 * n_l + n_ext) + 4 * h.H * (n_l + n_ext), 0);
     if (db) SAG_TRY(launch_colsum<T>(h, GY, ldgy, n_l, nullptr, w.cpart, db, s));
-    if (da_dst) SAG_TRY(launch_colsum<T>(h, sv.Wh, ldwh, n_l, w.der, w.cpart, da_dst, s));
-    if (da_src) SAG_TRY(launch_colsum<T>(h, sv.Wh, ldwh, n_ext, w.del, w.cpart, da_src, s));
+    if (da_dst && da_src) {
+        SAG_TRY(launch_colsum2<T>(h, sv.Wh, ldwh, n_l, w.der, w.cpart2, da_dst, n_ext, w.del, w.cpart, da_src, s));
+    } else {
+        if (da_dst) SAG_TRY(launch_colsum<T>(h, sv.Wh, ldwh, n_l, w.der, w.cpart, da_dst, s));
+        if (da_src) SAG_TRY(launch_colsum<T>(h, sv.Wh, ldwh, n_ext, w.del, w.cpart, da_src, s));
+    }
     return SAG_OK;
 }
 
