@@ -787,6 +787,10 @@ def main():
     crec, tsrc = stored_counters(dom["op"])
     roof["traffic"] = crec["traffic_bytes_per_launch"] if crec else None
     roof["traffic_source"] = tsrc
+    # the rate of the bytes the counters saw (L2 <-> fabric, MALL hits
+    # included) against the same peak, beside the algorithmic fraction
+    roof["traffic_GBps"] = round(roof["traffic"] / avg_s / 1e9, 1) if crec and roof["unit"] == "GB/s" else None
+    roof["traffic_frac"] = round(roof["traffic_GBps"] / HBM_PEAK_GBS, 4) if roof["traffic_GBps"] else None
     # L2-miss read requests of one launch (all whole 128-byte lines for the
     # gathers) and the rate this run achieved: random row gathers on this part
     # are capped by that rate, not by HBM bytes
