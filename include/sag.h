@@ -41,7 +41,9 @@
  *    `ws` whose size the matching *_workspace_bytes function returns (those
  *    functions run on the host only).  The library allocates no device
  *    memory, keeps no per-call state and may be called from several host
- *    threads on different streams.
+ *    threads on different streams.  Launch settings (occupancy, CU count,
+ *    LDS limits) are queried once per process, so the devices one process
+ *    uses must be of one kind.
  *  - Errors: arguments are validated on the host before anything is
  *    launched; a failure returns a negative sag_status and launches nothing.
  *    A HIP error returns SAG_E_HIP.  sag_last_error() gives a detail string

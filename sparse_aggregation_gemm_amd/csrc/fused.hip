@@ -404,12 +404,11 @@ namespace {
 
 template <class T, int G, int NV>
 void launch_at(const FusedArgs<T>& p, size_t lds, hipStream_t s) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&agg_transform<T, G, NV>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kMaxLds));
-        attr_set = true;
-    }
+    // (once per kernel instance; thread-safe static initialisation)
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&agg_transform<T, G, NV>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(kMaxLds));
+    (void)attr;
     agg_transform<T, G, NV><<<dim3(static_cast<unsigned>(p.n_tiles)), kThreads, lds, s>>>(p);
 }
 

@@ -720,20 +720,21 @@ sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t
     const int NB = static_cast<int>(cdiv(N, 32));
     const size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage +
                        static_cast<size_t>(kRwWaves) * NBW * 32 * sizeof(float);
-    static bool attr_set = false;
-    if (!attr_set) {
-        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, 131072));
-        attr_set = true;
-    }
+    // (once per kernel instance: the initialisation of a function-local
+    // static is thread-safe)
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        131072);
+    SAG_CHECK_HIP(attr);
     // persistent workgroups: exactly as many as are resident at once
-    static int per_cu = 0;
-    if (per_cu == 0) {
+    static const int per_cu = [lds] {
         int nb = 0;
-        SAG_CHECK_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &nb, reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>), kRwWaves * 64, lds));
-        per_cu = nb > 0 ? nb : 1;
-    }
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                   &nb, reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>), kRwWaves * 64, lds) ==
+                       hipSuccess && nb > 0
+                   ? nb
+                   : 1;
+    }();
     const int64_t n_tiles = cdiv(ao.M, kRwRows);
     int64_t grid = static_cast<int64_t>(device_cus()) * per_cu;
     if (grid > n_tiles) grid = n_tiles;
@@ -1120,29 +1121,27 @@ __global__ void relu_mask_kernel(int64_t M, int64_t C, int64_t N, const T* __res
     }
 }
 
+// Device properties, queried once per process (thread-safe static
+// initialisation): the library assumes the devices a process uses are alike.
 int device_cus() {
-    static int cus = 0;
-    if (!cus) {
+    static const int cus = [] {
         int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-            cus = v;
-        else
-            cus = 256;
-    }
+        return hipGetDevice(&dev) == hipSuccess &&
+                       hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+                   ? v
+                   : 256;
+    }();
     return cus;
 }
 
 size_t max_lds_per_block() {
-    static size_t lds = 0;
-    if (!lds) {
+    static const size_t lds = [] {
         int dev = 0, v = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0)
-            lds = static_cast<size_t>(v);
-        else
-            lds = 65536;
-    }
+        return hipGetDevice(&dev) == hipSuccess &&
+                       hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) == hipSuccess && v > 0
+                   ? static_cast<size_t>(v)
+                   : static_cast<size_t>(65536);
+    }();
     return lds;
 }
 
@@ -1150,13 +1149,10 @@ template <class T, int BN, bool MASK, int PD>
 sag_status launch_nn(const AOperand<T>& ao, const T* B, int64_t Kt, int64_t N, const EpiT<T>& e,
                      const float* bias, hipStream_t s) {
     const size_t lds = static_cast<size_t>(BN) * Kt * sizeof(T) + static_cast<size_t>(kNnWaves) * kNnTile;
-    static bool attr_set = false;
-    if (!attr_set) {
-        SAG_CHECK_HIP(hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK, PD>),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          static_cast<int>(max_lds_per_block())));
-        attr_set = true;
-    }
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_nn<T, BN, MASK, PD>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(max_lds_per_block()));
+    SAG_CHECK_HIP(attr);
     const int64_t n_nblk = cdiv(N, BN);
     const int64_t n_blk = cdiv(ao.M, kNnRows);
     int64_t n_mgroups = device_cus() / n_nblk;
@@ -1255,12 +1251,10 @@ void launch_tn_m(const TnPlan& p, const AOperand<T>& ao, const void* B, int64_t 
                  int64_t ldmask, int64_t N, float* part, float* pcs, hipStream_t s) {
     constexpr size_t lds = 2 * static_cast<size_t>(tn_stage_bytes<T, KT, BNT>());
     static_assert(lds >= static_cast<size_t>(kTnRows) * BNT * 4, "column-sum buffer");
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn<T, KT, BNT, MASK>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-        attr_set = true;
-    }
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&gemm_tn<T, KT, BNT, MASK>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       static_cast<int>(lds));
+    (void)attr;
     const unsigned grid = static_cast<unsigned>(p.n_chunks * p.n_ktile * p.n_ntile);
     gemm_tn<T, KT, BNT, MASK><<<grid, kTnThreads, lds, s>>>(
         ao, static_cast<const T*>(B), ldb, static_cast<const T*>(mask), ldmask, N, p.n_ktile, p.n_ntile,
