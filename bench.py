@@ -750,9 +750,17 @@ def main():
     # per-op statistics from the HIP events of the timed steps
     ops = {}
     for r in recs:
-        o = ops.setdefault(r["name"], {"n": 0, "ms": 0.0, "bytes": r["bytes"], "flops": r["flops"]})
+        # (launches of one op name may differ in their bytes -- the SAGE forward
+        # SpMM reads no values, its transpose does -- so bytes and flops are
+        # averaged over the launches)
+        o = ops.setdefault(r["name"], {"n": 0, "ms": 0.0, "bsum": 0, "fsum": 0})
         o["n"] += 1
         o["ms"] += r["ms"]
+        o["bsum"] += r["bytes"]
+        o["fsum"] += r["flops"]
+    for o in ops.values():
+        o["bytes"] = o["bsum"] / o["n"]
+        o["flops"] = o["fsum"] / o["n"]
     table = []
     for name, o in ops.items():
         avg = o["ms"] / o["n"]
@@ -798,7 +806,7 @@ def main():
     roof["read_requests_per_launch"] = reqs
     roof["read_request_rate_G_per_s"] = round(reqs / avg_s / 1e9, 2) if reqs else None
     roof["kernel"] = dom["op"]
-    roof["alg_bytes_per_launch"] = dom_o["bytes"]
+    roof["alg_bytes_per_launch"] = int(round(dom_o["bytes"]))
     roof["avg_launch_ms"] = dom["avg_ms"]
 
     A = m.built.A

@@ -337,7 +337,9 @@ sag_status sag_gcn_layer_backward(const sag_csr* AT, int64_t n_local,
  * mean aggregator, self first in the concatenation):
  *   M = A_mean H_ext;  Y = [H_local | M] W + b;  Out = relu ? max(Y,0) : Y.
  * W: [2 * d_in, d_out]; rows 0 .. d_in-1 act on the node's own row, the rest
- * on M. */
+ * on M.  A_mean is the CSR of sag_csr_build_normalize with the mean
+ * normalisation: every entry of row r holds 1/len(r), so the forward reads
+ * only the pattern and scales each row's sum by that value. */
 size_t sag_sage_save_bytes(int64_t n_local, int64_t d_in, int64_t d_out, sag_dtype dt);
 size_t sag_sage_forward_workspace_bytes(const sag_csr* A_mean, int64_t d_in, int64_t d_out,
                                         sag_dtype dt);

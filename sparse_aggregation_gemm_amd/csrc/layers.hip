@@ -333,7 +333,11 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
         if (fusion_enabled() && w.fz_bytes)
             return agg_transform_run(*A, H_ext, ldh, d_in, W, b, d_out, true, relu, dt, Y_pre, Out, ldo, save, ldm,
                                      w.fz, w.fz_bytes, s);
-        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldm, dt, Epilogue{}, w.spmm, w.spmm_bytes, s));
+        // (the mean normalisation gives every entry of row r the value
+        // 1/len(r): the SpMM scales each row's sum instead of reading values)
+        Epilogue em;
+        em.row_mean = 1;
+        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldm, dt, em, w.spmm, w.spmm_bytes, s));
         GemmA a;
         a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = n_l;
         a.a2 = save; a.lda2 = ldm; a.k2 = d_in;
@@ -361,6 +365,7 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
     e.addend = static_cast<const char*>(w.t1) + np * es;
     e.ld_add = ldpt;
     e.n_add = n_l;
+    e.row_mean = 1;
     return spmm_run(*A, w.t1, ldpt, dt, d_out, Out, ldo, dt, e, w.spmm, w.spmm_bytes, s);
 }
 

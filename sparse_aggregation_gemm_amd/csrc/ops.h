@@ -16,6 +16,8 @@ struct Epilogue {
     const float* bias = nullptr;    // [d]
     int relu = 0;
     void* pre = nullptr;            // output type, same ld as the output; nullable
+    int row_mean = 0;               // SpMM: every value of row r is 1/len(r) (the mean
+                                    // normalisation): values not read, each row's sum scaled
 };
 
 // Leading dimension of the library's own dense buffers: rows wider than 64

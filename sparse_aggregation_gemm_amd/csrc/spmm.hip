@@ -40,6 +40,7 @@ struct EpiArgs {
     const float* bias;
     int relu;
     int d;
+    int row_mean;   // scale each row's sum by 1/len (values not read)
 };
 
 template <class XT, class YT>
@@ -91,11 +92,17 @@ __device__ __forceinline__ void epi_load(const EpiArgs<YT>& e, int64_t row, int 
 // Epilogue and store of V consecutive outputs starting at column ch * V.
 template <class YT, int V>
 __device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int ch, float* a,
-                                          const EpiIn<YT, V>& in) {
+                                          const EpiIn<YT, V>& in, int len) {
     const int col0 = ch * V;
     if (col0 >= e.d) return;
     const int n = min(V, e.d - col0);
     constexpr int VY = Vec<YT>::N;
+    if (e.row_mean && len > 0) {
+        // the value the mean normalisation stores, 1/len rounded once
+        const float rs = 1.f / static_cast<float>(len);
+#pragma unroll
+        for (int k = 0; k < V; ++k) a[k] *= rs;
+    }
     if (e.add && row < e.n_add) {
         float t[V];
 #pragma unroll
@@ -186,7 +193,7 @@ __device__ __forceinline__ void short_rows(const SpArgs<XT, YT>& p, int64_t bloc
     for (int v = 0; v < NV; ++v) {
         const int cv = v * G + gl;
         if constexpr (NV != 1) epi_load<YT, V>(p.e, row, cv, cv < p.C, ein[v]);
-        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v], ein[v]);
+        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v], ein[v], len);
     }
 }
 
@@ -218,7 +225,7 @@ __device__ __forceinline__ void medium_rows(const SpArgs<XT, YT>& p, int64_t blo
     for (int v = 0; v < NV; ++v) {
         const int cv = v * G + lane;
         if constexpr (NV != 1) epi_load<YT, V>(p.e, row, cv, cv < p.C, ein[v]);
-        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v], ein[v]);
+        if (cv < p.C) epi_store<YT, V>(p.e, row, cv, acc[v], ein[v], len);
     }
 }
 
@@ -273,6 +280,7 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
     if (j >= p.n_long) return;
     const int lane = threadIdx.x & 63;
     const int64_t row = p.compact_long ? j : p.rec_long[j].x;
+    const int len = p.rec_long[j].y;
     const int32_t s0 = p.seg0[j], s1 = p.seg0[j + 1];
     const int64_t ldp = static_cast<int64_t>(p.C) * V;
     for (int ch = lane; ch < p.C; ch += 64) {
@@ -292,7 +300,7 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
                 a[q + 3] += t.w;
             }
         }
-        epi_store<YT, V>(p.e, row, ch, a, ein);
+        epi_store<YT, V>(p.e, row, ch, a, ein, len);
     }
 }
 
@@ -344,7 +352,7 @@ sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, vo
     p.C = static_cast<int>(cdiv(d, V));
     p.indptr = A.indptr;
     p.idx = A.indices;
-    p.val = A.values;
+    p.val = epi.row_mean ? nullptr : A.values;
     p.part = static_cast<float*>(ws);
     p.e.y = static_cast<YT*>(Y);
     p.e.ldy = ldy;
@@ -355,6 +363,7 @@ sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, vo
     p.e.bias = epi.bias;
     p.e.relu = epi.relu;
     p.e.d = static_cast<int>(d);
+    p.e.row_mean = epi.row_mean;
     const int C = p.C;
     if (C <= 4) return launch_bins<XT, YT, 4, 1>(A, p, s, long_only);
     if (C <= 8) return launch_bins<XT, YT, 8, 1>(A, p, s, long_only);
@@ -410,7 +419,7 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
         return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
     // algorithmic bytes: CSR arrays once, every X row once, every output once
     const int64_t ex = elt_size(xt), ey = elt_size(yt);
-    const int64_t bytes = 8 * (A.n_rows + 1) + A.nnz * (A.values ? 8 : 4) + ex * d * A.n_cols +
+    const int64_t bytes = 8 * (A.n_rows + 1) + A.nnz * (A.values && !epi.row_mean ? 8 : 4) + ex * d * A.n_cols +
                           ey * d * A.n_rows * (epi.pre ? 2 : 1) + (epi.addend ? ey * d * epi.n_add : 0);
     TraceScope trace(trace_enabled() ? shape_name("spmm", xt == SAG_BF16 ? (yt == SAG_BF16 ? "bf16" : "bf16>f32") : "f32",
                                                   A.n_rows, A.nnz, d)
