@@ -3,8 +3,9 @@
  * Y[r, :] = sum over entries p of row r, in ascending p, of val[p] * X[col[p], :]
  *
  * This is the aggregation A^T H of the CAGNET page's forward-propagation
- * equation, row by row ("the row-wise algorithm forms one row of output at a
- * time", 1D block-row section).  Each output row is independent, so rows may
+ * equation, computed output row by output row as in that page's 1D
+ * block-row algorithm ("Reducing Communication in Graph Neural Network
+ * Training", 1D algorithm section).  Each output row is independent, so rows may
  * be spread over threads; within a row the sum runs in entry order with a
  * separate multiply and add (built with -ffp-contract=off).
  *
