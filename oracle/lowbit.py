@@ -21,21 +21,24 @@ Definitions followed
 Readings (the quantization and dequantization equations are missing from
 the extracted page)
 -----------------------------------------------------------------------------
-* With Z = min_j h_j, R = max_j h_j - Z, the scale s = R / B and its
-  inverse r = B / R (fp32, each correctly rounded), element j maps to
-  t_j = (h_j - Z) * r (the bin position: (h_j - Z) measured in scales); its
-  code is floor(t_j) plus one with probability t_j - floor(t_j) (stochastic
-  rounding), at most B.  A row with R = 0 has all codes 0.  The recovered
-  element is Z + q_j s.  Every step is an fp32 operation rounded to nearest
-  even, in that order (no fused multiply-add), so that the integer
-  decisions are reproducible.
+* With Z = min_j h_j, R = max_j h_j - Z and the scale s = R / B (fp32,
+  correctly rounded), element j's bin position is t_j = (h_j - Z) / s (fp32,
+  correctly rounded): the distance from the zero-point measured in scales,
+  the plain inverse of the recovery Z + q s.  Its code is floor(t_j) plus one
+  with probability t_j - floor(t_j) (stochastic rounding), at most B.  A row
+  with R = 0 has all codes 0.  The recovered element is Z + q_j s.  Every
+  step is an fp32 operation rounded to nearest even, in that order (no fused
+  multiply-add), so that the integer decisions are reproducible.
 * The uniform draw of element j of the node with id `node`, call `epoch`,
   generator key `seed`: the Philox4x32-10 counter-based generator (Salmon,
   Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
-  SC'11) at counter (j // 8, node, epoch, 0) and key (seed low 32 bits, seed
-  high 32 bits); 16-bit half (j % 2) (low half first) of output word
-  (j // 2) % 4, times 2^-16.  u < frac rounds up.  (A 2^-16 grid for the
-  draw biases a code's expectation by less than 2^-16 of a bin.)
+  SC'11) at counter (j // 4, node, epoch, 0) and key (seed low 32 bits, seed
+  high 32 bits); output word j % 4, its top 24 bits times 2^-24: the fp32
+  uniform on [0, 1), whose 2^24 equally likely values k 2^-24 are all exact
+  in fp32.  u < frac rounds up.  Every fp32 t >= 1/2 has a fraction on that
+  2^-24 grid, so there the probability of rounding up is exactly the
+  fraction and the code's expectation is exactly t (the page's unbiased
+  Low-bit Module); below 1/2 the bias is under 2^-24 of a bin.
 * Codes are packed little-endian: element j occupies bits [b j, b j + b) of
   the row's code bytes.
 """
@@ -72,14 +75,22 @@ def uniforms(nodes, epoch: int, d: int, seed: int) -> np.ndarray:
     """float32 [n, d]: the draw of every element of every listed node."""
     nodes = np.asarray(nodes, np.int64)
     n = nodes.size
-    nblk = (d + 7) // 8
+    nblk = (d + 3) // 4
     ctr = np.zeros((n, nblk, 4), np.uint64)
     ctr[..., 0] = np.arange(nblk, dtype=np.uint64)[None, :]
     ctr[..., 1] = (nodes.astype(np.uint64) & np.uint64(0xFFFFFFFF))[:, None]
     ctr[..., 2] = np.uint64(epoch & 0xFFFFFFFF)
-    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(n, nblk * 4)
-    halves = np.stack([words & np.uint32(0xFFFF), words >> np.uint32(16)], axis=-1).reshape(n, nblk * 8)[:, :d]
-    return (halves.astype(np.float32) * np.float32(2.0 ** -16)).astype(np.float32)
+    words = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)).reshape(n, nblk * 4)[:, :d]
+    return ((words >> np.uint32(8)).astype(np.float32) * np.float32(2.0 ** -24)).astype(np.float32)
+
+
+def stochastic_round(t, u, B):
+    """The code of bin position t (fp32) with draw u in [0, 1): floor(t),
+    plus one when u < t - floor(t) (the fraction, exact in fp32), at most B."""
+    t = np.asarray(t, np.float32)
+    fl = np.floor(t).astype(np.float32)
+    q = fl + (np.asarray(u, np.float32) < (t - fl).astype(np.float32)).astype(np.float32)
+    return np.minimum(q, np.float32(B))
 
 
 def quantize_rows(H, nodes, epoch: int, seed: int, bits: int):
@@ -98,11 +109,8 @@ def quantize_rows(H, nodes, epoch: int, seed: int, bits: int):
     scale = (rng / B).astype(np.float32)
     u = uniforms(nodes, epoch, d, seed)
     with np.errstate(divide="ignore", invalid="ignore"):
-        inv = (B / rng).astype(np.float32)
-        t = ((H - zero[:, None]).astype(np.float32) * inv[:, None]).astype(np.float32)
-    fl = np.floor(t).astype(np.float32)
-    q = fl + (u < (t - fl).astype(np.float32)).astype(np.float32)
-    q = np.minimum(q, B)
+        t = ((H - zero[:, None]).astype(np.float32) / scale[:, None]).astype(np.float32)
+    q = stochastic_round(t, u, B)
     q = np.where(rng[:, None] > 0, q, np.float32(0))
     return q.astype(np.uint8), scale, zero
 

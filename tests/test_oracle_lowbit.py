@@ -35,6 +35,48 @@ def test_uniforms_are_uniform_and_keyed():
     assert np.array_equal(u[5:6], olb.uniforms([5], 3, 64, seed=12345))
 
 
+def test_draws_are_the_fp32_uniform_grid():
+    """Each draw is k 2^-24 with k the top 24 bits of the generator word that
+    the element's position selects (block j // 4, word j % 4)."""
+    nodes = np.array([0, 7, 123456, 2 ** 31 - 1])
+    d, epoch, seed = 11, 5, (0xABCDEF << 32) | 0x13579
+    u = olb.uniforms(nodes, epoch, d, seed)
+    k = u.astype(np.float64) * 2.0 ** 24
+    assert np.array_equal(k, np.floor(k)) and k.min() >= 0 and k.max() < 2 ** 24
+    for i, node in enumerate(nodes):
+        for j in range(d):
+            w = olb.philox4x32_10(np.array([[j // 4, node, epoch, 0]], np.uint32),
+                                  (seed & 0xFFFFFFFF, seed >> 32))[0, j % 4]
+            assert int(k[i, j]) == int(w) >> 8
+
+
+def _round_up_count(t, B):
+    """Over all 2^24 equally likely draws, how many round fp32 t up."""
+    grid = np.arange(2 ** 24, dtype=np.float32) * np.float32(2.0 ** -24)
+    q = olb.stochastic_round(np.full(grid.size, t, np.float32), grid, B)
+    return int(np.sum(q - np.floor(np.float32(t)), dtype=np.int64))
+
+
+@pytest.mark.parametrize("t", [0.5, 0.75, 1.0, 1.0000001, 2.9999998, 3.3, 127.00781, 200.5, 254.99998])
+def test_expected_code_is_exactly_t(t):
+    """Sylvie's Low-bit Module is unbiased: with the draw uniform over its
+    2^24 values, the code's expectation is exactly the bin position for
+    every fp32 t >= 1/2 (its fraction lies on the 2^-24 grid), counted over
+    all draws."""
+    t = np.float32(t)
+    frac = float(t) - np.floor(float(t))
+    assert _round_up_count(t, 255) == round(frac * 2 ** 24)
+
+
+@pytest.mark.parametrize("t", [0.3, 1e-3, 3e-7, 2.0 ** -30])
+def test_expected_code_below_one_half(t):
+    """Below 1/2 the fraction can be finer than the draw grid: the bias is
+    under 2^-24 of a bin."""
+    t = np.float32(t)
+    count = _round_up_count(t, 1)
+    assert abs(count / 2 ** 24 - float(t)) < 2.0 ** -24
+
+
 @pytest.mark.parametrize("bits", [1, 2, 4, 8])
 def test_grid_values_are_exact(bits):
     """Values on the quantization grid (a power-of-two scale) need no
