@@ -4,15 +4,18 @@
 // (B = 2^b - 1 bins) by stochastic rounding, with a per-row scale
 // (max(h) - min(h)) / B and zero-point min(h); the receiver recovers
 // zero + code * scale.  The page's equations are missing from the text; the
-// plain reading is taken: t = (h - zero) * (B / (max - min)), the position
-// in bins, code = floor(t) + 1 with probability t - floor(t) (at most B),
-// every step an fp32 operation rounded to nearest even in that order, so
-// that the integer decisions are reproducible.  The uniform draws come from
-// the Philox4x32-10 counter-based generator (Salmon, Moraes, Dror and Shaw,
-// "Parallel random numbers: as easy as 1, 2, 3", SC'11): element j of node
-// `node` in call `epoch` uses 16-bit half j % 2 (low first) of word
-// (j / 2) % 4 of the block at counter (j / 8, node, epoch, 0) under key
-// (seed low, seed high), times 2^-16 -- one block per eight elements.
+// plain reading is taken: t = (h - zero) / scale, the position in bins (the
+// inverse of the recovery), code = floor(t) + 1 with probability
+// t - floor(t) (at most B), every step an fp32 operation rounded to nearest
+// even in that order, so that the integer decisions are reproducible.  The
+// uniform draws come from the Philox4x32-10 counter-based generator (Salmon,
+// Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC'11): element j of node `node` in call `epoch` uses the top 24 bits of
+// word j % 4 of the block at counter (j / 4, node, epoch, 0) under key
+// (seed low, seed high), times 2^-24 -- the fp32 uniform on [0, 1), whose
+// values all lie on the grid of every fp32 fraction of a position >= 1/2, so
+// the rounding is exactly unbiased there (the page's unbiased Low-bit
+// Module).  Two blocks per eight elements.
 //
 // A group of G lanes handles a row, each lane eight consecutive elements at
 // a time (one 16-byte bf16 vector or two fp32 vectors), so that a lane's
@@ -84,17 +87,20 @@ __device__ __forceinline__ void store_codes(uint8_t* p, uint64_t packed) {
 }
 
 // The codes of eight elements f (the first `live` of them real; the others
-// get code 0) with the uniform draws in w, packed BITS bits each.
+// get code 0) with the uniform draws of element e in the top 24 bits of w[e],
+// packed BITS bits each.  The division by the scale is the correctly rounded
+// fp32 quotient (the compiler's default for '/' on this target; no fast-math
+// flags).
 template <int BITS, bool FULL>
-__device__ __forceinline__ uint64_t code_group(const float (&f)[8], int live, float z, float inv, float B,
-                                               const uint32_t (&w)[4]) {
+__device__ __forceinline__ uint64_t code_group(const float (&f)[8], int live, float z, float s, float B,
+                                               const uint32_t (&w)[8]) {
     uint32_t part[2] = {0u, 0u};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const float t = (f[e] - z) * inv;
+        const float t = (f[e] - z) / s;
         const float fl = floorf(t);
         const float fr = t - fl;
-        const float u = static_cast<float>((w[e / 2] >> (16 * (e & 1))) & 0xffffu) * 1.52587890625e-5f;   // 2^-16
+        const float u = static_cast<float>(w[e] >> 8) * 5.9604644775390625e-8f;   // 2^-24
         float q = u < fr ? fl + 1.f : fl;
         q = q < B ? q : B;
         uint32_t c = static_cast<uint32_t>(q);
@@ -190,7 +196,6 @@ __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
     const float z = ok && a.d > 0 ? mn : 0.f;
     const float R = ok && a.d > 0 ? mx - mn : 0.f;
     const float s = R / B;
-    const float inv = R > 0.f ? B / R : 0.f;
     if (!valid) return;
     const uint32_t node = static_cast<uint32_t>(a.nodes ? a.nodes[k] : k);
     uint8_t* out = a.codes + k * a.ld_codes;
@@ -204,11 +209,15 @@ __global__ __launch_bounds__(256) void quantize_rows(QArgs a) {
             } else {
                 load8<T>(row, g, a.d, f);
             }
-            uint32_t w[4] = {static_cast<uint32_t>(g), node, a.epoch, 0u};
-            philox4x32_10(w, a.key0, a.key1);
+            // elements 8g .. 8g + 7 draw from blocks 2g and 2g + 1
+            uint32_t b0[4] = {static_cast<uint32_t>(2 * g), node, a.epoch, 0u};
+            uint32_t b1[4] = {static_cast<uint32_t>(2 * g + 1), node, a.epoch, 0u};
+            philox4x32_10(b0, a.key0, a.key1);
             const int live = static_cast<int>(a.d - 8 * g < 8 ? a.d - 8 * g : 8);
-            packed = live == 8 ? code_group<BITS, true>(f, 8, z, inv, B, w)
-                               : code_group<BITS, false>(f, live, z, inv, B, w);
+            if (live > 4) philox4x32_10(b1, a.key0, a.key1);
+            const uint32_t w[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            packed = live == 8 ? code_group<BITS, true>(f, 8, z, s, B, w)
+                               : code_group<BITS, false>(f, live, z, s, B, w);
         }
         store_codes<BITS>(out + g * BITS, packed);
     }
