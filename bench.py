@@ -237,8 +237,9 @@ def pct(xs):
 class Model:
     """Device-resident inputs, weights and buffers of one workload."""
 
-    def __init__(self, w, sag, torch, seg_len):
+    def __init__(self, w, sag, torch, seg_len, fused=False):
         import numpy as np
+        self.fused = fused
         dev = torch.device("cuda:0")
         self.w, self.sag, self.torch, self.dev = w, sag, torch, dev
         self.tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -298,7 +299,8 @@ class Model:
         ctxs = []
         for l in range(w.n_layers):
             A = self.built.A
-            out, _, ctx = self.fwd(A, x, self.W[l], self.b[l], relu=w.relu[l], Out=self.out[l], ws=self.ws)
+            out, _, ctx = self.fwd(A, x, self.W[l], self.b[l], relu=w.relu[l], Out=self.out[l], ws=self.ws,
+                                   fused=self.fused)
             ctxs.append(ctx)
             x = out
         g = self.G
@@ -709,13 +711,12 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    sag.set_fusion(args.fusion)
     w = gen.make_config(args.config, args.scale)
     log(f"[bench] workload {w.name} (scale {args.scale}): drawing the graph")
     t0 = time.perf_counter()
     _ = w.edges
     log(f"[bench] graph drawn in {time.perf_counter() - t0:.1f} s")
-    m = Model(w, sag, torch, args.seg_len)
+    m = Model(w, sag, torch, args.seg_len, fused=args.fusion)
 
     if args.copy_calib:
         es = CALIB_ROW_BYTES // 2

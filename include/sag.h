@@ -40,8 +40,11 @@
  *  - Ownership: the caller allocates every buffer, including the workspace
  *    `ws` whose size the matching *_workspace_bytes function returns (those
  *    functions run on the host only).  The library allocates no device
- *    memory, keeps no per-call state and may be called from several host
- *    threads on different streams.  Launch settings (occupancy, CU count,
+ *    memory and keeps no mutable state that a computation depends on: every
+ *    choice (dtype, fusion, normalisation kind) is an argument of the call or
+ *    a field of the caller's sag_csr, so it may be called from several host
+ *    threads on different streams.  The opt-in measurement trace is per host
+ *    thread and changes no result.  Launch settings (occupancy, CU count,
  *    LDS limits) are queried once per process, so the devices one process
  *    uses must be of one kind.
  *  - Errors: arguments are validated on the host before anything is
@@ -109,7 +112,15 @@ enum {
  * then 4 * n_seg segment records {long row index, start_lo, start_hi, len},
  * then n_long + 1 int32 prefix counts of segments per long row.  Without a
  * schedule every row is treated as a medium row in natural order (correct,
- * slow on power-law degree laws). */
+ * slow on power-law degree laws).
+ *
+ * row_mean: nonzero says that every entry of row r holds 1/len(r) rounded
+ * once to fp32 (the A that sag_csr_build_normalize writes with
+ * SAG_NORM_MEAN; not its transpose).  Products over such a matrix read only
+ * its pattern and scale each row's sum by that value, once per row instead
+ * of once per entry; the result differs from reading the values only by
+ * fp32 rounding.  Zero (also for any transpose): the stored values are
+ * read. */
 typedef struct {
     int64_t n_rows;
     int64_t n_cols;
@@ -123,7 +134,7 @@ typedef struct {
     int64_t n_long;
     int64_t n_seg;
     int32_t seg_len;
-    int32_t reserved;
+    int32_t row_mean;
 } sag_csr;
 
 /* ---------------------------------------------------------------------------
@@ -161,6 +172,17 @@ typedef struct {
  */
 size_t sag_csr_build_workspace_bytes(int64_t n_edges, int64_t n_global,
                                      int64_t lo, int64_t hi, unsigned flags);
+
+/* Sizes of the build without its outputs (synchronises `stream`): the same
+ * inputs, validation and first steps as sag_csr_build_normalize up to the
+ * halo set, then *nnz and *n_halo (host) receive the entry count of A and
+ * the number of halo nodes, so a caller can allocate outputs of exactly
+ * that size.  Returns SAG_E_RANGE for an id outside [0, n_global) (the
+ * sizes are then 0).  ws as for the build (the same size query). */
+sag_status sag_csr_build_normalize_query(const int32_t* src, const int32_t* dst, int64_t n_edges,
+                                         int64_t n_global, int64_t lo, int64_t hi, unsigned flags,
+                                         int64_t* nnz /* host */, int64_t* n_halo /* host */,
+                                         void* ws, size_t ws_bytes, void* stream);
 
 sag_status sag_csr_build_normalize(const int32_t* src, const int32_t* dst, int64_t n_edges,
                                    int64_t n_global, int64_t lo, int64_t hi, unsigned flags,
@@ -218,15 +240,16 @@ sag_status sag_halo_push(const void* src, int64_t ld_src, const int32_t* ids, in
  * Each message row is one node feature vector h (finite values) quantized
  * to bits-bit codes (bits in {1, 2, 4, 8}; B = 2^bits - 1) with
  * zero = min(h), R = max(h) - min(h), scale = R / B, and per element
- * t = (h - zero) * (B / R), code = floor(t) + 1 with probability
+ * t = (h - zero) / scale, code = floor(t) + 1 with probability
  * t - floor(t), at most B (stochastic rounding; a row with R = 0 has all
  * codes 0; a subnormal R gives unspecified codes).  Each step is an fp32
  * operation rounded to nearest even, in that order.  The draw of element j
  * of stream id `node` in call `epoch`: Philox4x32-10 (Salmon, Moraes, Dror,
  * Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC'11) at counter
- * (j / 8, node, epoch, 0), key (seed & 0xffffffff, seed >> 32), 16-bit half
- * j % 2 (low first) of word (j / 2) % 4, times 2^-16; code + 1 when the
- * draw is below t - floor(t).
+ * (j / 4, node, epoch, 0), key (seed & 0xffffffff, seed >> 32), the top 24
+ * bits of word j % 4 times 2^-24 (the fp32 uniform on [0, 1)); code + 1
+ * when the draw is below t - floor(t).  For every t >= 1/2 the code's
+ * expectation is then exactly t (Sylvie, "Unbiased Low-bit Module").
  *
  * Codes: row k at codes + k * ld_codes (bytes); element j in bits
  * [bits*j, bits*j + bits) little-endian; codes must be 16-byte aligned and
@@ -293,6 +316,12 @@ sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dty
  * sag_*_save_bytes and its content is private to the library.  The
  * backward call must get the same A^T, H_ext, W, save and sizes.
  *
+ * Options (forward calls): a bit set; SAG_LAYER_FUSED asks for the fused
+ * aggregate -> transform kernel (sag_aggregate_transform) where it applies
+ * (the layer aggregates first and the widths fit); otherwise, and by
+ * default (0), the separate SpMM and product run.  Both give the same
+ * results up to fp32 summation order.  Unknown bits return SAG_E_INVALID.
+ *
  * Widths.  The SpMM width min(d_in, d_out) is at most 1024 (fp32) or 2048
  * (bf16).  The dense products keep their weight slice in LDS, so the K of
  * each (d_in for the GCN forward, 2 d_in for a SAGE layer that aggregates
@@ -301,13 +330,15 @@ sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dty
  * larger widths return SAG_E_UNSUPPORTED before any launch.
  */
 
+enum { SAG_LAYER_FUSED = 1 };
+
 /* GCN layer (CAGNET page, forward-propagation equation; Sylvie, "Forward
  * Propagation"):  Y = A H_ext W + b;  Out = relu ? max(Y, 0) : Y. */
 size_t sag_gcn_save_bytes(int64_t n_local, int64_t d_in, int64_t d_out, sag_dtype dt);
 size_t sag_gcn_forward_workspace_bytes(const sag_csr* A, int64_t d_in, int64_t d_out, sag_dtype dt);
 sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
                                  const void* W, const float* b, int64_t d_out, int relu,
-                                 sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                 unsigned options, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
                                  void* save, size_t save_bytes,
                                  void* ws, size_t ws_bytes, void* stream);
 
@@ -338,14 +369,17 @@ sag_status sag_gcn_layer_backward(const sag_csr* AT, int64_t n_local,
  *   M = A_mean H_ext;  Y = [H_local | M] W + b;  Out = relu ? max(Y,0) : Y.
  * W: [2 * d_in, d_out]; rows 0 .. d_in-1 act on the node's own row, the rest
  * on M.  A_mean is the CSR of sag_csr_build_normalize with the mean
- * normalisation: every entry of row r holds 1/len(r), so the forward reads
- * only the pattern and scales each row's sum by that value. */
+ * normalisation; tagged row_mean, the forward reads only its pattern and
+ * scales each row's sum by 1/len(r).  Any other CSR is used with its stored
+ * values (a sum aggregator for SAG_NORM_NONE), in the forward and, through
+ * its transpose, in the backward alike. */
 size_t sag_sage_save_bytes(int64_t n_local, int64_t d_in, int64_t d_out, sag_dtype dt);
 size_t sag_sage_forward_workspace_bytes(const sag_csr* A_mean, int64_t d_in, int64_t d_out,
                                         sag_dtype dt);
 sag_status sag_sage_layer_forward(const sag_csr* A_mean, const void* H_ext, int64_t ldh,
                                   int64_t d_in, const void* W, const float* b, int64_t d_out,
-                                  int relu, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                  int relu, unsigned options, sag_dtype dt, void* Y_pre, void* Out,
+                                  int64_t ldo,
                                   void* save, size_t save_bytes,
                                   void* ws, size_t ws_bytes, void* stream);
 
@@ -376,22 +410,16 @@ sag_status sag_sage_layer_backward(const sag_csr* AT_mean, int64_t n_local,
  * dt, W, b, H_ext, Out and ld's as for the layers; Z is [n_local, d_in]
  * (ld ldz).  Supported: d_out <= 256 and d_in up to about 1000 bf16 / 500
  * fp32 elements (GraphSAGE: half that); else SAG_E_UNSUPPORTED before any
- * launch.  After sag_set_fusion(1) the GCN and GraphSAGE forward calls use
- * it by themselves when they aggregate first and the widths fit (off by
- * default: on the 2.45M-node graph the separate SpMM and product are
- * faster).  ws: sag_aggregate_transform_workspace_bytes (16-B aligned). */
+ * launch.  The GCN and GraphSAGE forward calls use it when given
+ * SAG_LAYER_FUSED.  A row_mean CSR is summed over its pattern and each row
+ * scaled, as in the separate SpMM.
+ * ws: sag_aggregate_transform_workspace_bytes (16-B aligned). */
 size_t sag_aggregate_transform_workspace_bytes(const sag_csr* A, int64_t d_in, int64_t d_out,
                                                int self, sag_dtype dt);
 sag_status sag_aggregate_transform(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
                                    const void* W, const float* b, int64_t d_out, int self,
                                    int relu, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
                                    void* Z, int64_t ldz, void* ws, size_t ws_bytes, void* stream);
-/* Process-wide switch for the layers' use of the fused kernel (1: use it
- * where it applies; 0, the default: separate SpMM and product).  Returns
- * the previous setting.  Not synchronised with calls running on other
- * host threads. */
-int sag_set_fusion(int enable);
-
 /* ---------------------------------------------------------------------------
  * Graph-attention layer.  The pages name GAT (Velickovic et al., 2018) among
  * the models that partitioned full-graph training serves (Sylvie, first
@@ -474,15 +502,17 @@ sag_status sag_gemm_tn(int64_t M, int64_t N, const void* A1, int64_t lda1, int64
                        void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
- * Measurement (opt-in; process-wide state, for benchmarks and profiling).
- * While enabled, every internal operation (SpMM, dense product, mask,
+ * Measurement (opt-in, for benchmarks and profiling; not part of any
+ * computation: results are the same with it on or off).  The switch and
+ * the records belong to the calling host thread, so threads do not see each
+ * other's.  While enabled, every internal operation (SpMM, dense product, mask,
  * packing of B, halo gather) records a pair of HIP events on its stream,
  * with its name and shape ("spmm[bf16,rows,nnz,d]", "gemm_nn[bf16,M,K,N]",
  * ...), its algorithmic bytes (each operand read once, each output written
  * once: for the SpMM 8 (rows + 1) + 8 nnz + elt d (cols + rows)) and flops.
  * sag_trace_get synchronises on the record's stop event and returns its
  * elapsed milliseconds; name receives at most name_cap bytes including the
- * terminating NUL.  sag_trace_clear destroys the records. */
+ * terminating NUL.  sag_trace_clear destroys the calling thread's records. */
 sag_status sag_trace_enable(int on);
 int64_t sag_trace_count(void);
 sag_status sag_trace_get(int64_t i, char* name, size_t name_cap, float* ms, int64_t* bytes,

@@ -21,6 +21,7 @@ SAG_E_RANGE, SAG_E_HIP, SAG_E_UNSUPPORTED = -4, -5, -6
 SAG_F32, SAG_BF16 = 0, 1
 SAG_NORM_GCN, SAG_NORM_MEAN, SAG_NORM_NONE = 0, 1, 2
 SAG_SYMMETRIZE, SAG_SELF_LOOPS = 1, 2
+SAG_LAYER_FUSED = 1
 
 
 class SagCsr(ctypes.Structure):
@@ -29,7 +30,7 @@ class SagCsr(ctypes.Structure):
         ("indptr", vp), ("indices", vp), ("values", vp),
         ("sched", vp),
         ("n_short", i64), ("n_medium", i64), ("n_long", i64), ("n_seg", i64),
-        ("seg_len", i32), ("reserved", i32),
+        ("seg_len", i32), ("row_mean", i32),
     ]
 
 
@@ -38,6 +39,7 @@ PCSR = P(SagCsr)
 # name -> (restype, argtypes)
 SIGNATURES = {
     "sag_csr_build_workspace_bytes": (sz, [i64, i64, i64, i64, u32]),
+    "sag_csr_build_normalize_query": (cint, [vp, vp, i64, i64, i64, i64, u32, P(i64), P(i64), vp, sz, vp]),
     "sag_csr_build_normalize": (cint, [vp, vp, i64, i64, i64, i64, u32, cint, vp, i64, i64,
                                        vp, vp, vp, vp, vp, vp, vp, vp, P(i64), P(i64), vp, sz, vp]),
     "sag_csr_schedule_bytes": (sz, [i64, i64, i32]),
@@ -54,14 +56,14 @@ SIGNATURES = {
     "sag_spmm_csr_t": (cint, [PCSR, vp, i64, cint, i64, vp, i64, cint, vp, i64, i64, vp, sz, vp]),
     "sag_gcn_save_bytes": (sz, [i64, i64, i64, cint]),
     "sag_gcn_forward_workspace_bytes": (sz, [PCSR, i64, i64, cint]),
-    "sag_gcn_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, cint, vp, vp, i64,
+    "sag_gcn_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, u32, cint, vp, vp, i64,
                                      vp, sz, vp, sz, vp]),
     "sag_gcn_backward_workspace_bytes": (sz, [PCSR, i64, i64, i64, cint]),
     "sag_gcn_layer_backward": (cint, [PCSR, i64, vp, i64, i64, vp, i64, cint, vp, vp, i64,
                                       vp, vp, vp, i64, cint, vp, sz, vp, sz, vp]),
     "sag_sage_save_bytes": (sz, [i64, i64, i64, cint]),
     "sag_sage_forward_workspace_bytes": (sz, [PCSR, i64, i64, cint]),
-    "sag_sage_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, cint, vp, vp, i64,
+    "sag_sage_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, u32, cint, vp, vp, i64,
                                       vp, sz, vp, sz, vp]),
     "sag_sage_backward_workspace_bytes": (sz, [PCSR, i64, i64, i64, cint]),
     "sag_sage_layer_backward": (cint, [PCSR, i64, vp, i64, i64, vp, i64, cint, vp, vp, i64,
@@ -69,7 +71,6 @@ SIGNATURES = {
     "sag_aggregate_transform_workspace_bytes": (sz, [PCSR, i64, i64, cint, cint]),
     "sag_aggregate_transform": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, cint, cint, vp, vp, i64,
                                        vp, i64, vp, sz, vp]),
-    "sag_set_fusion": (cint, [cint]),
     "sag_gat_save_bytes": (sz, [i64, i64, i64, i64, cint]),
     "sag_gat_forward_workspace_bytes": (sz, [PCSR, i64, i64, i64, cint]),
     "sag_gat_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, vp, vp, i64, i64, ctypes.c_float, cint,

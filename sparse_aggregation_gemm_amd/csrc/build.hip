@@ -242,32 +242,34 @@ extern "C" size_t sag_csr_build_workspace_bytes(int64_t n_edges, int64_t n_globa
     return w.tmp_bytes;
 }
 
-extern "C" sag_status sag_csr_build_normalize(const int32_t* src, const int32_t* dst, int64_t n_edges,
-                                              int64_t n_global, int64_t lo, int64_t hi, unsigned flags,
-                                              sag_norm norm, const int32_t* deg_global,
-                                              int64_t cap_nnz, int64_t cap_halo,
-                                              int64_t* indptr, int32_t* indices, float* values,
-                                              int64_t* indptr_t, int32_t* indices_t, float* values_t,
-                                              int32_t* deg, int32_t* halo_gid,
-                                              int64_t* nnz_out, int64_t* n_halo_out,
-                                              void* ws, size_t ws_bytes, void* stream) {
-    if (!nnz_out || !n_halo_out) return fail(SAG_E_INVALID, "build: null size outputs");
-    *nnz_out = 0;
-    *n_halo_out = 0;
-    if (n_edges < 0 || n_global < 0 || cap_nnz < 0 || cap_halo < 0)
-        return fail(SAG_E_INVALID, "build: negative size");
+namespace sag {
+namespace {
+
+// Validation of the edge-list arguments shared by the build and its query.
+sag_status check_build_inputs(const int32_t* src, const int32_t* dst, int64_t n_edges, int64_t n_global, int64_t lo,
+                              int64_t hi, unsigned flags) {
+    if (n_edges < 0 || n_global < 0) return fail(SAG_E_INVALID, "build: negative size");
     if (n_global > INT32_MAX) return fail(SAG_E_INVALID, "build: n_global exceeds int32 ids");
     if (!(0 <= lo && lo <= hi && hi <= n_global)) return fail(SAG_E_INVALID, "build: need 0 <= lo <= hi <= n_global");
     if (flags & ~static_cast<unsigned>(SAG_SYMMETRIZE | SAG_SELF_LOOPS))
         return fail(SAG_E_INVALID, "build: unknown flag");
-    if (norm != SAG_NORM_GCN && norm != SAG_NORM_MEAN && norm != SAG_NORM_NONE)
-        return fail(SAG_E_INVALID, "build: bad norm");
     if (n_edges > 0 && (!src || !dst)) return fail(SAG_E_INVALID, "build: null edge list");
-    if (!indptr) return fail(SAG_E_INVALID, "build: null indptr");
-    if (cap_nnz > 0 && (!indices || !values)) return fail(SAG_E_INVALID, "build: null indices/values");
-    const bool want_t = indptr_t || indices_t || values_t;
-    if (want_t && (!indptr_t || (cap_nnz > 0 && (!indices_t || !values_t))))
-        return fail(SAG_E_INVALID, "build: transpose outputs must be all given or all NULL");
+    return SAG_OK;
+}
+
+// The front half of the build: keys of the 0/1 pattern sorted and made
+// unique, the halo set marked and ranked.  Leaves in the workspace what the
+// back half reads (the unique keys, the halo ranks in w.pos, the marks in
+// w.flags) and returns the sizes.  Synchronises the stream.
+struct Front {
+    BuildWs w;
+    BuildGeom g;
+    uint64_t* uniq = nullptr;
+    int64_t nnz = 0, n_halo = 0;
+};
+
+sag_status build_front(const int32_t* src, const int32_t* dst, int64_t n_edges, int64_t n_global, int64_t lo,
+                       int64_t hi, unsigned flags, void* ws, size_t ws_bytes, hipStream_t s, Front& f) {
     const int64_t n_local = hi - lo;
     const uint64_t nc = static_cast<uint64_t>(n_local + n_global);
     const int key_bits = bits_for(n_local > 0 ? static_cast<uint64_t>(n_local) * nc - 1 : 0);
@@ -275,9 +277,10 @@ extern "C" sag_status sag_csr_build_normalize(const int32_t* src, const int32_t*
     const int64_t cap = entry_capacity(n_edges, n_local, flags);
     if (ws_bytes < sag_csr_build_workspace_bytes(n_edges, n_global, lo, hi, flags) || !ws)
         return fail(SAG_E_WORKSPACE, "build: workspace too small");
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    BuildWs w = carve_build(ws, ws_bytes, cap > 0 ? cap : 1, n_global, n_local);
-    BuildGeom g{lo, hi, n_local, n_global, nc};
+    BuildWs& w = f.w;
+    w = carve_build(ws, ws_bytes, cap > 0 ? cap : 1, n_global, n_local);
+    f.g = BuildGeom{lo, hi, n_local, n_global, nc};
+    const BuildGeom& g = f.g;
 
     // 1. expand the edge list into keys; count them; detect bad ids
     SAG_CHECK_HIP(hipMemsetAsync(w.counter, 0, sizeof(unsigned long long), s));
@@ -329,6 +332,61 @@ extern "C" sag_status sag_csr_build_normalize(const int32_t* src, const int32_t*
         SAG_CHECK_HIP(hipMemcpyAsync(&n_halo, w.pos + n_global, sizeof(n_halo), hipMemcpyDeviceToHost, s));
         SAG_CHECK_HIP(hipStreamSynchronize(s));
     }
+    f.uniq = uniq;
+    f.nnz = nnz;
+    f.n_halo = n_halo;
+    return SAG_OK;
+}
+
+}  // namespace
+}  // namespace sag
+
+extern "C" sag_status sag_csr_build_normalize_query(const int32_t* src, const int32_t* dst, int64_t n_edges,
+                                                    int64_t n_global, int64_t lo, int64_t hi, unsigned flags,
+                                                    int64_t* nnz_out, int64_t* n_halo_out, void* ws,
+                                                    size_t ws_bytes, void* stream) {
+    if (!nnz_out || !n_halo_out) return fail(SAG_E_INVALID, "build_query: null size outputs");
+    *nnz_out = 0;
+    *n_halo_out = 0;
+    SAG_TRY(check_build_inputs(src, dst, n_edges, n_global, lo, hi, flags));
+    Front f;
+    SAG_TRY(build_front(src, dst, n_edges, n_global, lo, hi, flags, ws, ws_bytes, static_cast<hipStream_t>(stream),
+                        f));
+    *nnz_out = f.nnz;
+    *n_halo_out = f.n_halo;
+    return SAG_OK;
+}
+
+extern "C" sag_status sag_csr_build_normalize(const int32_t* src, const int32_t* dst, int64_t n_edges,
+                                              int64_t n_global, int64_t lo, int64_t hi, unsigned flags,
+                                              sag_norm norm, const int32_t* deg_global,
+                                              int64_t cap_nnz, int64_t cap_halo,
+                                              int64_t* indptr, int32_t* indices, float* values,
+                                              int64_t* indptr_t, int32_t* indices_t, float* values_t,
+                                              int32_t* deg, int32_t* halo_gid,
+                                              int64_t* nnz_out, int64_t* n_halo_out,
+                                              void* ws, size_t ws_bytes, void* stream) {
+    if (!nnz_out || !n_halo_out) return fail(SAG_E_INVALID, "build: null size outputs");
+    *nnz_out = 0;
+    *n_halo_out = 0;
+    SAG_TRY(check_build_inputs(src, dst, n_edges, n_global, lo, hi, flags));
+    if (cap_nnz < 0 || cap_halo < 0) return fail(SAG_E_INVALID, "build: negative size");
+    if (norm != SAG_NORM_GCN && norm != SAG_NORM_MEAN && norm != SAG_NORM_NONE)
+        return fail(SAG_E_INVALID, "build: bad norm");
+    if (!indptr) return fail(SAG_E_INVALID, "build: null indptr");
+    if (cap_nnz > 0 && (!indices || !values)) return fail(SAG_E_INVALID, "build: null indices/values");
+    const bool want_t = indptr_t || indices_t || values_t;
+    if (want_t && (!indptr_t || (cap_nnz > 0 && (!indices_t || !values_t))))
+        return fail(SAG_E_INVALID, "build: transpose outputs must be all given or all NULL");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    Front f;
+    SAG_TRY(build_front(src, dst, n_edges, n_global, lo, hi, flags, ws, ws_bytes, s, f));
+    BuildWs& w = f.w;
+    const BuildGeom& g = f.g;
+    const int64_t n_local = g.n_local;
+    const uint64_t nc = g.nc;
+    uint64_t* uniq = f.uniq;
+    const int64_t nnz = f.nnz, n_halo = f.n_halo;
     *nnz_out = nnz;
     *n_halo_out = n_halo;
     if (nnz > cap_nnz || n_halo > cap_halo)

@@ -49,7 +49,8 @@ template <class T>
 struct FusedArgs {
     const int64_t* indptr;
     const int32_t* idx;
-    const float* val;
+    const float* val;          // null: unit values (a row-mean CSR's pattern)
+    int row_mean;              // scale each summed row by 1/len (values not read)
     const int4* rec;           // schedule records (null: natural row order)
     int64_t n_rows;
     int64_t n_summed;          // records [0, n_summed) are summed here, the rest are long rows
@@ -161,6 +162,14 @@ __global__ __launch_bounds__(kThreads) void agg_transform(FusedArgs<T> p) {
             rowsum::group_row_sum<T, G, NV>(p.X, p.ldx, p.C, p.idx, p.val, start, mylen, lmax, acc);
         } else if (summed) {
             rowsum::wave_row_sum<T, G, NV>(p.X, p.ldx, p.C, p.idx, p.val, start, len, acc);
+        }
+        if (summed && p.row_mean && len > 0) {
+            // the value the mean normalisation stores, 1/len rounded once
+            const float rs = 1.f / static_cast<float>(len);
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int k = 0; k < V; ++k) acc[v][k] *= rs;
         }
         if (row >= 0 && !summed) {
             const int64_t j = i - p.n_summed;
@@ -374,15 +383,6 @@ constexpr size_t kMaxLds = 96 * 1024;
 
 }  // namespace
 
-namespace {
-// Off by default: on the workloads measured here the separate SpMM and
-// product are faster (the fused kernel's row sums run at lower occupancy,
-// with a barrier per 32-row tile, than the SpMM's short-lived wavefronts).
-int g_fusion = 0;
-}  // namespace
-
-bool fusion_enabled() { return g_fusion != 0; }
-
 bool agg_transform_fits(int64_t d_in, int64_t d_out, bool self, sag_dtype dt) {
     if (d_in <= 0 || d_out <= 0 || d_out > kMaxNB * 32) return false;
     if (d_in > (dt == SAG_BF16 ? 2048 : 1024)) return false;
@@ -439,7 +439,8 @@ sag_status run_typed(const sag_csr& A, const void* H_ext, int64_t ldh, int64_t d
     FusedArgs<T> p{};
     p.indptr = A.indptr;
     p.idx = A.indices;
-    p.val = A.values;
+    p.row_mean = A.row_mean != 0;
+    p.val = p.row_mean ? nullptr : A.values;
     p.rec = reinterpret_cast<const int4*>(A.sched);
     p.n_rows = A.n_rows;
     p.n_summed = has_long ? A.n_short + A.n_medium : A.n_rows;
@@ -489,7 +490,7 @@ sag_status agg_transform_run(const sag_csr& A, const void* H_ext, int64_t ldh, i
     const int64_t es = elt_size(dt);
     const int64_t K = (self ? 2 : 1) * d_in;
     // algorithmic bytes: CSR arrays, H_ext once, W, Z and the outputs once
-    const int64_t bytes = 8 * (A.n_rows + 1) + A.nnz * (A.values ? 8 : 4) + es * d_in * A.n_cols +
+    const int64_t bytes = 8 * (A.n_rows + 1) + A.nnz * (A.values && !A.row_mean ? 8 : 4) + es * d_in * A.n_cols +
                           es * K * d_out + (Z ? es * d_in * A.n_rows : 0) +
                           es * d_out * A.n_rows * (Y_pre ? 2 : 1);
     TraceScope trace(trace_enabled() ? shape_name(self ? "agg_transform_sage" : "agg_transform_gcn",
@@ -536,8 +537,4 @@ extern "C" sag_status sag_aggregate_transform(const sag_csr* A, const void* H_ex
                              ws_bytes, static_cast<hipStream_t>(stream));
 }
 
-extern "C" int sag_set_fusion(int enable) {
-    const int old = g_fusion;
-    g_fusion = enable ? 1 : 0;
-    return old;
-}
+

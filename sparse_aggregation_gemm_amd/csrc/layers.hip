@@ -149,10 +149,12 @@ extern "C" size_t sag_gcn_forward_workspace_bytes(const sag_csr* A, int64_t d_in
 }
 
 extern "C" sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
-                                            const void* W, const float* b, int64_t d_out, int relu, sag_dtype dt,
-                                            void* Y_pre, void* Out, int64_t ldo, void* save, size_t save_bytes,
-                                            void* ws, size_t ws_bytes, void* stream) {
+                                            const void* W, const float* b, int64_t d_out, int relu,
+                                            unsigned options, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                            void* save, size_t save_bytes, void* ws, size_t ws_bytes,
+                                            void* stream) {
     SAG_TRY(check_layer_common("gcn_forward", A, H_ext, ldh, d_in, W, d_out, dt));
+    if (options & ~static_cast<unsigned>(SAG_LAYER_FUSED)) return fail(SAG_E_INVALID, "gcn_forward: unknown option");
     if (!nn_k_fits(d_in, 0, dt)) return fail(SAG_E_UNSUPPORTED, "gcn_forward: d_in too large for the transform");
     const int64_t n_l = A->n_rows;
     SAG_TRY(check_dense("gcn_forward Out", Out, n_l, d_out, ldo, dt));
@@ -177,12 +179,16 @@ extern "C" sag_status sag_gcn_layer_forward(const sag_csr* A, const void* H_ext,
     e.bias = b;
     e.relu = relu;
     e.pre = Y_pre;
+    e.row_mean = A->row_mean != 0;
     if (aggregate_first(d_in, d_out)) {
         const int64_t ldz = ldv(d_in, dt);
-        if (fusion_enabled() && w.fz_bytes)
+        if ((options & SAG_LAYER_FUSED) && w.fz_bytes)
             return agg_transform_run(*A, H_ext, ldh, d_in, W, b, d_out, false, relu, dt, Y_pre, Out, ldo, save, ldz,
                                      w.fz, w.fz_bytes, s);
-        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldz, dt, Epilogue{}, w.spmm, w.spmm_bytes, s));
+        Epilogue ez;
+        ez.row_mean = A->row_mean != 0;
+        SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldz, dt, ez, w.spmm, w.spmm_bytes, s));
+        e.row_mean = 0;
         GemmA a;
         a.a1 = save; a.lda1 = ldz; a.k1 = d_in; a.m1 = n_l;
         return gemm_run(n_l, d_out, a, w.Bp, dt, Out, ldo, e, s);
@@ -293,10 +299,12 @@ extern "C" size_t sag_sage_forward_workspace_bytes(const sag_csr* A, int64_t d_i
 }
 
 extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext, int64_t ldh, int64_t d_in,
-                                             const void* W, const float* b, int64_t d_out, int relu, sag_dtype dt,
-                                             void* Y_pre, void* Out, int64_t ldo, void* save, size_t save_bytes,
-                                             void* ws, size_t ws_bytes, void* stream) {
+                                             const void* W, const float* b, int64_t d_out, int relu,
+                                             unsigned options, sag_dtype dt, void* Y_pre, void* Out, int64_t ldo,
+                                             void* save, size_t save_bytes, void* ws, size_t ws_bytes,
+                                             void* stream) {
     SAG_TRY(check_layer_common("sage_forward", A, H_ext, ldh, d_in, W, d_out, dt));
+    if (options & ~static_cast<unsigned>(SAG_LAYER_FUSED)) return fail(SAG_E_INVALID, "sage_forward: unknown option");
     if (!nn_k_fits(d_in, aggregate_first(d_in, d_out) ? d_in : 0, dt))
         return fail(SAG_E_UNSUPPORTED, "sage_forward: d_in too large for the transform");
     const int64_t n_l = A->n_rows;
@@ -330,13 +338,13 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
         nl.n0 = nl.nsplit = d_out;
         SAG_TRY(pack_b(src, d_in, d_in, nl, dt, w.Bp, s));
         const int64_t ldm = ldv(d_in, dt);
-        if (fusion_enabled() && w.fz_bytes)
+        if ((options & SAG_LAYER_FUSED) && w.fz_bytes)
             return agg_transform_run(*A, H_ext, ldh, d_in, W, b, d_out, true, relu, dt, Y_pre, Out, ldo, save, ldm,
                                      w.fz, w.fz_bytes, s);
-        // (the mean normalisation gives every entry of row r the value
-        // 1/len(r): the SpMM scales each row's sum instead of reading values)
+        // (a row-mean CSR gives every entry of row r the value 1/len(r): the
+        // SpMM then scales each row's sum instead of reading values)
         Epilogue em;
-        em.row_mean = 1;
+        em.row_mean = A->row_mean != 0;
         SAG_TRY(spmm_run(*A, H_ext, ldh, dt, d_in, save, ldm, dt, em, w.spmm, w.spmm_bytes, s));
         GemmA a;
         a.a1 = H_ext; a.lda1 = ldh; a.k1 = d_in; a.m1 = n_l;
@@ -365,7 +373,7 @@ extern "C" sag_status sag_sage_layer_forward(const sag_csr* A, const void* H_ext
     e.addend = static_cast<const char*>(w.t1) + np * es;
     e.ld_add = ldpt;
     e.n_add = n_l;
-    e.row_mean = 1;
+    e.row_mean = A->row_mean != 0;
     return spmm_run(*A, w.t1, ldpt, dt, d_out, Out, ldo, dt, e, w.spmm, w.spmm_bytes, s);
 }
 

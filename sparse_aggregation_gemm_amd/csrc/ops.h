@@ -44,7 +44,8 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
                     hipStream_t s);
 sag_status check_csr(const char* name, const sag_csr* A);
 // Only the long rows of a scheduled A (nothing without a schedule): row j of
-// the long bin's sum goes to Y row j (compact), with no epilogue.
+// the long bin's sum goes to Y row j (compact), with no epilogue but the
+// row-mean scaling when A is tagged row_mean.
 sag_status spmm_long_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype dt, int64_t d, void* Y,
                          int64_t ldy, void* ws, size_t ws_bytes, hipStream_t s);
 
@@ -56,9 +57,6 @@ size_t agg_transform_ws_bytes(const sag_csr& A, int64_t d_in, int64_t d_out, boo
 sag_status agg_transform_run(const sag_csr& A, const void* H_ext, int64_t ldh, int64_t d_in, const void* W,
                              const float* b, int64_t d_out, bool self, int relu, sag_dtype dt, void* Y_pre, void* Out,
                              int64_t ldo, void* Z, int64_t ldz, void* ws, size_t ws_bytes, hipStream_t s);
-// Whether the layers use the fused kernel where it applies (sag_set_fusion).
-bool fusion_enabled();
-
 // ---- dense products (MFMA) -------------------------------------------------------
 // Operand A of a GEMM: up to two column blocks along K, each [rows, K_i].
 // Rows >= m1 of block 1 read as zero (m1 < M lets block 1 cover only the

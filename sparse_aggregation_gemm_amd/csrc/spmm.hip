@@ -382,8 +382,10 @@ sag_status spmm_long_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype
                          void* ws, size_t ws_bytes, hipStream_t s) {
     if (!A.sched || A.n_long == 0 || d == 0) return SAG_OK;
     if (ws_bytes < spmm_ws_bytes(A, d) || !ws) return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
-    if (dt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, Epilogue{}, ws, s, true);
-    return run_typed<float, float>(A, X, ldx, d, Y, ldy, Epilogue{}, ws, s, true);
+    Epilogue e;
+    e.row_mean = A.row_mean != 0;
+    if (dt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, e, ws, s, true);
+    return run_typed<float, float>(A, X, ldx, d, Y, ldy, e, ws, s, true);
 }
 
 sag_status check_csr(const char* name, const sag_csr* A) {
@@ -458,6 +460,7 @@ static sag_status spmm_entry(const char* name, const sag_csr* A, const void* X, 
     e.addend = addend;
     e.ld_add = ld_add;
     e.n_add = addend ? n_add : 0;
+    e.row_mean = A->row_mean != 0;
     return spmm_run(*A, X, ldx, xt, d, Y, ldy, yt, e, ws, ws_bytes, static_cast<hipStream_t>(stream));
 }
 

@@ -1,9 +1,10 @@
 // Opt-in measurement: HIP events recorded on the caller's stream around each
 // internal operation (SpMM, dense products, gather, mask, build), with the
-// operation's algorithmic bytes and flops.  Process-wide state guarded by a
-// mutex; off unless sag_trace_enable(1) was called.
+// operation's algorithmic bytes and flops.  The switch and the records are
+// per host thread (thread_local), so concurrent callers neither see nor
+// disturb each other's records; off unless the thread called
+// sag_trace_enable(1).  No computation reads this state.
 #include <cstdio>
-#include <mutex>
 #include <vector>
 
 #include "trace.h"
@@ -17,35 +18,37 @@ struct Rec {
     int64_t bytes = 0, flops = 0;
 };
 
-std::mutex g_mu;
-bool g_on = false;
-std::vector<Rec> g_recs;
+thread_local bool t_on = false;
+thread_local std::vector<Rec> t_recs;
 
 }  // namespace
 
-bool trace_enabled() {
-    std::lock_guard<std::mutex> l(g_mu);
-    return g_on;
-}
+bool trace_enabled() { return t_on; }
 
 TraceScope::TraceScope(const std::string& name, hipStream_t s, int64_t bytes, int64_t flops)
     : stream_(s), index_(-1) {
-    std::lock_guard<std::mutex> l(g_mu);
-    if (!g_on) return;
+    if (!t_on) return;
     Rec r;
     r.name = name;
     r.bytes = bytes;
     r.flops = flops;
-    if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
-    if (hipEventRecord(r.a, s) != hipSuccess) return;
-    g_recs.push_back(r);
-    index_ = static_cast<int64_t>(g_recs.size()) - 1;
+    if (hipEventCreate(&r.a) != hipSuccess) return;
+    if (hipEventCreate(&r.b) != hipSuccess) {
+        (void)hipEventDestroy(r.a);
+        return;
+    }
+    if (hipEventRecord(r.a, s) != hipSuccess) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+        return;
+    }
+    t_recs.push_back(r);
+    index_ = static_cast<int64_t>(t_recs.size()) - 1;
 }
 
 TraceScope::~TraceScope() {
     if (index_ < 0) return;
-    std::lock_guard<std::mutex> l(g_mu);
-    if (index_ < static_cast<int64_t>(g_recs.size())) (void)hipEventRecord(g_recs[index_].b, stream_);
+    if (index_ < static_cast<int64_t>(t_recs.size())) (void)hipEventRecord(t_recs[index_].b, stream_);
 }
 
 std::string shape_name(const char* op, const char* dtype, int64_t a, int64_t b, int64_t c) {
@@ -60,27 +63,17 @@ std::string shape_name(const char* op, const char* dtype, int64_t a, int64_t b, 
 using namespace sag;
 
 extern "C" sag_status sag_trace_enable(int on) {
-    std::lock_guard<std::mutex> l(g_mu);
-    g_on = on != 0;
+    t_on = on != 0;
     return SAG_OK;
 }
 
-extern "C" int64_t sag_trace_count(void) {
-    std::lock_guard<std::mutex> l(g_mu);
-    return static_cast<int64_t>(g_recs.size());
-}
+extern "C" int64_t sag_trace_count(void) { return static_cast<int64_t>(t_recs.size()); }
 
 extern "C" sag_status sag_trace_get(int64_t i, char* name, size_t name_cap, float* ms, int64_t* bytes,
                                     int64_t* flops) {
-    Rec r;
-    {
-        std::lock_guard<std::mutex> l(g_mu);
-        if (i < 0 || i >= static_cast<int64_t>(g_recs.size())) return fail(SAG_E_INVALID, "trace: index out of range");
-        r = g_recs[i];
-    }
-    if (name && name_cap) {
-        std::snprintf(name, name_cap, "%s", r.name.c_str());
-    }
+    if (i < 0 || i >= static_cast<int64_t>(t_recs.size())) return fail(SAG_E_INVALID, "trace: index out of range");
+    const Rec& r = t_recs[i];
+    if (name && name_cap) std::snprintf(name, name_cap, "%s", r.name.c_str());
     if (bytes) *bytes = r.bytes;
     if (flops) *flops = r.flops;
     if (ms) {
@@ -91,12 +84,11 @@ extern "C" sag_status sag_trace_get(int64_t i, char* name, size_t name_cap, floa
 }
 
 extern "C" sag_status sag_trace_clear(void) {
-    std::lock_guard<std::mutex> l(g_mu);
-    for (Rec& r : g_recs) {
+    for (Rec& r : t_recs) {
         if (r.b) (void)hipEventSynchronize(r.b);
         if (r.a) (void)hipEventDestroy(r.a);
         if (r.b) (void)hipEventDestroy(r.b);
     }
-    g_recs.clear();
+    t_recs.clear();
     return SAG_OK;
 }

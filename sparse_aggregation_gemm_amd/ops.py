@@ -83,6 +83,7 @@ class Csr:
     indices: torch.Tensor
     values: torch.Tensor | None
     sched: torch.Tensor | None = None
+    row_mean: bool = False     # every entry of row r is 1/len(r) (the build's mean-normalised A)
     raw: L.SagCsr = field(default_factory=L.SagCsr)
 
     def __post_init__(self):
@@ -92,6 +93,7 @@ class Csr:
         self.raw.indptr = _ptr(self.indptr)
         self.raw.indices = _ptr(self.indices)
         self.raw.values = _ptr(self.values)
+        self.raw.row_mean = int(bool(self.row_mean))
 
     @property
     def nnz(self) -> int:
@@ -120,6 +122,25 @@ class Built:
     @property
     def n_halo(self) -> int:
         return int(self.halo_gid.numel())
+
+
+def csr_build_normalize_query(src: torch.Tensor, dst: torch.Tensor, n_global: int, lo: int, hi: int,
+                              symmetrize: bool, self_loops: bool) -> tuple[int, int]:
+    """sag_csr_build_normalize_query: (nnz, n_halo) of the build of rows
+    [lo, hi), without its outputs.  Synchronises the current stream."""
+    dev = src.device
+    src = src.to(torch.int32).contiguous()
+    dst = dst.to(torch.int32).contiguous()
+    n_edges = src.numel()
+    flags = (L.SAG_SYMMETRIZE if symmetrize else 0) | (L.SAG_SELF_LOOPS if self_loops else 0)
+    lib = L.lib()
+    ws = _ws(lib.sag_csr_build_workspace_bytes(n_edges, n_global, lo, hi, flags), dev)
+    nnz, n_halo = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = lib.sag_csr_build_normalize_query(_ptr(src), _ptr(dst), n_edges, n_global, lo, hi, flags,
+                                           ctypes.byref(nnz), ctypes.byref(n_halo), _ptr(ws), ws.numel(),
+                                           _stream(dev))
+    L.check("sag_csr_build_normalize_query", st)
+    return nnz.value, n_halo.value
 
 
 def csr_build_normalize(src: torch.Tensor, dst: torch.Tensor, n_global: int, lo: int, hi: int,
@@ -160,7 +181,7 @@ def csr_build_normalize(src: torch.Tensor, dst: torch.Tensor, n_global: int, lo:
     L.check("sag_csr_build_normalize", st)
     nnz, n_halo = nnz.value, n_halo.value
     n_ext = n_local + n_halo
-    A = Csr(n_local, n_ext, indptr, indices[:nnz], values[:nnz])
+    A = Csr(n_local, n_ext, indptr, indices[:nnz], values[:nnz], row_mean=(norm == "mean"))
     AT = None
     if transpose:
         AT = Csr(n_ext, n_local, indptr_t[:n_ext + 1], indices_t[:nnz], values_t[:nnz])
@@ -298,7 +319,7 @@ class LayerCtx:
     relu: bool
 
 
-def _layer_forward(kind, A: Csr, H_ext, W, b, relu, want_pre, Out=None, Y_pre=None, ws=None):
+def _layer_forward(kind, A: Csr, H_ext, W, b, relu, want_pre, Out=None, Y_pre=None, ws=None, fused=False):
     lib = L.lib()
     dt = dtype_code(H_ext.dtype)
     d_in = H_ext.shape[1]
@@ -317,8 +338,8 @@ def _layer_forward(kind, A: Csr, H_ext, W, b, relu, want_pre, Out=None, Y_pre=No
     if ws is None or ws.numel() < nws:
         ws = _ws(nws, dev)
     st = getattr(lib, f"sag_{kind}_layer_forward")(
-        A.ref, _ptr(H_ext), _ld(H_ext), d_in, _ptr(W), _ptr(b), d_out, int(relu), dt,
-        _ptr(Y_pre) if want_pre else None, _ptr(Out), _ld(Out), _ptr(save), save.numel(),
+        A.ref, _ptr(H_ext), _ld(H_ext), d_in, _ptr(W), _ptr(b), d_out, int(relu),
+        L.SAG_LAYER_FUSED if fused else 0, dt, _ptr(Y_pre) if want_pre else None, _ptr(Out), _ld(Out), _ptr(save), save.numel(),
         _ptr(ws), ws.numel(), _stream(dev))
     L.check(f"sag_{kind}_layer_forward", st)
     ctx = LayerCtx(kind, save, H_ext, W, d_in, d_out, bool(relu))
@@ -354,7 +375,9 @@ def _layer_backward(ctx: LayerCtx, AT: Csr | None, n_local: int, Y, G_out, want_
 
 
 def gcn_layer_forward(A: Csr, H_ext, W, b=None, relu=True, want_pre=False, **kw):
-    """sag_gcn_layer_forward: Out = relu(A H_ext W + b).  Returns (Out, Y_pre, ctx)."""
+    """sag_gcn_layer_forward: Out = relu(A H_ext W + b).  Returns (Out, Y_pre, ctx).
+    fused=True passes SAG_LAYER_FUSED (the fused aggregate -> transform
+    kernel where it applies)."""
     return _layer_forward("gcn", A, H_ext, W, b, relu, want_pre, **kw)
 
 
@@ -402,12 +425,6 @@ def aggregate_transform(A: Csr, H_ext, W, b=None, self_rows=False, relu=True, wa
                                      _stream(dev))
     L.check("sag_aggregate_transform", st)
     return Out, Y_pre, Z
-
-
-def set_fusion(enable: bool) -> bool:
-    """sag_set_fusion: whether the layers use the fused kernel; returns the
-    previous setting."""
-    return bool(L.lib().sag_set_fusion(int(bool(enable))))
 
 
 @dataclass

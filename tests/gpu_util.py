@@ -43,6 +43,18 @@ def bits16(t: torch.Tensor) -> np.ndarray:
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
 
 
+def elementwise_rel(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / |ref| over the entries with |ref| >= 1e-3 max |ref|
+    (reported beside the bound-relative error; not a gate)."""
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    sel = np.abs(ref) >= 1e-3 * np.abs(ref).max()
+    if not np.any(sel):
+        return 0.0
+    return float(np.max(np.abs(np.asarray(got, np.float64)[sel] - ref[sel]) / np.abs(ref[sel])))
+
+
 def tol(dtype: str) -> float:
     """Error bound relative to the magnitude of the summed terms: fp32 1e-5;
     bf16 inputs with fp32 accumulation 2e-2."""

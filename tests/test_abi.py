@@ -80,18 +80,35 @@ def test_host_side_validation():
     # bad seg_len for the schedule
     assert lib.sag_csr_schedule(ctypes.byref(A), 100, fake, 1 << 20, fake, 1 << 20, None) == L.SAG_E_INVALID
     # layers: width zero, bad dtype
-    assert lib.sag_gcn_layer_forward(ctypes.byref(A), fake, 4, 0, fake, None, 4, 1, 0, None, fake, 4,
+    assert lib.sag_gcn_layer_forward(ctypes.byref(A), fake, 4, 0, fake, None, 4, 1, 0, 0, None, fake, 4,
                                      None, 0, fake, 1 << 20, None) == L.SAG_E_INVALID
-    assert lib.sag_sage_layer_forward(ctypes.byref(A), fake, 4, 4, fake, None, 4, 1, 9, None, fake, 4,
+    assert lib.sag_sage_layer_forward(ctypes.byref(A), fake, 4, 4, fake, None, 4, 1, 0, 9, None, fake, 4,
                                       None, 0, fake, 1 << 20, None) == L.SAG_E_INVALID
     assert lib.sag_gemm(4, 4, fake, 4, 4, None, 0, 0, None, 0, fake, 4, 0, None, None, 0, 0, fake, None,
                         4, 3, fake, 1 << 20, None) == L.SAG_E_INVALID
     # a width beyond what the dense products hold in LDS: refused before any launch
     A.indptr = A.indices = A.values = fake
-    assert lib.sag_gcn_layer_forward(ctypes.byref(A), fake, 4096, 4096, fake, None, 16, 1, 0, None, fake, 16,
+    assert lib.sag_gcn_layer_forward(ctypes.byref(A), fake, 4096, 4096, fake, None, 16, 1, 0, 0, None, fake, 16,
                                      None, 0, fake, 1 << 30, None) == L.SAG_E_UNSUPPORTED
-    assert lib.sag_sage_layer_forward(ctypes.byref(A), fake, 4096, 2048, fake, None, 4096, 1, 0, None, fake,
+    assert lib.sag_sage_layer_forward(ctypes.byref(A), fake, 4096, 2048, fake, None, 4096, 1, 0, 0, None, fake,
                                       4096, None, 0, fake, 1 << 30, None) == L.SAG_E_UNSUPPORTED
+    # an option bit the layers do not know: refused before any launch
+    for fwd in (lib.sag_gcn_layer_forward, lib.sag_sage_layer_forward):
+        assert fwd(ctypes.byref(A), fake, 16, 16, fake, None, 16, 1, 2, 0, None, fake, 16, None, 0, fake, 1 << 30,
+                   None) == L.SAG_E_INVALID
+        assert b"option" in lib.sag_last_error()
+    # build query: bad range, unknown flag, null size outputs, small workspace
+    st = lib.sag_csr_build_normalize_query(None, None, 0, 10, 5, 3, 0, ctypes.byref(nnz), ctypes.byref(nh),
+                                           None, 0, None)
+    assert st == L.SAG_E_INVALID
+    st = lib.sag_csr_build_normalize_query(None, None, 0, 10, 0, 10, 8, ctypes.byref(nnz), ctypes.byref(nh),
+                                           None, 0, None)
+    assert st == L.SAG_E_INVALID
+    assert lib.sag_csr_build_normalize_query(None, None, 0, 10, 0, 10, 0, None, None, None, 0,
+                                             None) == L.SAG_E_INVALID
+    st = lib.sag_csr_build_normalize_query(fake, fake, 4, 10, 0, 10, 2, ctypes.byref(nnz), ctypes.byref(nh),
+                                           fake, 16, None)
+    assert st == L.SAG_E_WORKSPACE and nnz.value == 0 and nh.value == 0
     # push / low-bit messages: bad bits, misaligned code rows, null outputs
     assert lib.sag_code_row_bytes(128, 3) == 0 and lib.sag_code_row_bytes(128, 1) == 16
     assert lib.sag_code_row_bytes(100, 8) == 112 and lib.sag_code_row_bytes(1, 2) == 16

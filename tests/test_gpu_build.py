@@ -103,6 +103,34 @@ def test_out_of_range_id_is_reported():
         sag.csr_build_normalize(to_dev(src), to_dev(dst), 5, 0, 5, True, True, "gcn")
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_query_sizes_match_the_build(seed):
+    """sag_csr_build_normalize_query returns the entry count and halo size
+    that the build then produces (and the oracle's), without outputs; an
+    exact-size build from those sizes matches the oracle bit for bit."""
+    g = np.random.default_rng(300 + seed)
+    n = int(g.integers(2, 4000))
+    src, dst = _edges(seed, n, int(g.integers(0, 5 * n)))
+    lo = int(g.integers(0, n))
+    hi = int(g.integers(lo, n + 1))
+    sym, loops = bool(seed % 2), bool((seed // 2) % 2)
+    say(f"build query seed={seed} n={n} lo={lo} hi={hi} sym={sym} loops={loops}")
+    nnz, n_halo = sag.csr_build_normalize_query(to_dev(src), to_dev(dst), n, lo, hi, sym, loops)
+    ob = ocsr.build(src, dst, n, lo, hi, sym, loops, "gcn")
+    assert (nnz, n_halo) == (ob.A.nnz, ob.n_halo)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, lo, hi, sym, loops, "gcn", max_halo=n_halo)
+    _cmp_built(gb, ob)
+
+
+def test_query_reports_out_of_range_ids():
+    src = np.array([0, 1, 9], np.int32)
+    dst = np.array([1, 2, 3], np.int32)
+    say("build query with an id out of range")
+    with pytest.raises(sag._lib.SagError) as ei:
+        sag.csr_build_normalize_query(to_dev(src), to_dev(dst), 5, 0, 5, True, True)
+    assert ei.value.status == sag._lib.SAG_E_RANGE
+
+
 def test_capacity_too_small_reports_sizes():
     src, dst = _edges(3, 200, 800)
     say("build with a small halo capacity")

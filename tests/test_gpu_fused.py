@@ -123,15 +123,25 @@ def test_unsupported_width_is_refused():
 @pytest.mark.parametrize("fusion", [True, False])
 def test_layers_with_and_without_fusion(fusion):
     """The GCN and SAGE layers (aggregate first, forward + backward) agree
-    with the oracle both through the fused kernel and through the separate
-    SpMM and product."""
+    with the oracle both through the fused kernel (SAG_LAYER_FUSED) and
+    through the separate SpMM and product."""
     from test_gpu_layers import run_case
-    old = sag.set_fusion(fusion)
-    try:
-        src, dst, n = _uniform(11)
-        for model, norm in (("gcn", "gcn"), ("sage", "mean")):
-            for dt in ("f32", "bf16"):
-                run_case(model, dt, src, dst, n, 300, 2700, True, True, norm, 64, 128, True, stale_rows=n,
-                         seed=5, label=f"fusion={fusion}")
-    finally:
-        sag.set_fusion(old)
+    src, dst, n = _uniform(11)
+    for model, norm in (("gcn", "gcn"), ("sage", "mean")):
+        for dt in ("f32", "bf16"):
+            run_case(model, dt, src, dst, n, 300, 2700, True, True, norm, 64, 128, True, stale_rows=n,
+                     seed=5, label=f"fusion={fusion}", fused=fusion)
+
+
+@pytest.mark.parametrize("fusion", [True, False])
+@pytest.mark.parametrize("norm", ["none", "gcn"])
+def test_sage_layer_on_a_csr_that_is_not_a_mean(fusion, norm):
+    """A GraphSAGE layer over a CSR built without the mean normalisation
+    (not tagged row_mean) aggregates with the stored values -- a sum for
+    SAG_NORM_NONE -- in the fused and the separate forward and in the
+    backward alike, as the oracle does with the same CSR."""
+    from test_gpu_layers import run_case
+    src, dst, n = _uniform(17)
+    for dt in ("f32", "bf16"):
+        run_case("sage", dt, src, dst, n, 200, 2500, True, True, norm, 48, 96, True, stale_rows=n, seed=9,
+                 label=f"sage over a {norm} CSR, fusion={fusion}", fused=fusion)

@@ -19,7 +19,7 @@ from oracle import csr as ocsr, layers as olay
 pytestmark = pytest.mark.gpu
 
 sag = pytest.importorskip("sparse_aggregation_gemm_amd")
-from gpu_util import DEV, f64, round_to, say, to_dev, to_dev_dense, tol  # noqa: E402
+from gpu_util import DEV, elementwise_rel, f64, round_to, say, to_dev, to_dev_dense, tol  # noqa: E402
 
 
 def _err(got, ref, den):
@@ -31,7 +31,7 @@ def _bits_or_f32(x, dt):
 
 
 def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_out, relu,
-             stale_rows=0, stale_base=0, seed=0, seg_len=256, label=""):
+             stale_rows=0, stale_base=0, seed=0, seg_len=256, label="", fused=False):
     g = np.random.default_rng(seed)
     n_l = hi - lo
     say(f"layer {label} model={model} dt={dt} n_global={n_global} [{lo},{hi}) {d_in}->{d_out}")
@@ -59,7 +59,7 @@ def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_ou
     Wd = to_dev_dense(W, dt).contiguous()
     bd = to_dev(b)
     fwd = sag.gcn_layer_forward if model == "gcn" else sag.sage_layer_forward
-    Out, Ypre, ctx = fwd(gb.A, H_ext, Wd, bd, relu=relu, want_pre=True)
+    Out, Ypre, ctx = fwd(gb.A, H_ext, Wd, bd, relu=relu, want_pre=True, fused=fused)
 
     # ---- oracle forward
     H64 = olay.as_f64(np.concatenate([H_loc, ocsr.gather(stale, ocsr.halo_rows(ob, stale_base))]), dt)
@@ -72,6 +72,7 @@ def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_ou
         _, Yd = olay.sage_forward_den(ob.A, H64, n_l, W64, b)
     e_out = _err(f64(Out), Outr, Yd)
     e_pre = _err(f64(Ypre), Yr, Yd)
+    say(f"  forward err {e_pre:.2e} of the bound; per element {elementwise_rel(f64(Ypre), Yr):.2e}")
     assert e_out <= tol(dt) and e_pre <= tol(dt), f"{label}: forward err out {e_out:.2e} pre {e_pre:.2e}"
 
     # ---- backward with the same mask input on both sides
