@@ -300,6 +300,24 @@ sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dty
                           const void* addend, int64_t ld_add, int64_t n_add,
                           void* ws, size_t ws_bytes, void* stream);
 
+/* SpMM for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same product as
+ * sag_spmm_csr, with the same arguments but no workspace.  The long rows'
+ * partial sums go into a fixed device array of sag_spmm_noalloc_scratch_bytes()
+ * bytes (64 MiB) that the library holds on each GPU it runs on until the
+ * process ends; the call allocates nothing, not even for tracing (it records
+ * no trace events).  A matrix whose partials need more
+ * (sag_spmm_workspace_bytes(A, d) above that size) returns SAG_E_WORKSPACE
+ * before any launch.  Every call on one GPU shares that GPU's array, so
+ * calls that overlap on one GPU (different streams, or threads) race; calls
+ * ordered on one stream do not.  Nothing in the array needs clearing: each
+ * call writes every partial it reads.  Results are bitwise those of
+ * sag_spmm_csr. */
+size_t sag_spmm_noalloc_scratch_bytes(void);
+sag_status sag_spmm_csr_noalloc(const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
+                                void* Y, int64_t ldy, sag_dtype yt,
+                                const void* addend, int64_t ld_add, int64_t n_add, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Layers.  In all four calls: dt is the storage type of activations,
  * activation gradients and W (F32 or BF16); accumulation is fp32; b, dW and

@@ -10,6 +10,6 @@ from .ops import (  # noqa: F401
     dequantize_rows, dtype_code, empty_dense, GatCtx, gat_layer_backward, gat_layer_forward,
     gcn_layer_backward, gcn_layer_forward, gemm, gemm_tn,
     halo_gather, halo_push, padded_ld, quantize_rows, sage_layer_backward, sage_layer_forward,
-    spmm_csr, spmm_csr_t, trace_enable, trace_records, version,
+    spmm_csr, spmm_csr_noalloc, spmm_csr_t, spmm_noalloc_scratch_bytes, trace_enable, trace_records, version,
 )
 from . import _lib  # noqa: F401

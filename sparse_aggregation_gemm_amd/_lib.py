@@ -54,6 +54,8 @@ SIGNATURES = {
     "sag_spmm_workspace_bytes": (sz, [PCSR, i64]),
     "sag_spmm_csr": (cint, [PCSR, vp, i64, cint, i64, vp, i64, cint, vp, i64, i64, vp, sz, vp]),
     "sag_spmm_csr_t": (cint, [PCSR, vp, i64, cint, i64, vp, i64, cint, vp, i64, i64, vp, sz, vp]),
+    "sag_spmm_noalloc_scratch_bytes": (sz, []),
+    "sag_spmm_csr_noalloc": (cint, [PCSR, vp, i64, cint, i64, vp, i64, cint, vp, i64, i64, vp]),
     "sag_gcn_save_bytes": (sz, [i64, i64, i64, cint]),
     "sag_gcn_forward_workspace_bytes": (sz, [PCSR, i64, i64, cint]),
     "sag_gcn_layer_forward": (cint, [PCSR, vp, i64, i64, vp, vp, i64, cint, u32, cint, vp, vp, i64,

@@ -18,6 +18,8 @@
 // handed to the group that needs them with lane shuffles, so each lane keeps
 // several independent 16-byte loads in flight.  Accumulation is fp32 in a
 // fixed order, so results are bitwise reproducible.
+#include <mutex>
+
 #include "ops.h"
 #include "rowsum.h"
 #include "trace.h"
@@ -413,6 +415,18 @@ size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
     return static_cast<size_t>(A.n_seg) * static_cast<size_t>(round_up(C * 4, 8)) * sizeof(float);
 }
 
+namespace {
+
+sag_status spmm_dispatch(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
+                         int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s) {
+    if (xt == SAG_F32 && yt == SAG_F32) return run_typed<float, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
+    if (xt == SAG_BF16 && yt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, epi, ws, s);
+    if (xt == SAG_BF16 && yt == SAG_F32) return run_typed<uint16_t, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
+    return fail(SAG_E_UNSUPPORTED, "spmm: unsupported (X, Y) dtype pair");
+}
+
+}  // namespace
+
 sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
                     int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, size_t ws_bytes,
                     hipStream_t s) {
@@ -427,10 +441,7 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
                                                   A.n_rows, A.nnz, d)
                                      : std::string(),
                      s, bytes, 2 * A.nnz * d);
-    if (xt == SAG_F32 && yt == SAG_F32) return run_typed<float, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
-    if (xt == SAG_BF16 && yt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, epi, ws, s);
-    if (xt == SAG_BF16 && yt == SAG_F32) return run_typed<uint16_t, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
-    return fail(SAG_E_UNSUPPORTED, "spmm: unsupported (X, Y) dtype pair");
+    return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
 }
 
 }  // namespace sag
@@ -442,9 +453,9 @@ extern "C" size_t sag_spmm_workspace_bytes(const sag_csr* A, int64_t d) {
     return spmm_ws_bytes(*A, d);
 }
 
-static sag_status spmm_entry(const char* name, const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt,
+static sag_status spmm_check(const char* name, const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt,
                              int64_t d, void* Y, int64_t ldy, sag_dtype yt, const void* addend,
-                             int64_t ld_add, int64_t n_add, void* ws, size_t ws_bytes, void* stream) {
+                             int64_t ld_add, int64_t n_add) {
     SAG_TRY(check_csr(name, A));
     if (d < 0) return fail(SAG_E_INVALID, std::string(name) + ": negative width");
     const int64_t maxd = xt == SAG_BF16 ? 2048 : 1024;
@@ -456,12 +467,24 @@ static sag_status spmm_entry(const char* name, const sag_csr* A, const void* X, 
     if (!(xt == SAG_F32 && yt == SAG_F32) && !(xt == SAG_BF16 && yt == SAG_BF16) &&
         !(xt == SAG_BF16 && yt == SAG_F32))
         return fail(SAG_E_UNSUPPORTED, std::string(name) + ": unsupported (X, Y) dtype pair");
+    return SAG_OK;
+}
+
+static Epilogue entry_epilogue(const sag_csr* A, const void* addend, int64_t ld_add, int64_t n_add) {
     Epilogue e;
     e.addend = addend;
     e.ld_add = ld_add;
     e.n_add = addend ? n_add : 0;
     e.row_mean = A->row_mean != 0;
-    return spmm_run(*A, X, ldx, xt, d, Y, ldy, yt, e, ws, ws_bytes, static_cast<hipStream_t>(stream));
+    return e;
+}
+
+static sag_status spmm_entry(const char* name, const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt,
+                             int64_t d, void* Y, int64_t ldy, sag_dtype yt, const void* addend,
+                             int64_t ld_add, int64_t n_add, void* ws, size_t ws_bytes, void* stream) {
+    SAG_TRY(spmm_check(name, A, X, ldx, xt, d, Y, ldy, yt, addend, ld_add, n_add));
+    return spmm_run(*A, X, ldx, xt, d, Y, ldy, yt, entry_epilogue(A, addend, ld_add, n_add), ws, ws_bytes,
+                    static_cast<hipStream_t>(stream));
 }
 
 extern "C" sag_status sag_spmm_csr(const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
@@ -474,4 +497,57 @@ extern "C" sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t l
                                      void* Y, int64_t ldy, sag_dtype yt, const void* addend, int64_t ld_add,
                                      int64_t n_add, void* ws, size_t ws_bytes, void* stream) {
     return spmm_entry("spmm_csr_t", AT, X, ldx, xt, d, Y, ldy, yt, addend, ld_add, n_add, ws, ws_bytes, stream);
+}
+
+// ---- allocation-free variant ------------------------------------------------------
+// The long-row partials of sag_spmm_csr_noalloc live in this file-scope
+// device array instead of a caller workspace.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not the device address: the address comes from
+// hipGetSymbolAddress, once per device, and only that pointer is handed to
+// kernels.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use on
+// that device).
+sag_status scratch_address(void** out) {
+    int dev = -1;
+    SAG_CHECK_HIP(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(SAG_E_UNSUPPORTED, "spmm_csr_noalloc: device ordinal too large");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        SAG_CHECK_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+        if (!p) return fail(SAG_E_HIP, "spmm_csr_noalloc: no device address for the scratch array");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SAG_OK;
+}
+
+}  // namespace
+
+extern "C" size_t sag_spmm_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" sag_status sag_spmm_csr_noalloc(const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
+                                           void* Y, int64_t ldy, sag_dtype yt, const void* addend,
+                                           int64_t ld_add, int64_t n_add, void* stream) {
+    SAG_TRY(spmm_check("spmm_csr_noalloc", A, X, ldx, xt, d, Y, ldy, yt, addend, ld_add, n_add));
+    const size_t need = spmm_ws_bytes(*A, d);
+    if (need > kScratchBytes)
+        return fail(SAG_E_WORKSPACE, "spmm_csr_noalloc: the long rows' partial sums need " + std::to_string(need) +
+                                         " bytes, above the fixed scratch of " + std::to_string(kScratchBytes) +
+                                         " bytes (use sag_spmm_csr with a workspace)");
+    if (A->n_rows == 0 || d == 0) return SAG_OK;
+    void* ws = nullptr;
+    if (need > 0) SAG_TRY(scratch_address(&ws));
+    return spmm_dispatch(*A, X, ldx, xt, d, Y, ldy, yt, entry_epilogue(A, addend, ld_add, n_add), ws,
+                         static_cast<hipStream_t>(stream));
 }

@@ -305,6 +305,22 @@ def spmm_csr_t(AT: Csr, X, out_dtype=None, Y=None, addend=None):
     return _spmm("sag_spmm_csr_t", AT, X, out_dtype, Y, addend)
 
 
+def spmm_csr_noalloc(A: Csr, X, Y, addend=None):
+    """sag_spmm_csr_noalloc: Y = A X (+ addend) into the caller's Y, with
+    the long rows' partials in the library's fixed device scratch (no
+    workspace; nothing allocated by the call)."""
+    n_add = addend.shape[0] if addend is not None else 0
+    st = L.lib().sag_spmm_csr_noalloc(A.ref, _ptr(X), _ld(X), dtype_code(X.dtype), X.shape[1], _ptr(Y), _ld(Y),
+                                      dtype_code(Y.dtype), _ptr(addend), _ld(addend) if addend is not None else 0,
+                                      n_add, _stream(X.device))
+    L.check("sag_spmm_csr_noalloc", st)
+    return Y
+
+
+def spmm_noalloc_scratch_bytes() -> int:
+    return int(L.lib().sag_spmm_noalloc_scratch_bytes())
+
+
 # ---- layers ------------------------------------------------------------------------
 
 @dataclass
