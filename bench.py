@@ -17,7 +17,11 @@ carries per-step p10 / median / p90 from HIP events around each timed step,
 the same for up to five cold steps (each after a 1 GiB write that evicts L2
 and the MALL), per-operation times with algorithmic GB/s, TFLOP/s and their
 fractions of the HBM, MFMA and attainable (min(MFMA peak, intensity x HBM
-peak)) ceilings, and row-length statistics of the graph.
+peak)) ceilings, row-length statistics of the graph, the step with the first
+layer's input gradient computed as well, and (``configs``) the step time and
+dominant operation of each other workload at full size.  Their graphs are
+drawn in background processes started before the GPU is touched, so the
+drawing overlaps the headline's timing.
 """
 from __future__ import annotations
 
@@ -28,7 +32,9 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
+import tempfile
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +70,11 @@ def parse():
     p.add_argument("--scale", type=float, default=1.0)
     p.add_argument("--seg-len", type=int, default=1024)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--configs", default="1,2,3,5",
+                   help="other workloads timed at full size after the headline (comma list; empty: none)")
+    p.add_argument("--config-steps", type=int, default=10)
+    p.add_argument("--draw-edges", nargs=2, metavar=("CONFIG", "PATH"),
+                   help="no GPU work: draw a workload's edge list and save it (used by the background jobs)")
     p.add_argument("--no-extras", action="store_true",
                    help="time the step only (skip the overlapped-pull, fused-kernel, GAT and halo-message "
                         "sections), e.g. for hardware-counter passes")
@@ -279,7 +290,7 @@ class Model:
         self.bwd = sag.gcn_layer_backward if w.model == "gcn" else sag.sage_layer_backward
         # preallocated outputs and workspaces
         self.out = [sag.empty_dense(self.n_l, w.dims[l + 1], self.tdt, dev) for l in range(w.n_layers)]
-        self.dH = [sag.empty_dense(self.n_ext if l == 0 else self.n_l, w.dims[l], self.tdt, dev)
+        self.dH = [sag.empty_dense(self.n_ext, w.dims[l], self.tdt, dev)
                    for l in range(w.n_layers)]
         L = sag._lib.lib()
         dt = sag.dtype_code(self.tdt)
@@ -291,7 +302,9 @@ class Model:
                  for l in range(w.n_layers))
         self.ws = torch.empty(max(fw, bw, 256), dtype=torch.uint8, device=dev)
 
-    def step(self):
+    def step(self, want_dH0=False):
+        """One forward + backward pass; the first layer's input gradient
+        (dH_ext of the features, not trained) only with want_dH0."""
         w, sag = self.w, self.sag
         if self.n_h:
             sag.halo_gather(self.stale, self.built.halo_gid, self.H0[self.n_l:], row_base=w.stale_base)
@@ -305,7 +318,7 @@ class Model:
             x = out
         g = self.G
         for l in reversed(range(w.n_layers)):
-            want_dH = l > 0
+            want_dH = l > 0 or want_dH0
             _, _, dH = self.bwd(ctxs[l], self.built.AT, self.n_l, self.out[l], g, want_dH=want_dH,
                                 dH=self.dH[l] if want_dH else None, ws=self.ws)
             g = dH[: self.n_l] if want_dH else None
@@ -332,10 +345,11 @@ def cold_steps(m, torch, n, flush_bytes=1 << 30):
     return out
 
 
-def _oracle_sample(w, R: int):
-    """Seconds the oracle takes for every layer's forward and backward on
-    the local rows [0, R) of the workload's graph treated as a partition
-    (its halo columns included), and the partition's column count."""
+def _oracle_sample(w, R: int, dtype, reps: int = 1):
+    """Seconds (each of `reps` runs) the oracle takes for every layer's
+    forward and backward on the local rows [0, R) of the workload's graph
+    treated as a partition (its halo columns included), computing in
+    `dtype`, and the partition's column count."""
     import numpy as np
 
     from oracle import csr as ocsr, layers as olay
@@ -351,30 +365,37 @@ def _oracle_sample(w, R: int):
         deg = (deg + (1 if w.self_loops else 0)).astype(np.int32)
     ob = ocsr.build(src, dst, w.n_global, w.lo, w.lo + R, w.symmetrize, w.self_loops, w.norm, deg_global=deg)
     n_ext = ob.A.n_cols
-    total = 0.0
-    for l in range(w.n_layers):
-        d_in, d_out = w.dims[l], w.dims[l + 1]
-        H = g.standard_normal((n_ext, d_in))
-        W = olay.as_f64(w.weights_stored(l), w.dtype)
-        b = w.biases[l]
-        G = g.standard_normal((R, d_out))
-        t0 = time.perf_counter()
-        if w.model == "gcn":
-            Z, Y, _ = olay.gcn_forward(ob.A, H, W, b, w.relu[l])
-            olay.gcn_backward(ob.AT, Z, W, Y, w.relu[l], G, want_dH=l > 0)
-        else:
-            M, Y, _ = olay.sage_forward(ob.A, H, R, W, b, w.relu[l])
-            olay.sage_backward(ob.AT, H[:R], M, W, Y, w.relu[l], G, want_dH=l > 0)
-        total += time.perf_counter() - t0
-        del H, G
-    return total, n_ext
+    times = []
+    for _ in range(reps):
+        total = 0.0
+        for l in range(w.n_layers):
+            d_in, d_out = w.dims[l], w.dims[l + 1]
+            H = g.standard_normal((n_ext, d_in)).astype(dtype)
+            W = olay.as_f64(w.weights_stored(l), w.dtype).astype(dtype)
+            b = w.biases[l]
+            G = g.standard_normal((R, d_out)).astype(dtype)
+            t0 = time.perf_counter()
+            if w.model == "gcn":
+                Z, Y, _ = olay.gcn_forward(ob.A, H, W, b, w.relu[l])
+                olay.gcn_backward(ob.AT, Z, W, Y, w.relu[l], G, want_dH=l > 0)
+            else:
+                M, Y, _ = olay.sage_forward(ob.A, H, R, W, b, w.relu[l])
+                olay.sage_backward(ob.AT, H[:R], M, W, Y, w.relu[l], G, want_dH=l > 0)
+            total += time.perf_counter() - t0
+            del H, G
+        times.append(total)
+    return times, n_ext
 
 
-def cpu_baseline(w, rows_hint: int, target_s: float = 15.0):
-    """The oracle (float64, as it stands) timed on a bounded sample of the
-    same workload: a row range sized from a short first run so that the
-    layers take about target_s seconds, scaled to the full graph by
-    n_local / R."""
+def cpu_baseline(w, rows_hint: int, target_s: float = 4.0):
+    """The oracle timed on a bounded sample of the same workload: a row range
+    sized from a short first run so that one fp32 pass of the layers takes
+    about target_s seconds, scaled to the full graph by n_local / R.  The
+    value is the median of three runs of the oracle's fp32 instantiation
+    (the same loops as the parity oracle); one float64 run (the parity
+    oracle itself) is reported beside it."""
+    import numpy as np
+
     from oracle import native
 
     n_l = w.hi - w.lo
@@ -382,15 +403,19 @@ def cpu_baseline(w, rows_hint: int, target_s: float = 15.0):
         R = min(n_l, rows_hint)
     else:
         R0 = min(n_l, 16384)
-        t0, _ = _oracle_sample(w, R0)
-        R = min(n_l, max(R0, int(R0 * target_s / max(t0, 1e-3))))
-    total, n_ext = _oracle_sample(w, R)
+        t0, _ = _oracle_sample(w, R0, np.float32)
+        R = min(n_l, max(R0, int(R0 * target_s / max(t0[0], 1e-3))))
+    f32, n_ext = _oracle_sample(w, R, np.float32, reps=3)
+    f64, _ = _oracle_sample(w, R, np.float64)
     scale = n_l / R
-    ms = total * scale * 1e3
+    med = sorted(f32)[1]
     return {
-        "value": round(ms, 1), "unit": "ms", "cores": native.num_threads(), "kind": "oracle",
+        "value": round(med * scale * 1e3, 1), "unit": "ms", "cores": native.num_threads(), "kind": "oracle",
         "sample": (f"local rows [0,{R}) of the {n_l}-row graph as a partition ({n_ext - R} halo columns), "
-                   f"{w.n_layers}-layer fwd+bwd in float64 took {total:.2f} s, scaled by {scale:.2f}"),
+                   f"{w.n_layers}-layer fwd+bwd in the oracle's fp32 instantiation: median of 3 runs "
+                   f"{med:.2f} s (runs {', '.join(f'{t:.2f}' for t in f32)} s), scaled by {scale:.2f}"),
+        "float64": {"value": round(f64[0] * scale * 1e3, 1), "unit": "ms",
+                    "sample": f"the parity oracle (float64) on the same rows, one run {f64[0]:.2f} s, scaled"},
         "host": host_info(),
     }
 
@@ -463,103 +488,53 @@ def halo_messages(sag, torch, np, n_store=4_000_000, n_halo=3_800_000, d=128, re
                                       "sample": f"{cpu_rows} rows x {d}, 1-bit, numpy, scaled to {n_halo} rows"}}
 
 
-class TwoLayerShare:
-    """DIGEST on one GPU's share of the 100M-node graph: a 2-layer GCN
-    (128 -> 128 -> 128, bf16, ReLU) whose layer inputs take their halo rows
-    from per-layer stale stores (pull), whose fresh local rows go back into
-    the layer-1 store (push), and whose halo input gradients are added into
-    a gradient store (accumulating push).  `step(overlap)` runs forward and
-    backward either on one stream or with the pulls and the push on a second
-    stream: the layer-1 pull runs beside layer 0's forward and the push
-    beside layer 1, with events ordering every buffer they share."""
+def overlapped_pull(sag, torch, np, w, steps=10):
+    """ms per step of DIGEST's exchange around a 2-layer GCN (128 -> 128 ->
+    128, bf16, ReLU) on the workload's partition (sparse_aggregation_gemm_amd
+    .digest.StaleExchange: per-layer stale stores over every node id, the
+    pulls of both layers' halo rows, the push of the fresh layer-1 input
+    rows and the accumulating return of layer-1 halo gradients), with the
+    exchanges on the compute stream and on a second stream (HIP events
+    around `steps` steps, after two warmup steps of each)."""
+    from sparse_aggregation_gemm_amd.digest import StaleExchange
 
-    def __init__(self, sag, torch, np, scale, seed=3):
-        import gen
-        self.sag, self.torch = sag, torch
-        dev = torch.device("cuda:0")
-        w = gen.make_config(5, scale)
-        src, dst = w.edges
-        gb = sag.csr_build_normalize(torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), w.n_global,
-                                     w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
-        sag.csr_schedule(gb.A, 1024)
-        sag.csr_schedule(gb.AT, 1024)
-        self.gb, self.w = gb, w
-        n_l, n_h = gb.n_local, gb.n_halo
-        self.n_l, self.n_h = n_l, n_h
-        d = 128
-        bf = torch.bfloat16
-        g = torch.Generator(device=dev)
-        g.manual_seed(seed)
+    dev = torch.device("cuda:0")
+    src, dst = w.edges
+    gb = sag.csr_build_normalize(torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), w.n_global,
+                                 w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
+    sag.csr_schedule(gb.A, 1024)
+    sag.csr_schedule(gb.AT, 1024)
+    d, bf = 128, torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
 
-        def dense(rows, fill_random=True):
-            t = sag.empty_dense(rows, d, bf, dev, fill=0.0)
-            if fill_random:
-                t.copy_(torch.randn(rows, d, device=dev, generator=g))
-            return t
-        # stale stores over all global ids of the share (local, then remote)
-        self.stores = [dense(w.n_global), dense(w.n_global)]
-        self.grad_store = dense(w.n_global, False)
-        self.H = [dense(n_l + n_h), dense(n_l + n_h, False)]
-        lim = (6.0 / (2 * d)) ** 0.5
-        self.W = [((torch.rand(d, d, device=dev, generator=g) * 2 - 1) * lim).to(bf).contiguous() for _ in range(2)]
-        self.b = [torch.rand(d, device=dev, generator=g) * 0.2 - 0.1 for _ in range(2)]
-        self.G = dense(n_l)
-        self.Out = dense(n_l, False)
-        self.local_ids = torch.arange(w.lo, w.hi, dtype=torch.int32, device=dev)
-        self.s1 = torch.cuda.Stream(device=dev)
-        self.e_end = torch.cuda.Event()
-        self.e_end.record()
-        self.grads = None
-
-    def step(self, overlap):
-        sag, torch = self.sag, self.torch
-        gb, n_l = self.gb, self.n_l
-        halo = gb.halo_gid
-        s0 = torch.cuda.current_stream()
-        s1 = self.s1 if overlap else s0
-        e0, e1, ef0, epush = (torch.cuda.Event() for _ in range(4))
-        with torch.cuda.stream(s1):
-            s1.wait_event(self.e_end)
-            sag.halo_gather(self.stores[0], halo, self.H[0][n_l:])
-            e0.record(s1)
-            sag.halo_gather(self.stores[1], halo, self.H[1][n_l:])
-            e1.record(s1)
-        s0.wait_event(e0)
-        _, _, ctx0 = sag.gcn_layer_forward(gb.A, self.H[0], self.W[0], self.b[0], relu=True, Out=self.H[1][:n_l])
-        ef0.record(s0)
-        with torch.cuda.stream(s1):
-            s1.wait_event(ef0)
-            sag.halo_push(self.H[1][:n_l], self.local_ids, self.stores[1])
-            epush.record(s1)
-        s0.wait_event(e1)
-        _, _, ctx1 = sag.gcn_layer_forward(gb.A, self.H[1], self.W[1], self.b[1], relu=True, Out=self.Out)
-        dW1, db1, dH1 = sag.gcn_layer_backward(ctx1, gb.AT, n_l, self.Out, self.G)
-        sag.halo_push(dH1[n_l:], halo, self.grad_store, accumulate=True)
-        dW0, db0, _ = sag.gcn_layer_backward(ctx0, gb.AT, n_l, self.H[1][:n_l], dH1[:n_l], want_dH=False)
-        s0.wait_event(epush)
-        self.e_end.record(s0)
-        self.grads = (dW0, db0, dW1, db1)
-
-
-def overlapped_pull(sag, torch, np, scale=0.25, steps=10):
-    """ms per step of TwoLayerShare with the pulls and the push on the
-    compute stream and on a second stream (HIP events around `steps` steps,
-    after two warmup steps of each)."""
-    net = TwoLayerShare(sag, torch, np, scale)
-    out = {"workload": f"2-layer GCN 128 -> 128 -> 128 bf16 on the 100M-graph share at scale {scale}",
-           "n_local": net.n_l, "n_halo": net.n_h, "nnz": net.gb.A.nnz}
+    def dense(rows, rand=True):
+        t = sag.empty_dense(rows, d, bf, dev, fill=0.0)
+        if rand:
+            t.copy_(torch.randn(rows, d, device=dev, generator=g))
+        return t
+    stores = [dense(w.n_global), dense(w.n_global)]
+    gstores = [None, dense(w.n_global, False)]
+    lim = (6.0 / (2 * d)) ** 0.5
+    W = [((torch.rand(d, d, device=dev, generator=g) * 2 - 1) * lim).to(bf).contiguous() for _ in range(2)]
+    b = [torch.rand(d, device=dev, generator=g) * 0.2 - 0.1 for _ in range(2)]
+    H0, G = dense(gb.n_local), dense(gb.n_local)
+    ex = StaleExchange(gb, "gcn", [d, d, d], [True, True], stores, gstores,
+                       torch.arange(w.lo, w.hi, dtype=torch.int32, device=dev))
+    out = {"workload": f"2-layer GCN 128 -> 128 -> 128 bf16 on: {w.name} (scale {w.scale})",
+           "n_local": gb.n_local, "n_halo": gb.n_halo, "nnz": gb.A.nnz}
     for overlap in (False, True, False, True):
         for _ in range(2):
-            net.step(overlap)
+            ex.step(H0, W, b, G, overlap=overlap)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(steps):
-            net.step(overlap)
-        b.record()
+            ex.step(H0, W, b, G, overlap=overlap)
+        e.record()
         torch.cuda.synchronize()
-        out["overlapped_ms" if overlap else "one_stream_ms"] = round(a.elapsed_time(b) / steps, 3)
-    del net
+        out["overlapped_ms" if overlap else "one_stream_ms"] = round(a.elapsed_time(e) / steps, 3)
+    del ex, stores, gstores, gb
     torch.cuda.empty_cache()
     return out
 
@@ -693,15 +668,168 @@ def gat_layer(m, sag, torch, np, heads=4, reps=5, cpu_rows=4096):
                                         f"fwd+bwd in float64 took {cpu_s:.2f} s, scaled by {scale:.1f}")}}
 
 
+def op_table(recs, steps):
+    """Per-op statistics (HIP-event time per launch and per step,
+    algorithmic GB/s and TFLOP/s with their fractions of the ceilings) of a
+    run's trace records, slowest first."""
+    ops = {}
+    for r in recs:
+        # (launches of one op name may differ in their bytes -- the SAGE forward
+        # SpMM reads no values, its transpose does -- so bytes and flops are
+        # averaged over the launches)
+        o = ops.setdefault(r["name"], {"n": 0, "ms": 0.0, "bsum": 0, "fsum": 0})
+        o["n"] += 1
+        o["ms"] += r["ms"]
+        o["bsum"] += r["bytes"]
+        o["fsum"] += r["flops"]
+    for o in ops.values():
+        o["bytes"] = o["bsum"] / o["n"]
+        o["flops"] = o["fsum"] / o["n"]
+    table = []
+    for name, o in ops.items():
+        avg = o["ms"] / o["n"]
+        t = {"op": name, "launches_per_step": o["n"] / steps, "avg_ms": round(avg, 4),
+             "ms_per_step": round(o["ms"] / steps, 4),
+             "GBps": round(o["bytes"] / avg / 1e6, 1) if avg > 0 else None,
+             "TFLOPs": round(o["flops"] / avg / 1e9, 2) if avg > 0 else None}
+        if avg > 0:
+            t["frac_hbm"] = round(t["GBps"] / HBM_PEAK_GBS, 4)
+            if name.startswith("gemm") and o["flops"] > 0 and o["bytes"] > 0:
+                peak = MFMA_PEAK_TFLOPS["bf16" if "[bf16" in name else "f32"]
+                # the attainable ceiling: min(MFMA peak, arithmetic intensity x HBM peak)
+                attain = min(peak, o["flops"] / o["bytes"] * HBM_PEAK_GBS / 1e3)
+                t["frac_mfma"] = round(t["TFLOPs"] / peak, 4)
+                t["frac_attainable"] = round(t["TFLOPs"] / attain, 4)
+        table.append(t)
+    table.sort(key=lambda t: -t["ms_per_step"])
+    return table, ops
+
+
+def roofline_of(table, ops, dtype):
+    """The roofline object of the slowest op: algorithmic bytes (or flops)
+    per launch over its event-timed average launch."""
+    dom = table[0]
+    dom_o = ops[dom["op"]]
+    avg_s = dom["avg_ms"] / 1e3
+    ai = dom_o["flops"] / max(dom_o["bytes"], 1)
+    dtn = "bf16" if dtype == "bf16" else "f32"
+    ridge = MFMA_PEAK_TFLOPS[dtn] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if dom["op"].startswith("gemm") and ai > ridge:
+        roof = {"bound": "mfma", "achieved": round(dom_o["flops"] / avg_s / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS[dtn], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(dom_o["bytes"] / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom["op"]
+    roof["alg_bytes_per_launch"] = int(round(dom_o["bytes"]))
+    roof["avg_launch_ms"] = dom["avg_ms"]
+    return roof
+
+
+def timed_steps(m, sag, torch, steps, want_dH0=False):
+    """(ms per step over `steps` back-to-back steps, per-step event times,
+    trace records of those steps)."""
+    sag.trace_enable(True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    marks[0].record()
+    for i in range(steps):
+        m.step(want_dH0)
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    sag.trace_enable(False)
+    recs = sag.trace_records(clear=True)
+    return elapsed * 1e3 / steps, [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)], recs
+
+
+def edge_file(cfg: int) -> str:
+    return os.path.join(tempfile.gettempdir(), f"sag_bench_edges_c{cfg}_{os.getpid()}.npz")
+
+
+def start_edge_draws(cfgs):
+    """Background processes that draw the workloads' edge lists (numpy only,
+    no GPU), started before this process touches the GPU."""
+    jobs = {}
+    for c in cfgs:
+        path = edge_file(c)
+        proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--draw-edges", str(c), path],
+                                stdout=subprocess.DEVNULL, stderr=subprocess.PIPE)
+        jobs[c] = (proc, path)
+    return jobs
+
+
+def draw_edges(cfg: str, path: str):
+    import numpy as np
+
+    import gen
+    w = gen.make_config(int(cfg), 1.0)
+    src, dst = w.edges
+    np.savez(path, src=src, dst=dst)
+
+
+def workload_with_edges(cfg, jobs, gen):
+    """Full-size workload `cfg` with the edge list its background job drew."""
+    import numpy as np
+    w = gen.make_config(cfg, 1.0)
+    proc, path = jobs[cfg]
+    rc = proc.wait()
+    if rc != 0:
+        raise RuntimeError(f"drawing config {cfg} failed: {proc.stderr.read().decode()[-400:]}")
+    z = np.load(path)
+    w.__dict__["edges"] = (z["src"], z["dst"])
+    os.remove(path)
+    return w
+
+
+def config_run(w, sag, torch, args):
+    """Step time and dominant operation of one other workload at full size."""
+    m = Model(w, sag, torch, args.seg_len)
+    for _ in range(3):
+        m.step()
+    torch.cuda.synchronize()
+    steps = args.config_steps if w.cfg != 1 else 50
+    ms, per, recs = timed_steps(m, sag, torch, steps)
+    table, ops = op_table(recs, steps)
+    out = {"workload": w.name, "config": w.cfg, "dtype": w.dtype, "dims": w.dims, "layer": w.model,
+           "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
+           "ms_per_step": round(ms, 4), "step_ms": pct(per), "steps": steps,
+           "roofline": roofline_of(table, ops, w.dtype), "ops": table[:6], "graph": m.graph_stats}
+    del m
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.summarize_counters:
         summarize_counters(args)
         return
+    if args.draw_edges:
+        draw_edges(*args.draw_edges)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the hot path here is one "
               "GPU's share of a graph, with no collectives.", file=sys.stderr)
         sys.exit(2)
+    cfgs = [int(c) for c in args.configs.split(",") if c.strip()] if args.configs else []
+    cfgs = [c for c in cfgs if c != args.config]
+    # (started before torch is imported: the children never see GPU state)
+    jobs = start_edge_draws([c for c in cfgs if c != 1] + ([5] if not args.no_extras and 5 not in cfgs else []))
+    try:
+        run(args, cfgs, jobs)
+    finally:
+        for proc, path in jobs.values():
+            if proc.poll() is None:
+                proc.kill()
+                proc.wait()
+            if os.path.exists(path):
+                os.remove(path)
+
+
+def run(args, cfgs, jobs):
     import numpy as np
     import torch
 
@@ -732,83 +860,35 @@ def main():
         m.step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    sag.trace_enable(True)
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    marks[0].record()
-    for i in range(args.steps):
-        m.step()
-        marks[i + 1].record()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    sag.trace_enable(False)
-    recs = sag.trace_records(clear=True)
-    ms_step = elapsed * 1e3 / args.steps
-    warm = [marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)]
+    ms_step, warm, recs = timed_steps(m, sag, torch, args.steps)
     cold = cold_steps(m, torch, min(args.steps, 5))
-
-    # per-op statistics from the HIP events of the timed steps
-    ops = {}
-    for r in recs:
-        # (launches of one op name may differ in their bytes -- the SAGE forward
-        # SpMM reads no values, its transpose does -- so bytes and flops are
-        # averaged over the launches)
-        o = ops.setdefault(r["name"], {"n": 0, "ms": 0.0, "bsum": 0, "fsum": 0})
-        o["n"] += 1
-        o["ms"] += r["ms"]
-        o["bsum"] += r["bytes"]
-        o["fsum"] += r["flops"]
-    for o in ops.values():
-        o["bytes"] = o["bsum"] / o["n"]
-        o["flops"] = o["fsum"] / o["n"]
-    table = []
-    for name, o in ops.items():
-        avg = o["ms"] / o["n"]
-        t = {"op": name, "launches_per_step": o["n"] / args.steps, "avg_ms": round(avg, 4),
-             "ms_per_step": round(o["ms"] / args.steps, 4),
-             "GBps": round(o["bytes"] / avg / 1e6, 1) if avg > 0 else None,
-             "TFLOPs": round(o["flops"] / avg / 1e9, 2) if avg > 0 else None}
-        if avg > 0:
-            t["frac_hbm"] = round(t["GBps"] / HBM_PEAK_GBS, 4)
-            if name.startswith("gemm") and o["flops"] > 0 and o["bytes"] > 0:
-                peak = MFMA_PEAK_TFLOPS["bf16" if "[bf16" in name else "f32"]
-                # the attainable ceiling: min(MFMA peak, arithmetic intensity x HBM peak)
-                attain = min(peak, o["flops"] / o["bytes"] * HBM_PEAK_GBS / 1e3)
-                t["frac_mfma"] = round(t["TFLOPs"] / peak, 4)
-                t["frac_attainable"] = round(t["TFLOPs"] / attain, 4)
-        table.append(t)
-    table.sort(key=lambda t: -t["ms_per_step"])
+    table, ops = op_table(recs, args.steps)
     spmm = [t for t in table if t["op"].startswith("spmm")]
-    dom = table[0]
-    dom_o = ops[dom["op"]]
-    avg_s = dom["avg_ms"] / 1e3
-    ai = dom_o["flops"] / max(dom_o["bytes"], 1)
-    dtn = "bf16" if w.dtype == "bf16" else "f32"
-    ridge = MFMA_PEAK_TFLOPS[dtn] * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if dom["op"].startswith("gemm") and ai > ridge:
-        roof = {"bound": "mfma", "achieved": round(dom_o["flops"] / avg_s / 1e12, 2),
-                "peak": MFMA_PEAK_TFLOPS[dtn], "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(dom_o["bytes"] / avg_s / 1e9, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    crec, tsrc = stored_counters(dom["op"])
+    roof = roofline_of(table, ops, w.dtype)
+    crec, tsrc = stored_counters(roof["kernel"])
+    avg_s = roof["avg_launch_ms"] / 1e3
     roof["traffic"] = crec["traffic_bytes_per_launch"] if crec else None
     roof["traffic_source"] = tsrc
-    # the rate of the bytes the counters saw (L2 <-> fabric, MALL hits
-    # included) against the same peak, beside the algorithmic fraction
-    roof["traffic_GBps"] = round(roof["traffic"] / avg_s / 1e9, 1) if crec and roof["unit"] == "GB/s" else None
-    roof["traffic_frac"] = round(roof["traffic_GBps"] / HBM_PEAK_GBS, 4) if roof["traffic_GBps"] else None
+    # the rate of the bytes the counters saw (L2 <-> fabric, hits in the
+    # memory-side cache (MALL) included, so an upper proxy for DRAM bytes)
+    # against the same peak, beside the algorithmic fraction
+    roof["traffic_GBps_mall_inclusive"] = (round(roof["traffic"] / avg_s / 1e9, 1)
+                                           if crec and roof["unit"] == "GB/s" else None)
+    roof["traffic_frac_mall_inclusive"] = (round(roof["traffic_GBps_mall_inclusive"] / HBM_PEAK_GBS, 4)
+                                           if roof["traffic_GBps_mall_inclusive"] else None)
     # L2-miss read requests of one launch (all whole 128-byte lines for the
     # gathers) and the rate this run achieved: random row gathers on this part
     # are capped by that rate, not by HBM bytes
     reqs = crec.get("read_requests_kernel") if crec else None
     roof["read_requests_per_launch"] = reqs
     roof["read_request_rate_G_per_s"] = round(reqs / avg_s / 1e9, 2) if reqs else None
-    roof["kernel"] = dom["op"]
-    roof["alg_bytes_per_launch"] = int(round(dom_o["bytes"]))
-    roof["avg_launch_ms"] = dom["avg_ms"]
+
+    # the same step with the first layer's input gradient as well
+    for _ in range(2):
+        m.step(True)
+    ms_dh0, per_dh0, _ = timed_steps(m, sag, torch, args.steps, want_dH0=True)
+    first_dH = {"without_ms": round(ms_step, 4), "with_ms": round(ms_dh0, 4), "with_step_ms": pct(per_dh0),
+                "note": "headline steps skip the first layer's input gradient (the features are not trained)"}
 
     A = m.built.A
     conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
@@ -817,9 +897,8 @@ def main():
             "graph": m.graph_stats}
     build_ms = m.build_ms
     overlap = fused = gat = halo = None
+    errors = {}
     if not args.no_extras:
-        log("[bench] DIGEST pull overlapped with compute (2-layer GCN on the 100M-graph share, scale 0.25)")
-        overlap = overlapped_pull(sag, torch, np)
         log("[bench] fused aggregate -> transform against the separate kernels")
         fused = fused_vs_separate(m, sag, torch)
         log("[bench] graph-attention layer on the same partition")
@@ -829,6 +908,24 @@ def main():
     if not args.no_extras:
         log("[bench] halo messages (pull, low-bit quantize/dequantize, push) at the 100M-graph share's shape")
         halo = halo_messages(sag, torch, np)
+    others = []
+    for c in cfgs:
+        try:
+            log(f"[bench] config {c} at full size")
+            wc = gen.make_config(1, 1.0) if c == 1 else workload_with_edges(c, jobs, gen)
+            others.append(config_run(wc, sag, torch, args))
+            if c == 5 and not args.no_extras:
+                log("[bench] DIGEST exchange overlapped with compute on the 100M-graph share")
+                overlap = overlapped_pull(sag, torch, np, wc)
+            del wc
+        except Exception as e:   # a failed extra section is reported, the headline stands
+            errors[f"config{c}"] = repr(e)[:400]
+    if not args.no_extras and overlap is None and 5 in jobs:
+        try:
+            log("[bench] DIGEST exchange overlapped with compute on the 100M-graph share")
+            overlap = overlapped_pull(sag, torch, np, workload_with_edges(5, jobs, gen))
+        except Exception as e:
+            errors["overlapped_pull"] = repr(e)[:400]
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] CPU baseline (oracle on a row sample)")
@@ -842,15 +939,19 @@ def main():
         "build_ms": round(build_ms, 1),
         "step_ms": pct(warm),
         "cold": {"step_ms": pct(cold), "steps": len(cold), "flush_bytes": 1 << 30} if cold else None,
+        "first_layer_dH": first_dH,
         "spmm": spmm,
         "ops": table,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "configs": others,
         "halo_messages": halo,
         "fused_aggregate_transform": fused,
         "overlapped_pull": overlap,
         "gat": gat,
     }
+    if errors:
+        out["errors"] = errors
     print(json.dumps(out), flush=True)
 
 

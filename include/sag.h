@@ -527,7 +527,9 @@ sag_status sag_gemm_tn(int64_t M, int64_t N, const void* A1, int64_t lda1, int64
  * packing of B, halo gather) records a pair of HIP events on its stream,
  * with its name and shape ("spmm[bf16,rows,nnz,d]", "gemm_nn[bf16,M,K,N]",
  * ...), its algorithmic bytes (each operand read once, each output written
- * once: for the SpMM 8 (rows + 1) + 8 nnz + elt d (cols + rows)) and flops.
+ * once: for the SpMM 8 (rows + 1) + 8 nnz (4 nnz when no values are read)
+ * + elt d (cols + rows), the epilogue's addend and Y_pre not counted) and
+ * flops.
  * sag_trace_get synchronises on the record's stop event and returns its
  * elapsed milliseconds; name receives at most name_cap bytes including the
  * terminating NUL.  sag_trace_clear destroys the calling thread's records. */

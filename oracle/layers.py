@@ -26,6 +26,9 @@ Readings
   nearest value with 8 significant bits, ties to even) where a bf16 path
   stores one between layers.  Subnormal bf16 values are not modelled.
 
+The layers compute in the floating type of their input H (float64 for every
+parity check; float32 only when the oracle is timed as a CPU baseline).
+
 ``*_den`` functions evaluate the same expressions on absolute values; the
 result bounds the magnitude of every term summed into an output and serves as
 the denominator of the relative error of a floating-point result.
@@ -58,16 +61,23 @@ def spmm(A: CSR, X: np.ndarray, abs_mode: bool = False, rows=None) -> np.ndarray
     return native.spmm(A.indptr, A.indices, A.values, X, abs_mode=abs_mode, rows=rows)
 
 
-def _bias(b, n):
-    return np.zeros(n) if b is None else np.asarray(b, np.float64)
+def _bias(b, n, dt=np.float64):
+    return np.zeros(n, dt) if b is None else np.asarray(b, dt)
+
+
+def _ft(x):
+    """The floating type the layer computes in: float32 for a float32 input,
+    else float64."""
+    return np.float32 if np.asarray(x).dtype == np.float32 else np.float64
 
 
 # ---- GCN -------------------------------------------------------------------
 
 def gcn_forward(A: CSR, H_ext, W, b, relu: bool):
     """Z = A H_ext; Y = Z W + b; Out = relu(Y) or Y."""
+    dt = _ft(H_ext)
     Z = spmm(A, H_ext)
-    Y = Z @ np.asarray(W, np.float64) + _bias(b, W.shape[1])
+    Y = Z @ np.asarray(W, dt) + _bias(b, W.shape[1], dt)
     Out = np.maximum(Y, 0.0) if relu else Y
     return Z, Y, Out
 
@@ -81,7 +91,7 @@ def gcn_forward_den(A: CSR, H_ext, W, b):
 def gcn_backward(AT: CSR, Z, W, Y, relu: bool, G, want_dH: bool = True):
     """G_Y = G * 1[Y>0]; dW = Z^T G_Y; db = colsum G_Y; dZ = G_Y W^T;
     dH_ext = A^T dZ (over the transposed CSR)."""
-    W = np.asarray(W, np.float64)
+    W = np.asarray(W, _ft(Z))
     GY = G * (Y > 0) if relu else G
     dW = Z.T @ GY
     db = GY.sum(axis=0)
@@ -104,9 +114,10 @@ def gcn_backward_den(AT: CSR, Z, W, Y, relu: bool, G, want_dH: bool = True):
 
 def sage_forward(Am: CSR, H_ext, n_local: int, W, b, relu: bool):
     """M = mean-CSR H_ext; X = [H_local | M]; Y = X W + b; Out = relu(Y)."""
+    dt = _ft(H_ext)
     M = spmm(Am, H_ext)
     X = np.concatenate([H_ext[:n_local], M], axis=1)
-    Y = X @ np.asarray(W, np.float64) + _bias(b, W.shape[1])
+    Y = X @ np.asarray(W, dt) + _bias(b, W.shape[1], dt)
     Out = np.maximum(Y, 0.0) if relu else Y
     return M, Y, Out
 
@@ -121,7 +132,7 @@ def sage_forward_den(Am: CSR, H_ext, n_local: int, W, b):
 def sage_backward(AmT: CSR, H_local, M, W, Y, relu: bool, G, want_dH: bool = True):
     """dW = [H|M]^T G_Y; db; [dH_self | dM] = G_Y W^T;
     dH_ext = mean-CSR^T dM, plus dH_self on the local rows."""
-    W = np.asarray(W, np.float64)
+    W = np.asarray(W, _ft(H_local))
     d = H_local.shape[1]
     GY = G * (Y > 0) if relu else G
     X = np.concatenate([H_local, M], axis=1)

@@ -38,6 +38,8 @@ def lib():
         L.orc_spmm_f64.restype = None
         L.orc_spmm_rows_f64.argtypes = [i64, vp, vp, vp, vp, vp, i64, i64, vp, i64, ctypes.c_int]
         L.orc_spmm_rows_f64.restype = None
+        L.orc_spmm_f32.argtypes = [i64, vp, vp, vp, vp, i64, i64, vp, i64, ctypes.c_int]
+        L.orc_spmm_f32.restype = None
         L.orc_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -51,10 +53,19 @@ def spmm(indptr, indices, values, X, abs_mode=False, rows=None):
     """fp64 CSR x dense: Y = A X (or only rows ``rows`` of it).
 
     indptr int64[n+1], indices int32[nnz], values float32[nnz] or None (all
-    ones), X float64 [n_cols, d].  Returns float64 [n or len(rows), d]."""
+    ones), X float64 [n_cols, d].  Returns float64 [n or len(rows), d].
+    A float32 X runs the same loops in fp32 (the timing instantiation; all
+    rows only) and returns float32."""
     indptr = np.ascontiguousarray(indptr, np.int64)
     indices = np.ascontiguousarray(indices, np.int32)
     values = None if values is None else np.ascontiguousarray(values, np.float32)
+    if np.asarray(X).dtype == np.float32 and rows is None:
+        X = np.ascontiguousarray(X, np.float32)
+        n, d = indptr.size - 1, X.shape[1]
+        Y = np.empty((n, d), np.float32)
+        lib().orc_spmm_f32(n, _p(indptr), _p(indices), _p(values), _p(X), d, d, _p(Y), d,
+                           int(bool(abs_mode)))
+        return Y
     X = np.ascontiguousarray(X, np.float64)
     n = indptr.size - 1
     d = X.shape[1]

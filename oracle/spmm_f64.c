@@ -1,4 +1,6 @@
-/* CPU oracle (test infrastructure only): CSR sparse x dense product in fp64.
+/* CPU oracle (test infrastructure only): CSR sparse x dense product in fp64
+ * (and the same loops in fp32, used only to time the oracle as a CPU
+ * baseline; parity always uses fp64).
  *
  * Y[r, :] = sum over entries p of row r, in ascending p, of val[p] * X[col[p], :]
  *
@@ -69,4 +71,27 @@ int orc_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* The fp32 instantiation of orc_spmm_f64: the same loops with float
+ * accumulators (timing only). */
+void orc_spmm_f32(int64_t n_rows, const int64_t* indptr, const int32_t* indices,
+                  const float* val, const float* X, int64_t ldx, int64_t d,
+                  float* Y, int64_t ldy, int abs_mode)
+{
+    #pragma omp parallel for schedule(dynamic, 256)
+    for (int64_t r = 0; r < n_rows; ++r) {
+        float* y = Y + r * ldy;
+        for (int64_t j = 0; j < d; ++j) y[j] = 0.0f;
+        for (int64_t p = indptr[r]; p < indptr[r + 1]; ++p) {
+            float a = val ? val[p] : 1.0f;
+            const float* x = X + (int64_t)indices[p] * ldx;
+            if (abs_mode) {
+                a = fabsf(a);
+                for (int64_t j = 0; j < d; ++j) y[j] += a * fabsf(x[j]);
+            } else {
+                for (int64_t j = 0; j < d; ++j) y[j] += a * x[j];
+            }
+        }
+    }
 }

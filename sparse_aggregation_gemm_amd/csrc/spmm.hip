@@ -433,10 +433,12 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
     if (A.n_rows == 0 || d == 0) return SAG_OK;
     if (ws_bytes < spmm_ws_bytes(A, d) || (spmm_ws_bytes(A, d) > 0 && !ws))
         return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
-    // algorithmic bytes: CSR arrays once, every X row once, every output once
+    // algorithmic bytes of the product itself: CSR arrays once (values only
+    // when read), every X row once, every output row once; the epilogue's
+    // addend and Y_pre are not counted
     const int64_t ex = elt_size(xt), ey = elt_size(yt);
     const int64_t bytes = 8 * (A.n_rows + 1) + A.nnz * (A.values && !epi.row_mean ? 8 : 4) + ex * d * A.n_cols +
-                          ey * d * A.n_rows * (epi.pre ? 2 : 1) + (epi.addend ? ey * d * epi.n_add : 0);
+                          ey * d * A.n_rows;
     TraceScope trace(trace_enabled() ? shape_name("spmm", xt == SAG_BF16 ? (yt == SAG_BF16 ? "bf16" : "bf16>f32") : "f32",
                                                   A.n_rows, A.nnz, d)
                                      : std::string(),

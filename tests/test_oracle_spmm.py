@@ -95,3 +95,27 @@ def test_rows_subset_matches_full():
     X = g.standard_normal((300, 7))
     rows = np.array([5, 0, 299, 17])
     assert np.array_equal(layers.spmm(b.A, X, rows=rows), layers.spmm(b.A, X)[rows])
+
+
+def test_fp32_instantiation_follows_the_fp64_loops():
+    """The timing instantiation (float32 X) runs the same loops in fp32: it
+    agrees with the fp64 product to fp32 rounding (at most len(row) ulps of
+    the absolute-value sum), and exactly on small integers."""
+    import numpy as np
+    from oracle import csr, native
+    g = np.random.default_rng(4)
+    n = 700
+    src, dst = g.integers(0, n, 9000), g.integers(0, n, 9000)
+    b = csr.build(src, dst, n, 0, n, True, True, "gcn")
+    X = g.standard_normal((n, 24))
+    y64 = native.spmm(b.A.indptr, b.A.indices, b.A.values, X.astype(np.float32).astype(np.float64))
+    y32 = native.spmm(b.A.indptr, b.A.indices, b.A.values, X.astype(np.float32))
+    den = native.spmm(b.A.indptr, b.A.indices, b.A.values, np.abs(X.astype(np.float32).astype(np.float64)),
+                      abs_mode=True)
+    lens = np.diff(b.A.indptr)[:, None]
+    assert y32.dtype == np.float32
+    assert np.all(np.abs(y32 - y64) <= (lens + 1) * 2.0 ** -24 * den + 1e-30)
+    Xi = g.integers(-8, 9, (n, 24)).astype(np.float32)
+    ones = np.ones(b.A.nnz, np.float32)
+    assert np.array_equal(native.spmm(b.A.indptr, b.A.indices, ones, Xi),
+                          native.spmm(b.A.indptr, b.A.indices, ones, Xi.astype(np.float64)))
