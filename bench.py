@@ -797,6 +797,10 @@ def config_run(w, sag, torch, args):
            "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
            "ms_per_step": round(ms, 4), "step_ms": pct(per), "steps": steps,
            "roofline": roofline_of(table, ops, w.dtype), "ops": table[:6], "graph": m.graph_stats}
+    if any(w.dims[l] <= w.dims[l + 1] for l in range(w.n_layers)) and w.cfg != 1:
+        # layers that aggregate first: the fused aggregate -> transform kernel
+        # against the separate SpMM and product
+        out["fused_aggregate_transform"] = fused_vs_separate(m, sag, torch)
     del m
     torch.cuda.empty_cache()
     return out
