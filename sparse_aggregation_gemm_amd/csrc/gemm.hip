@@ -1282,6 +1282,20 @@ sag_status tn_typed(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t
     float* pcs = c.take<float>(p.n_chunks * p.ldp_n);
     if (!c.fits()) return fail(SAG_E_WORKSPACE, "gemm_tn: workspace too small");
     float* cs = colsum ? pcs : nullptr;
+    const int64_t total = (k1 + k2) * N;
+    const int64_t work = total > N ? total : N;
+    if (M == 0) {
+        // a sum over no rows: the reduce over zero chunks writes the zeros
+        // into all K1 + K2 rows the caller named (an operand with no rows may
+        // come without a pointer), and the product kernel, whose row clamps
+        // assume at least one row, does not run
+        const int64_t zk1 = C ? A.k1 : 0, zk2 = C ? A.k2 : 0;
+        const int64_t zwork = (zk1 + zk2) * N > N ? (zk1 + zk2) * N : N;
+        tn_reduce<<<dim3(static_cast<unsigned>(cdiv(zwork, 256))), 256, 0, s>>>(
+            part, 0, p.ldp_k, p.ldp_n, zk1, zk1, zk2, N, C, ldc, pcs, colsum);
+        SAG_LAUNCH_CHECK();
+        return SAG_OK;
+    }
     if (p.kt == 512) {
         // (bf16 only: the plan keeps fp32 tiles at 256)
         if constexpr (sizeof(T) == 2) {
@@ -1292,8 +1306,6 @@ sag_status tn_typed(int64_t M, int64_t N, const GemmA& A, const void* B, int64_t
     else if (p.kt == 256) launch_tn<T, 256, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
     else launch_tn<T, 128, 128>(p, ao, B, ldb, mask, ldmask, N, part, cs, s);
     SAG_LAUNCH_CHECK();
-    const int64_t total = (k1 + k2) * N;
-    const int64_t work = total > N ? total : N;
     tn_reduce<<<dim3(static_cast<unsigned>(cdiv(work, 256))), 256, 0, s>>>(
         part, p.n_chunks, p.ldp_k, p.ldp_n, k1, kp(k1, dt), k2, N, C, ldc, pcs, colsum);
     SAG_LAUNCH_CHECK();

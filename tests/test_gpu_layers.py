@@ -191,3 +191,46 @@ def test_partition_consistency_with_fresh_halo():
         parts.append(f64(out))
     got = np.concatenate(parts)
     assert np.max(np.abs(got - ref)) <= 1e-5 * max(1.0, np.max(np.abs(ref)))
+
+
+@pytest.mark.parametrize("model", ["gcn", "sage"])
+@pytest.mark.parametrize("d_in,d_out", [(24, 40), (40, 24)])
+def test_empty_partition(model, d_in, d_out):
+    """A partition with no local rows (lo == hi): nothing to aggregate, the
+    outputs have no rows, and the weight and bias gradients -- sums over no
+    rows -- are exactly zero (not whatever their buffers held)."""
+    g = np.random.default_rng(5)
+    n = 300
+    src = g.integers(0, n, 900).astype(np.int32)
+    dst = g.integers(0, n, 900).astype(np.int32)
+    say(f"empty partition {model} {d_in}->{d_out}")
+    norm = "gcn" if model == "gcn" else "mean"
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 120, 120, True, True, norm)
+    assert gb.n_local == 0 and gb.n_halo == 0
+    H = sag.empty_dense(0, d_in, torch.float32, DEV)
+    w_rows = 2 * d_in if model == "sage" else d_in
+    W = torch.randn(w_rows, d_out, device=DEV)
+    b = torch.randn(d_out, device=DEV)
+    fwd = sag.gcn_layer_forward if model == "gcn" else sag.sage_layer_forward
+    bwd = sag.gcn_layer_backward if model == "gcn" else sag.sage_layer_backward
+    Out, _, ctx = fwd(gb.A, H, W, b, relu=True)
+    assert Out.shape[0] == 0
+    G = sag.empty_dense(0, d_out, torch.float32, DEV)
+    dW, db, dH = bwd(ctx, gb.AT, 0, Out, G)
+    torch.cuda.synchronize()
+    assert dW.shape == (w_rows, d_out) and torch.count_nonzero(dW).item() == 0
+    assert torch.count_nonzero(db).item() == 0
+    assert dH.shape[0] == 0
+
+
+@pytest.mark.parametrize("model", ["gcn", "sage"])
+def test_rows_without_entries(model):
+    """Local rows that aggregate nothing (no edges into the range, no self
+    connections): the aggregate is zero, so Out = act(b) (GraphSAGE: act of
+    the self term plus b) and the gradients follow, against the oracle."""
+    g = np.random.default_rng(6)
+    n = 1000
+    src = g.integers(0, 500, 3000).astype(np.int32)
+    dst = g.integers(0, 500, 3000).astype(np.int32)      # rows 600..899 receive nothing
+    run_case(model, "f32", src, dst, n, 600, 900, False, False, "gcn" if model == "gcn" else "mean", 16, 32,
+             True, seed=7, label="rows without entries")

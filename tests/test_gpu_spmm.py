@@ -206,3 +206,17 @@ def test_spmm_empty():
     say("spmm empty rows")
     Y = sag.spmm_csr(gb.A, X)
     assert np.all(f64(Y) == 0.0)
+
+
+@pytest.mark.parametrize("dt,d", [("f32", 1024), ("bf16", 2048), ("bf16", 1030)])
+@pytest.mark.parametrize("sched", [None, 64])
+def test_spmm_widest_rows(dt, d, sched):
+    """The widest rows the SpMM takes (256 vectors of 16 bytes: four per
+    lane), with short, medium and segmented long rows, and a ragged width."""
+    w, src, dst = _graph(2, 0.002)
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, 0, w.n_global, True, True, "gcn")
+    if sched:
+        sag.csr_schedule(gb.A, sched)
+    ob = ocsr.build(src, dst, w.n_global, 0, w.n_global, True, True, "gcn")
+    X = gen.normal_f32((ob.A.n_cols, d), np.random.default_rng(d))
+    _check_spmm(gb.A, ob.A, X, dt, dt, "widest rows", sched)
