@@ -170,3 +170,25 @@ def test_share_of_large_graph_bf16():
     src, dst = w.edges
     run_gat("bf16", src, dst, w.n_global, w.lo, w.hi, False, True, 128, 4, 32, True,
             stale_rows=w.stale_rows, stale_base=w.stale_base, label="share with halo")
+
+
+def test_empty_partition():
+    """No local rows: every gradient is a sum over nothing, exactly zero."""
+    g = np.random.default_rng(8)
+    n, d_in, heads, dh = 300, 16, 2, 8
+    src = g.integers(0, n, 900).astype(np.int32)
+    dst = g.integers(0, n, 900).astype(np.int32)
+    say("gat empty partition")
+    gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 50, 50, True, True, "none")
+    assert gb.n_local == 0 and gb.n_halo == 0
+    H = sag.empty_dense(0, d_in, torch.float32, DEV)
+    W = torch.randn(d_in, heads * dh, device=DEV)
+    a = torch.randn(heads, dh, device=DEV)
+    Out, ctx = sag.gat_layer_forward(gb.A, H, W, a, a, torch.randn(heads * dh, device=DEV), heads=heads)
+    assert Out.shape[0] == 0
+    G = sag.empty_dense(0, heads * dh, torch.float32, DEV)
+    dW, da_src, da_dst, db, dH = sag.gat_layer_backward(ctx, gb.A, gb.AT, Out, G)
+    torch.cuda.synchronize()
+    for t in (dW, da_src, da_dst, db):
+        assert torch.count_nonzero(t).item() == 0
+    assert dH.shape[0] == 0
