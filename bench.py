@@ -73,6 +73,9 @@ def parse():
     p.add_argument("--configs", default="1,2,3,5",
                    help="other workloads timed at full size after the headline (comma list; empty: none)")
     p.add_argument("--config-steps", type=int, default=10)
+    p.add_argument("--no-background", action="store_true",
+                   help="draw the other workloads' graphs in this process (also chosen under a profiler, whose "
+                        "preloaded library may initialise the GPU before a child could be started)")
     p.add_argument("--draw-edges", nargs=2, metavar=("CONFIG", "PATH"),
                    help="no GPU work: draw a workload's edge list and save it (used by the background jobs)")
     p.add_argument("--no-extras", action="store_true",
@@ -148,7 +151,7 @@ def summarize_counters(args):
            "kernel_fetch_kib": sum(kf) / len(kf), "kernel_write_kib": sum(kw) / len(kw),
            "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
            "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b))}
-    cmd = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-calib")
+    cmd = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras --configs '' --copy-calib")
     sizes = ""
     if args.sizes_dir:
         names = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
@@ -749,6 +752,11 @@ def edge_file(cfg: int) -> str:
     return os.path.join(tempfile.gettempdir(), f"sag_bench_edges_c{cfg}_{os.getpid()}.npz")
 
 
+def under_profiler() -> bool:
+    """Whether a profiler's library is preloaded into this process."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def start_edge_draws(cfgs):
     """Background processes that draw the workloads' edge lists (numpy only,
     no GPU), started before this process touches the GPU."""
@@ -771,9 +779,13 @@ def draw_edges(cfg: str, path: str):
 
 
 def workload_with_edges(cfg, jobs, gen):
-    """Full-size workload `cfg` with the edge list its background job drew."""
+    """Full-size workload `cfg` with the edge list its background job drew
+    (drawn here when there is no job)."""
     import numpy as np
     w = gen.make_config(cfg, 1.0)
+    if cfg not in jobs:
+        _ = w.edges
+        return w
     proc, path = jobs[cfg]
     rc = proc.wait()
     if rc != 0:
@@ -821,7 +833,8 @@ def main():
     cfgs = [int(c) for c in args.configs.split(",") if c.strip()] if args.configs else []
     cfgs = [c for c in cfgs if c != args.config]
     # (started before torch is imported: the children never see GPU state)
-    jobs = start_edge_draws([c for c in cfgs if c != 1] + ([5] if not args.no_extras and 5 not in cfgs else []))
+    wanted = [c for c in cfgs if c != 1] + ([5] if not args.no_extras and 5 not in cfgs else [])
+    jobs = {} if args.no_background or under_profiler() else start_edge_draws(wanted)
     try:
         run(args, cfgs, jobs)
     finally:
@@ -924,7 +937,7 @@ def run(args, cfgs, jobs):
             del wc
         except Exception as e:   # a failed extra section is reported, the headline stands
             errors[f"config{c}"] = repr(e)[:400]
-    if not args.no_extras and overlap is None and 5 in jobs:
+    if not args.no_extras and overlap is None:
         try:
             log("[bench] DIGEST exchange overlapped with compute on the 100M-graph share")
             overlap = overlapped_pull(sag, torch, np, workload_with_edges(5, jobs, gen))
