@@ -115,20 +115,27 @@ struct AOperand {
     int64_t M;
     const T* safe;   // any valid 16-byte aligned address
 
+    // (a column in a block's padding is clamped to the block's last vector:
+    // the row pitch covers that vector, so even the last row stays inside
+    // the operand; fix() zeroes the values)
+    static __device__ __forceinline__ int64_t last_vec(int64_t k) { return (k + Vec<T>::N - 1) / Vec<T>::N * Vec<T>::N - Vec<T>::N; }
     __device__ __forceinline__ const uint4* addr(int64_t r, int64_t k0) const {
         const T* p = safe;
         if (r < M) {
             if (k0 < k1p) {
-                if (r < m1) p = a1 + r * lda1 + k0;
+                const int64_t last = last_vec(k1);
+                if (r < m1) p = a1 + r * lda1 + (k0 < last ? k0 : last);
             } else if (k0 < k1p + k2p) {
-                p = a2 + r * lda2 + (k0 - k1p);
+                const int64_t kk = k0 - k1p, last = last_vec(k2);
+                p = a2 + r * lda2 + (kk < last ? kk : last);
             }
         }
         return reinterpret_cast<const uint4*>(p);
     }
     __device__ __forceinline__ const uint4* mask_addr(int64_t r, int64_t k0) const {
         const T* p = safe;
-        if (mask && r < M && r < m1 && k0 < k1p) p = mask + r * ldmask + k0;
+        const int64_t last = last_vec(k1);
+        if (mask && r < M && r < m1 && k0 < k1p) p = mask + r * ldmask + (k0 < last ? k0 : last);
         return reinterpret_cast<const uint4*>(p);
     }
     __device__ __forceinline__ uint4 fix(uint4 v, int64_t r, int64_t k0) const {
@@ -777,6 +784,350 @@ sag_status try_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt
     return SAG_E_UNSUPPORTED;
 }
 
+// ---- NN with A streamed through an LDS ring (bf16, no mask, no addend) -------------
+// The weights stay in registers as in gemm_nn_rw (wavefront w owns the
+// 32-column block w over all of K), but the 32-row tiles of A go from HBM
+// straight into LDS with direct loads (global_load_lds_dwordx4: lane i of a
+// wavefront writes bytes [16 i, 16 i + 16) of a 1 KB block at the address
+// in M0), so registers no longer bound the prefetch depth: S slots, S - 1
+// tiles in flight behind the one being multiplied.  In a slot, unit c (16
+// bytes) of row r sits at position c ^ (r & 15), so the 32 rows that a
+// wavefront reads at once spread over all banks.  Units past a block's
+// columns, and rows past the operand, are loaded from a zero vector; the
+// one unit of a block that is partly inside it is masked in LDS by the lane
+// that loaded it, once per tile, so the MFMA loop has no branches and its
+// LDS reads run a batch ahead of the products.
+//
+// Synchronisation: each wavefront waits for its own direct loads of the
+// next tile with an explicit count, then the workgroup meets at a bare
+// barrier (a fence would wait for every load in flight, draining the ring).
+// The count is exact because every wavefront with a block issues at least
+// kRgStores stores per tile (stores that fall outside C go to a sink) and
+// nothing else touches vector memory in the loop; the empty asm statements
+// keep the compiler from moving memory operations across these points.
+constexpr int kRgWaves = 8;
+constexpr int kRgRows = 32;
+constexpr int kRgStores = 2;                     // C stores per tile and lane (two 16-row halves)
+
+__device__ __attribute__((aligned(16))) uint4 g_ring_zero;                 // never written
+__device__ __attribute__((aligned(16))) uint4 g_ring_sink[kRgWaves * 64];  // never read
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// One direct load: 16 bytes per lane from g into LDS at lds + 16 * lane.  In
+// asm rather than through the builtin: the compiler would otherwise make
+// every later LDS read wait for the newest direct load (it cannot tell the
+// ring slots apart), which would drain the ring at each step.  No register
+// is written; M0 (the LDS address; nothing else in these kernels uses it) is
+// declared clobbered, and a wait state separates its write from the load
+// that reads it.
+__device__ __forceinline__ void lds_direct_load16(const void* g, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+                 : "memory", "m0");
+}
+
+// s_waitcnt with vmcnt = N and lgkmcnt = 0 (expcnt not waited for); the
+// immediate holds vmcnt in bits 3:0 and 15:14, expcnt in 6:4, lgkmcnt in 11:8
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt out of range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4)); }
+__device__ __forceinline__ void mem_order() { asm volatile("" ::: "memory"); }
+
+template <int KS, int S, bool PP, int WPE>
+__global__ __launch_bounds__(kRgWaves * 64, WPE) void gemm_nn_ring(AOperand<uint16_t> A,
+                                                                  const uint16_t* __restrict__ Bp, int64_t Kt,
+                                                                  int64_t N, int NB, int64_t n_tiles,
+                                                                  EpiT<uint16_t> e, const float* __restrict__ bias,
+                                                                  int fixup) {
+    using T = uint16_t;
+    constexpr int U = KS * 2;                     // 16-byte units of a tile row
+    constexpr int ROWB = U * 16;
+    constexpr int SLOT = kRgRows * ROWB;          // = 1024 KS
+    constexpr int IPW = SLOT / 1024 / kRgWaves;   // direct-load instructions per wavefront and tile
+    constexpr int D = S - 1;                      // tiles in flight ahead
+    constexpr int BT = KS >= 32 ? 4 : 8;          // LDS reads issued a batch ahead of the MFMAs
+    static_assert(U >= 16 && IPW >= 1 && IPW * 1024 * kRgWaves == SLOT, "tile shape");
+    static_assert(S >= 2 && (S & (S - 1)) == 0 && KS % BT == 0, "ring size");
+    __shared__ __attribute__((aligned(16))) unsigned char ring[S * SLOT];
+    __shared__ __attribute__((aligned(16))) unsigned char stage_all[kRgWaves * kRwStage];
+    __shared__ float bias_s[kRgWaves * 32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+    const int64_t G = gridDim.x;
+    const int64_t t0 = blockIdx.x;
+    if (t0 >= n_tiles) return;
+    const bool has = wave < NB;                   // wavefront-uniform
+    // with PP, of wavefronts w and w + 4 (which share a SIMD) the second
+    // finishes tile k - 1 before multiplying tile k, so that its epilogue
+    // runs while the first one's MFMAs do, and the other way round (its
+    // accumulators then live across the barrier: too many registers at K = 512)
+    const bool late = PP && wave >= kRgWaves / 2;
+    unsigned char* stage = stage_all + wave * kRwStage;
+
+    for (int n = tid; n < kRgWaves * 32; n += kRgWaves * 64) bias_s[n] = bias && n < N ? bias[n] : 0.f;
+    uint4 w[KS];
+    {
+        const T* col = Bp + static_cast<int64_t>(wave * 32 + l32) * Kt + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            w[ks] = has ? *reinterpret_cast<const uint4*>(col + ks * 16) : make_uint4(0, 0, 0, 0);
+    }
+    // the weights and the bias are in before any direct load is counted
+    wait_vm_lgkm0<0>();
+    __syncthreads();
+
+    // sources of this thread's direct loads: instruction m writes bytes
+    // [1024 j, 1024 j + 1024) of a slot, j = wave * IPW + m.  Per m, two
+    // registers: the column in its operand (-1: a unit that reads as zero)
+    // and a packed word: the row in the tile (bits 0-4), the operand (bit 5:
+    // A2) and the elements inside the operand of a partly covered unit
+    // (bits 8-11; 8 when the unit is whole)
+    int scol[IPW], sinf[IPW];
+#pragma unroll
+    for (int m = 0; m < IPW; ++m) {
+        const int q = (wave * IPW + m) * 64 + lane;
+        const int r = q / U, p = q % U;
+        const int64_t k0 = static_cast<int64_t>(p ^ (r & 15)) * 8;
+        int col = -1, second = 0, n = 8;
+        if (A.a1 && k0 < A.k1p) {
+            if (k0 < A.k1) {
+                col = static_cast<int>(k0);
+                if (A.k1 - k0 < 8) n = static_cast<int>(A.k1 - k0);
+            }
+        } else if (A.a2 && k0 < A.k1p + A.k2p) {
+            if (k0 - A.k1p < A.k2) {
+                col = static_cast<int>(k0 - A.k1p);
+                second = 1;
+                if (A.k2 - (k0 - A.k1p) < 8) n = static_cast<int>(A.k2 - (k0 - A.k1p));
+            }
+        }
+        scol[m] = col;
+        sinf[m] = r | (second << 5) | (n << 8);
+    }
+    const int wbase = wave * IPW * 1024;
+    const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr_t)ring));
+    auto slot_of = [](int64_t k) { return static_cast<int>(k & (S - 1)) * SLOT; };
+    auto dma = [&](int64_t k, int64_t tile) __attribute__((always_inline)) {
+        const uint32_t dst = ring_lds + static_cast<uint32_t>(slot_of(k) + wbase);
+#pragma unroll
+        for (int m = 0; m < IPW; ++m) {
+            const int64_t row = tile * kRgRows + (sinf[m] & 31);
+            const bool second = sinf[m] & 32;
+            const T* base = second ? A.a2 : A.a1;
+            const int64_t ld = second ? A.lda2 : A.lda1;
+            const int64_t lim = second ? A.M : A.m1;
+            const void* g = scol[m] >= 0 && row < lim ? static_cast<const void*>(base + row * ld + scol[m])
+                                                      : static_cast<const void*>(&g_ring_zero);
+            lds_direct_load16(g, dst + m * 1024);
+        }
+    };
+    auto sink_stores = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kRgStores; ++i) g_ring_sink[wave * 64 + lane] = make_uint4(0, 0, 0, 0);
+    };
+    // wait for this thread's loads of tile k + 1 (the count is explained
+    // below), zero the part past the operand of the partly covered units
+    // among them, and meet the workgroup
+    auto arrive = [&](int64_t k_next) __attribute__((always_inline)) {
+        constexpr int kAfterHas = (D - 1) * IPW + D * kRgStores;
+        constexpr int kAfterIdle = (D - 1) * IPW;
+        mem_order();
+        if (has) wait_vm_lgkm0<kAfterHas>();
+        else wait_vm_lgkm0<kAfterIdle>();
+        mem_order();
+        if (fixup) {
+            unsigned char* base = ring + slot_of(k_next) + wbase + lane * 16;
+#pragma unroll
+            for (int m = 0; m < IPW; ++m) {
+                const int n = sinf[m] >> 8;
+                if (n < 8) {
+                    uint4* u = reinterpret_cast<uint4*>(base + m * 1024);
+                    *u = keep_first<T>(*u, n);
+                }
+            }
+            mem_order();
+            wait_lgkm0();
+        }
+        mem_order();
+        __builtin_amdgcn_s_barrier();
+        mem_order();
+    };
+
+    // byte offset in a slot of row l32's unit 2 i + h (i < 8) after the
+    // permutation; unit 16 b + c lies 256 b bytes further
+    int off8[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) off8[i] = l32 * ROWB + (((2 * i + h) ^ (l32 & 15)) << 4);
+
+    f32x16_t acc;
+    auto multiply = [&](int64_t k) __attribute__((always_inline)) {
+        const unsigned char* rp = ring + slot_of(k);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        uint4 ab[2][BT];
+        auto rd = [&](auto b_c, uint4 (&dst)[BT]) __attribute__((always_inline)) {
+            constexpr int b = decltype(b_c)::value;
+#pragma unroll
+            for (int i = 0; i < BT; ++i) {
+                const int ks = b * BT + i;
+                dst[i] = *reinterpret_cast<const uint4*>(rp + off8[ks & 7] + 256 * (ks >> 3));
+            }
+        };
+        rd(std::integral_constant<int, 0>{}, ab[0]);
+        static_for<0, KS / BT>([&](auto b_c) __attribute__((always_inline)) {
+            constexpr int b = decltype(b_c)::value;
+            if constexpr (b + 1 < KS / BT) rd(std::integral_constant<int, b + 1>{}, ab[(b + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < BT; ++i)
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w[b * BT + i]),
+                                                             __builtin_bit_cast(bf16x8_t, ab[b & 1][i]), acc, 0, 0,
+                                                             0);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // bias, one rounding, staged as row l32, columns 8q + 4h .. +3 of the
+    // block, then stored as 16-byte row pieces (N is a multiple of 8)
+    auto finish = [&](int64_t tile) __attribute__((always_inline)) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 bv = *reinterpret_cast<const float4*>(bias_s + wave * 32 + 8 * q + 4 * h);
+            const float y[4] = {acc[4 * q] + bv.x, acc[4 * q + 1] + bv.y, acc[4 * q + 2] + bv.z,
+                                acc[4 * q + 3] + bv.w};
+            *reinterpret_cast<uint2*>(stage + l32 * 80 + (8 * q + 4 * h) * 2) =
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int i = 0; i < kRgStores; ++i) {
+            const int r = (lane >> 2) + 16 * i, c = lane & 3;
+            const int64_t grow = tile * kRgRows + r;
+            const int64_t col = static_cast<int64_t>(wave) * 32 + c * 8;
+            const bool inside = grow < A.M && col < N;
+            uint4 v = *reinterpret_cast<const uint4*>(stage + r * 80 + c * 16);
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                T* dst;
+                if (pass == 0) {
+                    if (!e.pre) continue;
+                    dst = e.pre;
+                } else {
+                    dst = e.c;
+                    if (e.relu) {
+                        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            // zero negative values (not -0 or NaN, as max(y, 0) on the fp32 value)
+                            const uint32_t bb = (q & 1) ? (wv[q / 2] >> 16) : (wv[q / 2] & 0xffffu);
+                            const uint32_t mag = bb & 0x7fffu;
+                            if ((bb & 0x8000u) && mag != 0u && mag <= 0x7f80u)
+                                wv[q / 2] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
+                        }
+                        v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                    }
+                }
+                uint4* p = inside ? reinterpret_cast<uint4*>(dst + grow * e.ldc + col) : &g_ring_sink[wave * 64 + lane];
+                *p = v;
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    };
+
+    // Vector-memory operations issued after tile k + 1's direct loads when
+    // step k waits for them: the stores of the step that issued them, then
+    // D - 1 more steps of loads and stores (each step issues at least
+    // kRgStores stores per wavefront with a block, and the prologue issues
+    // sink stores in place of the steps before the first, so the count
+    // holds there too).
+    const int64_t steps = (n_tiles - t0 + G - 1) / G;
+    for (int v = 0; v < D; ++v) {
+        dma(v, t0 + v * G);
+        mem_order();
+        if (has) sink_stores();
+        mem_order();
+    }
+    arrive(0);
+    for (int64_t k = 0; k < steps; ++k) {
+        // slot (k + D) % S was multiplied in the step before and every
+        // wavefront has passed the barrier since
+        dma(k + D, t0 + (k + D) * G);
+        mem_order();
+        if (has) {
+            if (late) {
+                if (k > 0) finish(t0 + (k - 1) * G);
+                else sink_stores();
+                mem_order();
+                multiply(k);
+            } else {
+                multiply(k);
+                mem_order();
+                finish(t0 + k * G);
+            }
+        }
+        arrive(k + 1);
+    }
+    if (has && late) finish(t0 + (steps - 1) * G);
+    // no direct load may still be writing LDS when the workgroup ends
+    wait_vm_lgkm0<0>();
+}
+
+template <int KS, int S, bool PP, int WPE>
+sag_status launch_nn_ring(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt, int64_t N,
+                          const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
+    const void* fn = reinterpret_cast<const void*>(&gemm_nn_ring<KS, S, PP, WPE>);
+    // The wait counts assume that no vector-memory load of the compiler's own
+    // runs in the loop; register spills would add scratch loads whose waits
+    // the compiler counts without the direct loads it cannot see.  An
+    // instance with a private segment is therefore never launched.
+    static const bool spill_free = [fn] {
+        hipFuncAttributes a{};
+        return hipFuncGetAttributes(&a, fn) == hipSuccess && a.localSizeBytes == 0;
+    }();
+    if (!spill_free) return SAG_E_UNSUPPORTED;
+    const int NB = static_cast<int>(cdiv(N, 32));
+    // persistent workgroups: exactly as many as are resident at once
+    static const int per_cu = [fn] {
+        int nb = 0;
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kRgWaves * 64, 0) == hipSuccess && nb > 0 ? nb
+                                                                                                                : 1;
+    }();
+    const int64_t n_tiles = cdiv(ao.M, kRgRows);
+    int64_t grid = static_cast<int64_t>(device_cus()) * per_cu;
+    if (grid > n_tiles) grid = n_tiles;
+    const int fixup = (ao.a1 && ao.k1 % 8) || (ao.a2 && ao.k2 % 8);
+    gemm_nn_ring<KS, S, PP, WPE><<<dim3(static_cast<unsigned>(grid)), kRgWaves * 64, 0, s>>>(ao, B, Kt, N, NB,
+                                                                                            n_tiles, e, bias, fixup);
+    SAG_LAUNCH_CHECK();
+    return SAG_OK;
+}
+
+#ifndef SAG_NN_RING
+#define SAG_NN_RING 1
+#endif
+
+// The ring kernel for bf16 without a mask or an addend, 128 < N <= 256 with
+// N a multiple of 8 (one 32-column block per wavefront, whole 16-byte
+// stores) and a packed K of 256 or 512; SAG_E_UNSUPPORTED otherwise.  (At
+// K = 128 the register-prefetch kernel runs two workgroups per CU and is
+// faster: 0.40 against 0.44 ms for 2.45M rows to 256 columns.)
+sag_status try_nn_ring(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t Kt, int64_t N,
+                       const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
+    if (!SAG_NN_RING || e.add || ao.mask || N % 8) return SAG_E_UNSUPPORTED;
+    const int64_t NB = cdiv(N, 32);
+    if (NB <= 4 || NB > kRgWaves) return SAG_E_UNSUPPORTED;
+    switch (Kt) {
+        case 256: return launch_nn_ring<16, 8, true, 1>(ao, B, Kt, N, e, bias, s);
+        case 512: return launch_nn_ring<32, 4, false, 1>(ao, B, Kt, N, e, bias, s);
+        default: return SAG_E_UNSUPPORTED;
+    }
+}
+
 // ---- TN (weight gradient) -----------------------------------------------------------
 // C[k, n] = sum over a chunk of rows m of A[m, k] B[m, n].  Tile: KT rows of C
 // (K up to 512 in one tile) by BNT columns; 8 wavefronts, WK along K by WN
@@ -1204,7 +1555,9 @@ sag_status nn_typed(int64_t M, int64_t N, const GemmA& A, const void* Bp, sag_dt
     const T* B = static_cast<const T*>(Bp);
     if constexpr (sizeof(T) == 2) {
         if (nn_rw_enabled()) {
-            const sag_status st = try_nn_rw(ao, B, Kt, N, e, epi.bias, s);
+            sag_status st = try_nn_ring(ao, B, Kt, N, e, epi.bias, s);
+            if (st != SAG_E_UNSUPPORTED) return st;
+            st = try_nn_rw(ao, B, Kt, N, e, epi.bias, s);
             if (st != SAG_E_UNSUPPORTED) return st;
         }
     }

@@ -110,6 +110,30 @@ def test_gemm_few_rows(dt, M, K, N):
     assert np.array_equal(f64(C), ref)
 
 
+@pytest.mark.parametrize("M,K1,K2,N", [(2053, 512, 0, 200), (777, 100, 100, 136), (64, 128, 0, 256),
+                                        (100_003, 200, 56, 256), (120_001, 256, 256, 248), (50_000, 100, 0, 160)])
+def test_gemm_streamed_tiles(M, K1, K2, N):
+    """bf16 products with 128 < N <= 256 (N a multiple of 8) and a packed K of
+    256 or 512, whose row tiles stream through an LDS ring (and one at a
+    packed K of 128, which takes the register-prefetch kernel): column
+    blocks past N (a wavefront with no block, one half outside), rows past
+    M, partly covered 16-byte units in both K blocks, and enough tiles per
+    workgroup for the ring to wrap many times.  Exact small integers (every
+    sum is exact in fp32), so the result is the exact product rounded once
+    to bf16, bit for bit."""
+    g = np.random.default_rng(M + K1 + K2 + N)
+    _, A1 = _mat(g, (M, K1), "bf16", integers=True)
+    A2 = _mat(g, (M, K2), "bf16", integers=True)[1] if K2 else None
+    _, W = _mat(g, (K1 + K2, N), "bf16", integers=True)
+    W = W.contiguous()
+    b = g.integers(-3, 4, N).astype(np.float32)
+    say(f"gemm streamed tiles M={M} K={K1}+{K2} N={N}")
+    C = sag.gemm(A1, W, A2=A2, bias=to_dev(b), relu=True)
+    A64 = f64(A1) if not K2 else np.concatenate([f64(A1), f64(A2)], 1)
+    exact = A64 @ f64(W) + b
+    assert np.array_equal(f64(C), olay.round_bf16(np.maximum(exact, 0)))
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [80, 300])
 def test_gemm_exact_integers(dt, N):
@@ -161,13 +185,13 @@ def test_gemm_tn_two_blocks():
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("masked", [False, True])
-def test_gemm_tight_row_pitch(dt, masked):
+@pytest.mark.parametrize("masked,N", [(False, 96), (True, 96), (False, 256)])
+def test_gemm_tight_row_pitch(dt, masked, N):
     """Operands whose row pitch is the width rounded to 16 bytes only (e.g.
     100 bf16 in rows of 104) and that end exactly at the end of their
     allocation: the padded k-steps must not read past the rows."""
-    g = np.random.default_rng(31)
-    M, K1, K2, N = 333, 100, 42, 96
+    g = np.random.default_rng(31 + N)
+    M, K1, K2 = 333, 100, 42
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     v = 4 if dt == "f32" else 8
 
