@@ -151,7 +151,9 @@ def summarize_counters(args):
            "kernel_fetch_kib": sum(kf) / len(kf), "kernel_write_kib": sum(kw) / len(kw),
            "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
            "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b))}
-    cmd = ("python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-extras --configs '' --copy-calib")
+    cfg_arg = f" --config {args.config}" if args.config != 4 else ""
+    sizes_arg = f" --sizes-dir {args.sizes_dir}" if args.sizes_dir else ""
+    cmd = f"python3 bench.py{cfg_arg} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --configs '' --copy-calib"
     sizes = ""
     if args.sizes_dir:
         names = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
@@ -188,7 +190,7 @@ Commands (each a run of its own, from the repository root):
 ```
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize_counters[0]} -o fetch -- {cmd}
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize_counters[1]} -o write -- {cmd}
-python3 bench.py --summarize-counters {args.summarize_counters[0]} {args.summarize_counters[1]} \\
+python3 bench.py{cfg_arg} --summarize-counters {args.summarize_counters[0]} {args.summarize_counters[1]}{sizes_arg} \\
     --op '{args.op}' --kernel '{args.kernel}' --out {args.out}
 ```
 
@@ -225,6 +227,29 @@ def stored_counters(op: str):
                     return rec, os.path.relpath(f, ROOT)
     return None, None
 
+
+
+def with_traffic(roof):
+    """roof plus the HBM traffic of its kernel from a committed counter
+    summary taken on the current kernel sources (null fields without one)."""
+    crec, tsrc = stored_counters(roof["kernel"])
+    avg_s = roof["avg_launch_ms"] / 1e3
+    roof["traffic"] = crec["traffic_bytes_per_launch"] if crec else None
+    roof["traffic_source"] = tsrc
+    # the rate of the bytes the counters saw (L2 <-> fabric, hits in the
+    # memory-side cache (MALL) included, so an upper proxy for DRAM bytes)
+    # against the same peak, beside the algorithmic fraction
+    roof["traffic_GBps_mall_inclusive"] = (round(roof["traffic"] / avg_s / 1e9, 1)
+                                           if crec and roof["unit"] == "GB/s" else None)
+    roof["traffic_frac_mall_inclusive"] = (round(roof["traffic_GBps_mall_inclusive"] / HBM_PEAK_GBS, 4)
+                                           if roof["traffic_GBps_mall_inclusive"] else None)
+    # L2-miss read requests of one launch (all whole 128-byte lines for the
+    # gathers) and the rate this run achieved: random row gathers on this part
+    # are capped by that rate, not by HBM bytes
+    reqs = crec.get("read_requests_kernel") if crec else None
+    roof["read_requests_per_launch"] = reqs
+    roof["read_request_rate_G_per_s"] = round(reqs / avg_s / 1e9, 2) if reqs else None
+    return roof
 
 
 def graph_stats(A, n_l, torch):
@@ -808,7 +833,7 @@ def config_run(w, sag, torch, args):
     out = {"workload": w.name, "config": w.cfg, "dtype": w.dtype, "dims": w.dims, "layer": w.model,
            "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
            "ms_per_step": round(ms, 4), "step_ms": pct(per), "steps": steps,
-           "roofline": roofline_of(table, ops, w.dtype), "ops": table[:6], "graph": m.graph_stats}
+           "roofline": with_traffic(roofline_of(table, ops, w.dtype)), "ops": table[:6], "graph": m.graph_stats}
     if any(w.dims[l] <= w.dims[l + 1] for l in range(w.n_layers)) and w.cfg != 1:
         # layers that aggregate first: the fused aggregate -> transform kernel
         # against the separate SpMM and product
@@ -881,24 +906,7 @@ def run(args, cfgs, jobs):
     cold = cold_steps(m, torch, min(args.steps, 5))
     table, ops = op_table(recs, args.steps)
     spmm = [t for t in table if t["op"].startswith("spmm")]
-    roof = roofline_of(table, ops, w.dtype)
-    crec, tsrc = stored_counters(roof["kernel"])
-    avg_s = roof["avg_launch_ms"] / 1e3
-    roof["traffic"] = crec["traffic_bytes_per_launch"] if crec else None
-    roof["traffic_source"] = tsrc
-    # the rate of the bytes the counters saw (L2 <-> fabric, hits in the
-    # memory-side cache (MALL) included, so an upper proxy for DRAM bytes)
-    # against the same peak, beside the algorithmic fraction
-    roof["traffic_GBps_mall_inclusive"] = (round(roof["traffic"] / avg_s / 1e9, 1)
-                                           if crec and roof["unit"] == "GB/s" else None)
-    roof["traffic_frac_mall_inclusive"] = (round(roof["traffic_GBps_mall_inclusive"] / HBM_PEAK_GBS, 4)
-                                           if roof["traffic_GBps_mall_inclusive"] else None)
-    # L2-miss read requests of one launch (all whole 128-byte lines for the
-    # gathers) and the rate this run achieved: random row gathers on this part
-    # are capped by that rate, not by HBM bytes
-    reqs = crec.get("read_requests_kernel") if crec else None
-    roof["read_requests_per_launch"] = reqs
-    roof["read_request_rate_G_per_s"] = round(reqs / avg_s / 1e9, 2) if reqs else None
+    roof = with_traffic(roofline_of(table, ops, w.dtype))
 
     # the same step with the first layer's input gradient as well
     for _ in range(2):
