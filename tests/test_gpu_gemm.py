@@ -111,14 +111,15 @@ def test_gemm_few_rows(dt, M, K, N):
 
 
 @pytest.mark.parametrize("M,K1,K2,N", [(2053, 512, 0, 200), (777, 100, 100, 136), (64, 128, 0, 256),
-                                        (100_003, 200, 56, 256), (120_001, 256, 256, 248), (50_000, 100, 0, 160)])
+                                        (100_003, 300, 100, 256), (120_001, 256, 256, 248), (50_000, 100, 100, 160)])
 def test_gemm_streamed_tiles(M, K1, K2, N):
     """bf16 products with 128 < N <= 256 (N a multiple of 8) and a packed K of
     256 or 512, whose row tiles stream through an LDS ring (and one at a
     packed K of 128, which takes the register-prefetch kernel): column
-    blocks past N (a wavefront with no block, one half outside), rows past
-    M, partly covered 16-byte units in both K blocks, and enough tiles per
-    workgroup for the ring to wrap many times.  Exact small integers (every
+    blocks past N (wavefronts with no block in either half of the
+    workgroup, one block half outside), rows past M, partly covered 16-byte
+    units in both K blocks at both packed K, and enough tiles per workgroup
+    for the ring to wrap many times.  Exact small integers (every
     sum is exact in fp32), so the result is the exact product rounded once
     to bf16, bit for bit."""
     g = np.random.default_rng(M + K1 + K2 + N)
