@@ -261,8 +261,11 @@ def graph_stats(A, n_l, torch):
     srt = torch.sort(lens).values
     p99 = float(srt[min(A.n_rows - 1, int(0.99 * (A.n_rows - 1) + 0.5))])
     halo = int((A.indices >= n_l).sum()) if A.n_cols > n_l else 0
+    # (edge_reuse: how many times a gathered row is read on average, the
+    # edge-gather bytes nnz * d * elt over the input rows' elt * d * n_cols)
     return {"row_len_min": int(srt[0]), "row_len_mean": round(float(lens.mean()), 2), "row_len_p99": int(p99),
-            "row_len_max": int(srt[-1]), "halo_share_of_nnz": round(halo / max(A.nnz, 1), 4)}
+            "row_len_max": int(srt[-1]), "halo_share_of_nnz": round(halo / max(A.nnz, 1), 4),
+            "edge_reuse": round(A.nnz / max(A.n_cols, 1), 2)}
 
 
 def pct(xs):
@@ -722,6 +725,12 @@ def op_table(recs, steps):
              "TFLOPs": round(o["flops"] / avg / 1e9, 2) if avg > 0 else None}
         if avg > 0:
             t["frac_hbm"] = round(t["GBps"] / HBM_PEAK_GBS, 4)
+            sp = re.match(r"spmm\w*\[([\w>]+),(\d+),(\d+),(\d+)\]", name)
+            if sp:
+                # every entry re-reading its row: nnz * d * element bytes of X
+                eg = int(sp.group(3)) * int(sp.group(4)) * (2 if sp.group(1).startswith("bf16") else 4)
+                t["edge_gather_GBps"] = round(eg / avg / 1e6, 1)
+                t["edge_gather_frac_hbm"] = round(t["edge_gather_GBps"] / HBM_PEAK_GBS, 4)
             if name.startswith("gemm") and o["flops"] > 0 and o["bytes"] > 0:
                 peak = MFMA_PEAK_TFLOPS["bf16" if "[bf16" in name else "f32"]
                 # the attainable ceiling: min(MFMA peak, arithmetic intensity x HBM peak)
