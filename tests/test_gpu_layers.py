@@ -137,7 +137,7 @@ def test_share_of_large_graph_gcn_bf16():
 
 @pytest.mark.parametrize("model", ["gcn", "sage"])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("d_in,d_out", [(16, 64), (64, 16), (41, 41), (100, 47), (8, 300)])
+@pytest.mark.parametrize("d_in,d_out", [(16, 64), (64, 16), (41, 41), (100, 47), (8, 300), (96, 200), (200, 160)])
 @pytest.mark.parametrize("halo", [False, True])
 def test_orders_and_partitions(model, dt, d_in, d_out, halo):
     g = np.random.default_rng(d_in * 1000 + d_out)
