@@ -725,8 +725,8 @@ sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t
                         const EpiT<uint16_t>& e, const float* bias, hipStream_t s) {
     constexpr int PF = rw_pf<KS, NBW, MASK>(), WPE = rw_wpe<KS, NBW, MASK>();
     const int NB = static_cast<int>(cdiv(N, 32));
-    const size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage +
-                       static_cast<size_t>(kRwWaves) * NBW * 32 * sizeof(float);
+    constexpr size_t lds = 2 * static_cast<size_t>(rw_atile<KS>()) + static_cast<size_t>(kRwWaves) * NBW * kRwStage +
+                           static_cast<size_t>(kRwWaves) * NBW * 32 * sizeof(float);
     // (once per kernel instance: the initialisation of a function-local
     // static is thread-safe)
     static const hipError_t attr = hipFuncSetAttribute(
@@ -734,7 +734,7 @@ sag_status launch_nn_rw(const AOperand<uint16_t>& ao, const uint16_t* B, int64_t
         131072);
     SAG_CHECK_HIP(attr);
     // persistent workgroups: exactly as many as are resident at once
-    static const int per_cu = [lds] {
+    static const int per_cu = [] {
         int nb = 0;
         return hipOccupancyMaxActiveBlocksPerMultiprocessor(
                    &nb, reinterpret_cast<const void*>(&gemm_nn_rw<KS, NBW, MASK, PF, WPE>), kRwWaves * 64, lds) ==
@@ -817,13 +817,23 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 // One direct load: 16 bytes per lane from g into LDS at lds + 16 * lane.  In
 // asm rather than through the builtin: the compiler would otherwise make
 // every later LDS read wait for the newest direct load (it cannot tell the
-// ring slots apart), which would drain the ring at each step.  No register
-// is written; M0 (the LDS address; nothing else in these kernels uses it) is
-// declared clobbered, and a wait state separates its write from the load
-// that reads it.
+// ring slots apart), which would drain the ring at each step.  The load takes
+// its LDS address from M0, a register the compiler reserves for itself, so
+// the asm keeps M0's value in a scratch SGPR and puts it back after issuing
+// the load (a wait state on each side of the load; no vector register is
+// written).
 __device__ __forceinline__ void lds_direct_load16(const void* g, uint32_t lds) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
-                 : "memory", "m0");
+    uint32_t keep;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(keep)
+        : "v"(g), "s"(lds)
+        : "memory");
 }
 
 // s_waitcnt with vmcnt = N and lgkmcnt = 0 (expcnt not waited for); the
