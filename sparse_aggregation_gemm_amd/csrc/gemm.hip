@@ -274,6 +274,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
+// ReLU on eight packed bf16 values: zeroes the negative ones, leaving -0 and
+// NaN as they are (as max(y, 0) on the fp32 value before rounding would).
+__device__ __forceinline__ uint4 relu_bf16x8(uint4 v) {
+    uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t b = (q & 1) ? (wv[q / 2] >> 16) : (wv[q / 2] & 0xffffu);
+        const uint32_t mag = b & 0x7fffu;
+        if ((b & 0x8000u) && mag != 0u && mag <= 0x7f80u) wv[q / 2] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
+    }
+    return make_uint4(wv[0], wv[1], wv[2], wv[3]);
+}
+
 template <class T, int BN, bool MASK, int PD>
 __global__ __launch_bounds__(kNnWaves * 64, 1) void gemm_nn(AOperand<T> A, const T* __restrict__ Bp, int64_t Kt,
                                                              int64_t N, int64_t n_nblk, int64_t n_mgroups,
@@ -644,18 +657,7 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
                         dst = e.pre;
                     } else {
                         dst = e.c;
-                        if (e.relu) {
-                            uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                            for (int q = 0; q < 8; ++q) {
-                                // zero negative values (not -0 or NaN, as max(y, 0) on the fp32 value)
-                                const uint32_t b = (q & 1) ? (wv[q / 2] >> 16) : (wv[q / 2] & 0xffffu);
-                                const uint32_t mag = b & 0x7fffu;
-                                if ((b & 0x8000u) && mag != 0u && mag <= 0x7f80u)
-                                    wv[q / 2] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
-                            }
-                            v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                        }
+                        if (e.relu) v = relu_bf16x8(v);
                     }
                     T* p = dst + grow * e.ldc + col;
                     if (n == 8) {
@@ -1029,18 +1031,7 @@ __global__ __launch_bounds__(kRgWaves * 64, WPE) void gemm_nn_ring(AOperand<uint
                     dst = e.pre;
                 } else {
                     dst = e.c;
-                    if (e.relu) {
-                        uint32_t wv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                        for (int q = 0; q < 8; ++q) {
-                            // zero negative values (not -0 or NaN, as max(y, 0) on the fp32 value)
-                            const uint32_t bb = (q & 1) ? (wv[q / 2] >> 16) : (wv[q / 2] & 0xffffu);
-                            const uint32_t mag = bb & 0x7fffu;
-                            if ((bb & 0x8000u) && mag != 0u && mag <= 0x7f80u)
-                                wv[q / 2] &= (q & 1) ? 0x0000ffffu : 0xffff0000u;
-                        }
-                        v = make_uint4(wv[0], wv[1], wv[2], wv[3]);
-                    }
+                    if (e.relu) v = relu_bf16x8(v);
                 }
                 uint4* p = inside ? reinterpret_cast<uint4*>(dst + grow * e.ldc + col) : &g_ring_sink[wave * 64 + lane];
                 *p = v;
