@@ -70,6 +70,14 @@ def _ld(x: torch.Tensor) -> int:
     return max(x.stride(0), x.shape[1]) if x.shape[0] <= 1 else x.stride(0)
 
 
+def _need_rows(what: str, t, n: int) -> None:
+    """ValueError unless t (when given) has at least n rows: the C ABI takes
+    pointers and cannot see tensor sizes, so a short buffer would be read or
+    written past its end on the GPU."""
+    if t is not None and t.shape[0] < n:
+        raise ValueError(f"{what} has {t.shape[0]} rows; the call reads or writes {n}")
+
+
 def _ws(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
@@ -209,7 +217,9 @@ def csr_info(A: Csr) -> dict:
 
 
 def halo_gather(src: torch.Tensor, rows: torch.Tensor, out: torch.Tensor, row_base: int = 0) -> torch.Tensor:
-    """sag_halo_gather: out[k] = src[rows[k] - row_base] (bitwise)."""
+    """sag_halo_gather: out[k] = src[rows[k] - row_base] (bitwise).  The ids
+    must lie in src's rows (the kernel does not check them)."""
+    _need_rows("halo_gather out", out, rows.numel())
     rows = rows.to(torch.int32).contiguous()
     st = L.lib().sag_halo_gather(_ptr(src), _ld(src), _ptr(rows), row_base, rows.numel(), src.shape[1],
                                  dtype_code(src.dtype), _ptr(out), _ld(out) if out.shape[0] else src.shape[1],
@@ -222,6 +232,7 @@ def halo_push(src: torch.Tensor, ids: torch.Tensor, dst: torch.Tensor, row_base:
               accumulate: bool = False) -> torch.Tensor:
     """sag_halo_push: dst[ids[k] - row_base] = src[k] (or += for gradients);
     targets outside dst's rows are skipped."""
+    _need_rows("halo_push src", src, ids.numel())
     ids = ids.to(torch.int32).contiguous()
     st = L.lib().sag_halo_push(_ptr(src), _ld(src), _ptr(ids), row_base, ids.numel(), src.shape[1],
                                dtype_code(src.dtype), int(bool(accumulate)), _ptr(dst), _ld(dst), dst.shape[0],
@@ -280,6 +291,8 @@ def dequantize_rows(codes: torch.Tensor, scale: torch.Tensor, zero: torch.Tensor
 
 
 def _spmm(name, A: Csr, X, out_dtype=None, Y=None, addend=None):
+    _need_rows(f"{name} X", X, A.n_cols)
+    _need_rows(f"{name} Y", Y, A.n_rows)
     lib = L.lib()
     d = X.shape[1]
     yt = out_dtype or X.dtype
@@ -309,6 +322,8 @@ def spmm_csr_noalloc(A: Csr, X, Y, addend=None):
     """sag_spmm_csr_noalloc: Y = A X (+ addend) into the caller's Y, with
     the long rows' partials in the library's fixed device scratch (no
     workspace; nothing allocated by the call)."""
+    _need_rows("spmm_csr_noalloc X", X, A.n_cols)
+    _need_rows("spmm_csr_noalloc Y", Y, A.n_rows)
     n_add = addend.shape[0] if addend is not None else 0
     st = L.lib().sag_spmm_csr_noalloc(A.ref, _ptr(X), _ld(X), dtype_code(X.dtype), X.shape[1], _ptr(Y), _ld(Y),
                                       dtype_code(Y.dtype), _ptr(addend), _ld(addend) if addend is not None else 0,
@@ -336,6 +351,10 @@ class LayerCtx:
 
 
 def _layer_forward(kind, A: Csr, H_ext, W, b, relu, want_pre, Out=None, Y_pre=None, ws=None, fused=False):
+    _need_rows(f"{kind}_layer_forward H_ext (local + halo rows)", H_ext, A.n_cols)
+    _need_rows(f"{kind}_layer_forward W", W, (2 if kind == "sage" else 1) * H_ext.shape[1])
+    _need_rows(f"{kind}_layer_forward Out", Out, A.n_rows)
+    _need_rows(f"{kind}_layer_forward Y_pre", Y_pre, A.n_rows)
     lib = L.lib()
     dt = dtype_code(H_ext.dtype)
     d_in = H_ext.shape[1]
@@ -364,6 +383,13 @@ def _layer_forward(kind, A: Csr, H_ext, W, b, relu, want_pre, Out=None, Y_pre=No
 
 def _layer_backward(ctx: LayerCtx, AT: Csr | None, n_local: int, Y, G_out, want_dH=True,
                     want_db=True, dH=None, ws=None):
+    _need_rows(f"{ctx.kind}_layer_backward G_out", G_out, n_local)
+    if ctx.relu:
+        _need_rows(f"{ctx.kind}_layer_backward Y", Y, n_local)
+    if AT is not None:
+        _need_rows(f"{ctx.kind}_layer_backward H_ext", ctx.H_ext, AT.n_rows)
+        if want_dH:
+            _need_rows(f"{ctx.kind}_layer_backward dH", dH, AT.n_rows)
     lib = L.lib()
     kind = ctx.kind
     dt = dtype_code(G_out.dtype)
@@ -417,6 +443,9 @@ def aggregate_transform(A: Csr, H_ext, W, b=None, self_rows=False, relu=True, wa
     """sag_aggregate_transform: Out = act(Z W + b) or act([H_local | Z] W + b)
     with Z = A H_ext summed and multiplied in one kernel.  Returns
     (Out, Y_pre, Z)."""
+    _need_rows("aggregate_transform H_ext (local + halo rows)", H_ext, A.n_cols)
+    _need_rows("aggregate_transform Out", Out, A.n_rows)
+    _need_rows("aggregate_transform Z", Z, A.n_rows)
     lib = L.lib()
     dt = dtype_code(H_ext.dtype)
     d_in = H_ext.shape[1]
@@ -461,6 +490,8 @@ def gat_layer_forward(A: Csr, H_ext, W, a_src, a_dst, b=None, heads=1, slope=0.2
                       Out=None, ws=None):
     """sag_gat_layer_forward: Out = act(concat_k sum_u alpha^k_vu (H_ext W)_k[u] + b).
     W [d_in, heads * d_head]; a_src, a_dst fp32 [heads, d_head].  Returns (Out, ctx)."""
+    _need_rows("gat_layer_forward H_ext (local + halo rows)", H_ext, A.n_cols)
+    _need_rows("gat_layer_forward Out", Out, A.n_rows)
     lib = L.lib()
     dt = dtype_code(H_ext.dtype)
     d_in = H_ext.shape[1]
@@ -487,6 +518,11 @@ def gat_layer_forward(A: Csr, H_ext, W, a_src, a_dst, b=None, heads=1, slope=0.2
 
 def gat_layer_backward(ctx: GatCtx, A: Csr, AT: Csr, Y, G_out, want_dH=True, dH=None, ws=None):
     """sag_gat_layer_backward: returns (dW, da_src, da_dst, db, dH_ext)."""
+    _need_rows("gat_layer_backward G_out", G_out, A.n_rows)
+    if ctx.relu:
+        _need_rows("gat_layer_backward Y", Y, A.n_rows)
+    if want_dH:
+        _need_rows("gat_layer_backward dH", dH, AT.n_rows)
     lib = L.lib()
     dt = dtype_code(G_out.dtype)
     dev = G_out.device
@@ -519,6 +555,13 @@ def gat_layer_backward(ctx: GatCtx, A: Csr, AT: Csr, Y, G_out, want_dH=True, dH=
 def gemm(A1, B, A2=None, mask=None, trans_b=False, bias=None, addend=None, relu=False,
          want_pre=False):
     """sag_gemm: C = [A1 | A2] B (+ bias) (+ addend), optional ReLU."""
+    M = A1.shape[0]
+    _need_rows("gemm A2", A2, M)
+    _need_rows("gemm mask", mask, M)
+    _need_rows("gemm B (rows = K)" if not trans_b else "gemm B (transposed: rows = N)", B,
+               0 if trans_b else A1.shape[1] + (A2.shape[1] if A2 is not None else 0))
+    _need_rows("gemm addend", addend, M)
+    _need_rows("gemm bias", bias, B.shape[0] if trans_b else B.shape[1])
     lib = L.lib()
     dt = dtype_code(A1.dtype)
     M = A1.shape[0]
@@ -542,6 +585,10 @@ def gemm(A1, B, A2=None, mask=None, trans_b=False, bias=None, addend=None, relu=
 
 def gemm_tn(A1, B, A2=None, mask=None, want_colsum=True):
     """sag_gemm_tn: C = [A1 | A2]^T (B * 1[mask > 0]) in fp32, and column sums."""
+    M = A1.shape[0]
+    _need_rows("gemm_tn A2", A2, M)
+    _need_rows("gemm_tn B", B, M)
+    _need_rows("gemm_tn mask", mask, M)
     lib = L.lib()
     dt = dtype_code(A1.dtype)
     M, K1 = A1.shape
