@@ -46,7 +46,7 @@ def padded_ld(d: int, dtype: torch.dtype) -> int:
 
 
 def empty_dense(rows: int, d: int, dtype: torch.dtype, device, fill=None) -> torch.Tensor:
-    """[rows, d] view of a [rows, ld] buffer with ld padded to 16 bytes."""
+    """[rows, d] view of a [rows, ld] buffer with ld = padded_ld(d, dtype)."""
     buf = torch.empty((rows, padded_ld(d, dtype)), dtype=dtype, device=device)
     if fill is not None:
         buf.fill_(fill)
