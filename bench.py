@@ -252,6 +252,51 @@ def with_traffic(roof):
     return roof
 
 
+def gather_probe_of(roof, built, sag, torch, reps=5):
+    """The row-gather probe over the dominant SpMM's own column ids (of each
+    matrix whose launches make up the op) and rows of its width
+    and dtype: the rate at which the memory system serves that access
+    pattern with no values, row structure or epilogue, and the op's average
+    launch against it.  None when the dominant op is not an SpMM."""
+    mt = re.match(r"spmm\w*\[([\w>]+),(\d+),(\d+),(\d+)\]", roof["kernel"])
+    if not mt:
+        return None
+    dt = torch.bfloat16 if mt.group(1).startswith("bf16") else torch.float32
+    rows, d = int(mt.group(2)), int(mt.group(4))
+    # the op's launches: A's product and, when the halo is empty, the
+    # transposed one (same row count, so the same op name; on the workloads
+    # here the dominant op of such a graph has both)
+    mats = [M for M in (built.A, built.AT) if M is not None and M.n_rows == rows]
+    if not mats:
+        return None
+    X = sag.empty_dense(max(M.n_cols for M in mats), d, dt, "cuda:0", fill=1.0)
+    es = X.element_size()
+    pitch, rb = X.stride(0) * es, d * es
+    sink, times, lines = None, [], []
+    for M in mats:
+        ids = M.indices
+        sink = sag.gather_probe(X, ids, sink)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            sag.gather_probe(X, ids, sink)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / reps)
+        # 128-byte lines the rows span where they lie (the buffer starts on a line)
+        lines.append(int((((ids.to(torch.int64) * pitch) % 128 + rb - 1) // 128 + 1).sum().item()))
+    del X, sink
+    probe_ms = sum(times) / len(times)
+    n_lines = sum(lines) / len(lines)
+    return {"probe_ms": round(probe_ms, 4), "probe_ms_each": [round(t, 4) for t in times],
+            "lines_per_launch": int(n_lines), "G_lines_per_s": round(n_lines / probe_ms / 1e6, 2),
+            "kernel_ms": roof["avg_launch_ms"], "probe_over_kernel": round(probe_ms / roof["avg_launch_ms"], 4),
+            "note": "the same ids gathered with the SpMM's lane layout and nothing else (over each matrix whose "
+                    "launches make up the op, averaged like the op); probe_over_kernel near 1 means the product "
+                    "runs at the rate the memory system serves these rows"}
+
+
 def graph_stats(A, n_l, torch):
     """Row-length statistics of the local CSR (self-loops included) and the
     share of its entries that fall in halo columns."""
@@ -886,6 +931,8 @@ def config_run(w, sag, torch, args):
     ms, per, recs = timed_steps(m, sag, torch, steps)
     g_ms, g_per, g_err = graph_steps(m, torch, steps)
     table, ops = op_table(recs, steps)
+    roof = with_traffic(roofline_of(table, ops, w.dtype))
+    roof["gather_probe"] = gather_probe_of(roof, m.built, sag, torch) if w.cfg != 1 else None
     out = {"workload": w.name, "config": w.cfg, "dtype": w.dtype, "dims": w.dims, "layer": w.model,
            "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
            "ms_per_step": round(min(ms, g_ms) if g_ms is not None else ms, 4),
@@ -894,7 +941,7 @@ def config_run(w, sag, torch, args):
            "eager_ms_per_step": round(ms, 4),
            "graph_replay": {"ms_per_step": round(g_ms, 4) if g_ms is not None else None,
                             "verified": g_ms is not None, "error": g_err},
-           "roofline": with_traffic(roofline_of(table, ops, w.dtype)), "ops": table[:6], "graph": m.graph_stats}
+           "roofline": roof, "ops": table[:6], "graph": m.graph_stats}
     if any(w.dims[l] <= w.dims[l + 1] for l in range(w.n_layers)) and w.cfg != 1:
         # layers that aggregate first: the fused aggregate -> transform kernel
         # against the separate SpMM and product
@@ -979,6 +1026,8 @@ def run(args, cfgs, jobs):
     table, ops = op_table(recs, args.steps)
     spmm = [t for t in table if t["op"].startswith("spmm")]
     roof = with_traffic(roofline_of(table, ops, w.dtype))
+    log("[bench] row-gather probe over the dominant SpMM's column ids")
+    roof["gather_probe"] = gather_probe_of(roof, m.built, sag, torch)
 
     # the same step with the first layer's input gradient as well
     for _ in range(2):

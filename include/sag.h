@@ -539,6 +539,23 @@ sag_status sag_trace_get(int64_t i, char* name, size_t name_cap, float* ms, int6
                          int64_t* flops);
 sag_status sag_trace_clear(void);
 
+/* Row-gather probe (measurement only): the rate at which the memory system
+ * delivers the rows an SpMM over the same ids gathers, without its row
+ * structure, values or epilogue.  Reads rows ids[0..n) of X (d elements of
+ * type dt, row pitch ldx elements; every id must lie in [0, rows of X),
+ * which is not checked) in order, in equal contiguous chunks of ids per
+ * wavefront, with the SpMM's lane layout, and folds every 16-byte vector of
+ * the rows' first ceil(d * elt / 16) vectors into per-lane sums of uint32
+ * words (wrapping) written to sink.  sink: device memory of
+ * sag_gather_probe_sink_bytes() bytes, 16-B aligned, owned by the caller;
+ * summed over all its 16-byte entries, word k (0..3) equals the sum mod
+ * 2^32 of word k of every such vector of every gathered row.  X and ldx * elt
+ * must be 16-B aligned; rows wider than 4 KB return SAG_E_UNSUPPORTED.
+ * Asynchronous on `stream`. */
+size_t sag_gather_probe_sink_bytes(void);
+sag_status sag_gather_probe(const void* X, int64_t ldx, int64_t d, sag_dtype dt, const int32_t* ids,
+                            int64_t n, void* sink, size_t sink_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Diagnostics. */
 const char* sag_status_string(sag_status s);

@@ -8,7 +8,7 @@ from .ops import (  # noqa: F401
     Built, Csr, LayerCtx, aggregate_transform, as_dense, code_row_bytes, csr_build_normalize,
     csr_build_normalize_query, csr_info, csr_schedule,
     dequantize_rows, dtype_code, empty_dense, GatCtx, gat_layer_backward, gat_layer_forward,
-    gcn_layer_backward, gcn_layer_forward, gemm, gemm_tn,
+    gather_probe, gcn_layer_backward, gcn_layer_forward, gemm, gemm_tn,
     halo_gather, halo_push, padded_ld, quantize_rows, sage_layer_backward, sage_layer_forward,
     spmm_csr, spmm_csr_noalloc, spmm_csr_t, spmm_noalloc_scratch_bytes, trace_enable, trace_records, version,
 )

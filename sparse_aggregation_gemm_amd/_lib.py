@@ -91,6 +91,8 @@ SIGNATURES = {
     "sag_trace_count": (i64, []),
     "sag_trace_get": (cint, [i64, ctypes.c_char_p, sz, P(ctypes.c_float), P(i64), P(i64)]),
     "sag_trace_clear": (cint, []),
+    "sag_gather_probe_sink_bytes": (sz, []),
+    "sag_gather_probe": (cint, [vp, i64, i64, cint, vp, i64, vp, sz, vp]),
     "sag_status_string": (ctypes.c_char_p, [cint]),
     "sag_last_error": (ctypes.c_char_p, []),
     "sag_version": (ctypes.c_char_p, []),

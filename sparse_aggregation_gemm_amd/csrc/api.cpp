@@ -26,6 +26,17 @@ sag_status check_dense(const char* name, const void* p, int64_t rows, int64_t d,
     return SAG_OK;
 }
 
+int device_cus() {
+    static const int cus = [] {
+        int dev = 0, v = 0;
+        return hipGetDevice(&dev) == hipSuccess &&
+                       hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
+                   ? v
+                   : 256;
+    }();
+    return cus;
+}
+
 }  // namespace sag
 
 extern "C" {

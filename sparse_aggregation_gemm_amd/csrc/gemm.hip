@@ -21,6 +21,10 @@
 #include "trace.h"
 
 namespace sag {
+
+// Compute units of the current device (api.cpp), queried once per process.
+int device_cus();
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -703,7 +707,6 @@ __global__ __launch_bounds__(kRwWaves * 64, WPE) void gemm_nn_rw(AOperand<uint16
     }
 }
 
-int device_cus();
 
 // Tiles in flight per workgroup: as many as the registers hold next to the
 // weight fragments (every slot is live at once: the loop issues the same
@@ -1475,17 +1478,6 @@ __global__ void relu_mask_kernel(int64_t M, int64_t C, int64_t N, const T* __res
 
 // Device properties, queried once per process (thread-safe static
 // initialisation): the library assumes the devices a process uses are alike.
-int device_cus() {
-    static const int cus = [] {
-        int dev = 0, v = 0;
-        return hipGetDevice(&dev) == hipSuccess &&
-                       hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0
-                   ? v
-                   : 256;
-    }();
-    return cus;
-}
-
 size_t max_lds_per_block() {
     static const size_t lds = [] {
         int dev = 0, v = 0;

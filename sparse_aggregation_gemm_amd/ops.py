@@ -624,5 +624,21 @@ def trace_records(clear: bool = True) -> list:
     return out
 
 
+def gather_probe(X: torch.Tensor, ids: torch.Tensor, sink: torch.Tensor | None = None) -> torch.Tensor:
+    """sag_gather_probe: read rows ids of X (in order, the SpMM's lane layout)
+    and fold them into the returned sink (uint8 bytes; viewed as int32 words,
+    word k of the sum over its 16-byte entries is the wrapping sum of word k
+    of every vector read).  A measurement helper: it times the row gather of
+    an SpMM over the same ids without the product around it."""
+    ids = ids.to(torch.int32).contiguous()
+    lib = L.lib()
+    if sink is None:
+        sink = torch.empty(int(lib.sag_gather_probe_sink_bytes()), dtype=torch.uint8, device=X.device)
+    st = lib.sag_gather_probe(_ptr(X), _ld(X), X.shape[1], dtype_code(X.dtype), _ptr(ids), ids.numel(),
+                              _ptr(sink), sink.numel(), _stream(X.device))
+    L.check("sag_gather_probe", st)
+    return sink
+
+
 def version() -> str:
     return L.lib().sag_version().decode()
