@@ -93,6 +93,9 @@ def parse():
     p.add_argument("--op", help="trace op name the summary is for (with --summarize-counters)")
     p.add_argument("--kernel", help="kernel name substring of that op (with --summarize-counters)")
     p.add_argument("--out", help="summary file to write (with --summarize-counters)")
+    p.add_argument("--dispatches-per-launch", type=int, default=1,
+                   help="dispatches of the kernel that make one launch of the op: 2 for a product over a hub "
+                        "split (hub pass, cold pass); with --summarize-counters")
     p.add_argument("--sizes-dir", help="optional third pass (TCC_EA0_RDREQ_sum and its 32B/64B/128B parts) "
                                        "for an independent count of the bytes read (with --summarize-counters)")
     return p.parse_args()
@@ -142,15 +145,17 @@ def summarize_counters(args):
     _, kw = _pick(write, args.kernel)
     f_fetch = CALIB_READ / (sum(cf) / len(cf) * 1024)
     f_write = CALIB_WRITE / (sum(cw) / len(cw) * 1024)
-    fetch_b = sum(kf) / len(kf) * 1024 * f_fetch
-    write_b = sum(kw) / len(kw) * 1024 * f_write
+    k = args.dispatches_per_launch
+    fetch_b = sum(kf) / len(kf) * 1024 * f_fetch * k
+    write_b = sum(kw) / len(kw) * 1024 * f_write * k
     rec = {"op": args.op, "kernel": kname, "sources_sha256_16": sources_digest(args.op),
            "dispatches": [len(kf), len(kw)], "calib_fetch_kib": sum(cf) / len(cf),
            "calib_write_kib": sum(cw) / len(cw), "calib_read_bytes": CALIB_READ,
            "calib_write_bytes": CALIB_WRITE, "scale_fetch": round(f_fetch, 4), "scale_write": round(f_write, 4),
            "kernel_fetch_kib": sum(kf) / len(kf), "kernel_write_kib": sum(kw) / len(kw),
            "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
-           "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b))}
+           "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
+           "dispatches_per_launch": k}
     cfg_arg = f" --config {args.config}" if args.config != 4 else ""
     sizes_arg = f" --sizes-dir {args.sizes_dir}" if args.sizes_dir else ""
     cmd = f"python3 bench.py{cfg_arg} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --configs '' --copy-calib"
@@ -168,8 +173,9 @@ def summarize_counters(args):
             rows.append(f"| {label} | {v[names[0]]:.0f} | {v[names[1]]:.0f} | {v[names[2]]:.0f} | "
                         f"{v[names[3]]:.0f} | {b:.4e} |")
             tag = "calib" if label.startswith("cal") else "kernel"
-            rec["sized_read_bytes_" + tag] = int(round(b))
-            rec["read_requests_" + tag] = int(round(v[names[0]]))
+            per_launch = k if tag == "kernel" else 1   # the op's launch: k dispatches of the kernel
+            rec["sized_read_bytes_" + tag] = int(round(b * per_launch))
+            rec["read_requests_" + tag] = int(round(v[names[0]] * per_launch))
         sizes = f"""
 Cross-check: read requests by size (one more pass), bytes = 32 n32 + 64 n64 + 128 n128:
 
@@ -181,6 +187,10 @@ rocprofv3 --pmc {' '.join(names)} --output-format csv -d {args.sizes_dir} -o siz
 |---|---|---|---|---|---|
 {chr(10).join(rows)}
 """
+    k_arg = f" --dispatches-per-launch {k}" if k != 1 else ""
+    k_note = (f"\nOne launch of the op is {k} dispatches of this kernel (a product over a hub split: the hub pass,\n"
+              f"then the cold pass), so the per-launch figures below are {k} times the per-dispatch means.\n"
+              if k != 1 else "")
     text = f"""# HBM traffic of `{args.op}` from TCC byte counters
 
 Kernel: `{kname}`
@@ -191,8 +201,9 @@ Commands (each a run of its own, from the repository root):
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize_counters[0]} -o fetch -- {cmd}
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize_counters[1]} -o write -- {cmd}
 python3 bench.py{cfg_arg} --summarize-counters {args.summarize_counters[0]} {args.summarize_counters[1]}{sizes_arg} \\
-    --op '{args.op}' --kernel '{args.kernel}' --out {args.out}
+    --op '{args.op}' --kernel '{args.kernel}' --out {args.out}{k_arg}
 ```
+{k_note}
 
 `--copy-calib` runs one identity row gather through the library before the steps:
 {CALIB_ROWS} rows of {CALIB_ROW_BYTES} B, so {CALIB_READ} bytes read (rows + int32 row list) and
@@ -293,8 +304,9 @@ def gather_probe_of(roof, built, sag, torch, reps=5):
             "lines_per_launch": int(n_lines), "G_lines_per_s": round(n_lines / probe_ms / 1e6, 2),
             "kernel_ms": roof["avg_launch_ms"], "probe_over_kernel": round(probe_ms / roof["avg_launch_ms"], 4),
             "note": "the same ids gathered with the SpMM's lane layout and nothing else (over each matrix whose "
-                    "launches make up the op, averaged like the op); probe_over_kernel near 1 means the product "
-                    "runs at the rate the memory system serves these rows"}
+                    "launches make up the op, averaged like the op, in one pass); probe_over_kernel near 1 means "
+                    "the product runs at the rate the memory system serves these rows, above 1 (a matrix with a "
+                    "hub split, two passes) that it beats the one-pass gather"}
 
 
 def graph_stats(A, n_l, torch):
@@ -339,6 +351,13 @@ class Model:
         self.built = sag.csr_build_normalize(s_d, d_d, w.n_global, w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
         sag.csr_schedule(self.built.A, seg_len)
         sag.csr_schedule(self.built.AT, seg_len)
+        # graphs with many entries per row: products in two passes (hub columns, then the rest)
+        self.hub_split = {}
+        for name, M in (("A", self.built.A), ("AT", self.built.AT)):
+            if sag.hub_split_pays(M):
+                sag.csr_hub_split(M, seg_len=seg_len)
+                self.hub_split[name] = {"hub_cols": sag.ops.HUB_COLS,
+                                        "hub_share_of_nnz": round(M.hub_part.nnz / max(M.nnz, 1), 4)}
         torch.cuda.synchronize()
         self.build_ms = (time.perf_counter() - t0) * 1e3
         del s_d, d_d
@@ -935,6 +954,7 @@ def config_run(w, sag, torch, args):
     roof["gather_probe"] = gather_probe_of(roof, m.built, sag, torch) if w.cfg != 1 else None
     out = {"workload": w.name, "config": w.cfg, "dtype": w.dtype, "dims": w.dims, "layer": w.model,
            "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
+           "hub_split": m.hub_split or None,
            "ms_per_step": round(min(ms, g_ms) if g_ms is not None else ms, 4),
            "mode": "graph" if g_ms is not None and g_ms < ms else "eager",
            "step_ms": pct(g_per if g_ms is not None and g_ms < ms else per), "steps": steps,
@@ -1041,6 +1061,7 @@ def run(args, cfgs, jobs):
     conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
             "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion,
+            "hub_split": m.hub_split or None,
             "graph": m.graph_stats}
     build_ms = m.build_ms
     overlap = fused = gat = halo = None

@@ -53,8 +53,9 @@
  *    for the calling thread.  CSR contents (ordering, index ranges) are not
  *    re-validated by compute calls: a CSR that did not come from
  *    sag_csr_build_normalize (or equal one) gives undefined results.
- *  - Every call is asynchronous on `stream` except the two documented as
- *    synchronising (sag_csr_build_normalize and sag_csr_schedule).
+ *  - Every call is asynchronous on `stream` except those documented as
+ *    synchronising (sag_csr_build_normalize and its query, sag_csr_schedule
+ *    and sag_csr_hub_split).
  *  - Results are deterministic: the same inputs, sizes and schedule give
  *    the same bits on every run (no floating-point atomics).
  */
@@ -120,8 +121,21 @@ enum {
  * its pattern and scale each row's sum by that value, once per row instead
  * of once per entry; the result differs from reading the values only by
  * fp32 rounding.  Zero (also for any transpose): the stored values are
- * read. */
-typedef struct {
+ * read.
+ *
+ * hub_part, cold_part (both or neither; host pointers): a hub split of this
+ * matrix (sag_csr_hub_split): two CSRs over the same rows and columns, the
+ * first holding the entries that fall in the columns with the most entries,
+ * the second the rest, each row's entries in their order in this matrix and
+ * with their values (row_mean 0, any schedule of their own).  Products over
+ * a matrix with a split (sag_spmm_csr, sag_spmm_csr_t and the layers) take
+ * two passes: the hub part into fp32 partial rows, whose gathers keep
+ * hitting the same few rows of X and so are served from L2, then the cold
+ * part with each row's partial added to its sum before the epilogue.  The
+ * result differs from the one-pass product only by fp32 summation order.
+ * The split pays on graphs with many entries per row, where the partial
+ * rows cost little next to the gathers they speed up. */
+typedef struct sag_csr {
     int64_t n_rows;
     int64_t n_cols;
     int64_t nnz;
@@ -135,6 +149,8 @@ typedef struct {
     int64_t n_seg;
     int32_t seg_len;
     int32_t row_mean;
+    const struct sag_csr* hub_part;
+    const struct sag_csr* cold_part;
 } sag_csr;
 
 /* ---------------------------------------------------------------------------
@@ -203,6 +219,29 @@ size_t sag_csr_schedule_bytes(int64_t n_rows, int64_t nnz, int32_t seg_len);
 size_t sag_csr_schedule_workspace_bytes(int64_t n_rows);
 sag_status sag_csr_schedule(sag_csr* A, int32_t seg_len, void* buf, size_t buf_bytes,
                             void* ws, size_t ws_bytes, void* stream);
+
+/* Hub split of a CSR (setup, once per matrix; synchronises `stream`).
+ * The hub columns are the n_hub columns holding the most entries of A
+ * (ties to the lower column id; all columns when n_hub >= n_cols).  Writes
+ * two CSRs over A's rows and columns: the hub part (every entry of A in a
+ * hub column) and the cold part (every other entry), each row's entries in
+ * their order in A, values copied with them (values_* NULL when A has
+ * none).  The caller wraps the arrays in two sag_csr structs (row_mean 0,
+ * optionally scheduled with sag_csr_schedule) and attaches them to A's
+ * hub_part and cold_part; nothing else of A changes.
+ * Outputs (device, capacities in entries): indptr_hub, indptr_cold
+ * [n_rows + 1]; indices_hub, values_hub [cap_hub]; indices_cold,
+ * values_cold [cap_cold].  *nnz_hub (host) receives the hub part's entry
+ * count (the cold part has nnz - *nnz_hub).  A part larger than its
+ * capacity returns SAG_E_WORKSPACE with *nnz_hub set and outputs
+ * unspecified; cap = nnz always suffices.  A with row_mean set must store
+ * its values (the parts carry them).  ws: sag_csr_hub_split_workspace_bytes
+ * bytes. */
+size_t sag_csr_hub_split_workspace_bytes(int64_t n_rows, int64_t n_cols);
+sag_status sag_csr_hub_split(const sag_csr* A, int64_t n_hub,
+                             int64_t cap_hub, int64_t* indptr_hub, int32_t* indices_hub, float* values_hub,
+                             int64_t cap_cold, int64_t* indptr_cold, int32_t* indices_cold, float* values_cold,
+                             int64_t* nnz_hub /* host */, void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * Halo gather -- the DIGEST "pull": dst[k, :] = src[rows[k] - row_base, :]
@@ -311,8 +350,10 @@ sag_status sag_spmm_csr_t(const sag_csr* AT, const void* X, int64_t ldx, sag_dty
  * before any launch.  Every call on one GPU shares that GPU's array, so
  * calls that overlap on one GPU (different streams, or threads) race; calls
  * ordered on one stream do not.  Nothing in the array needs clearing: each
- * call writes every partial it reads.  Results are bitwise those of
- * sag_spmm_csr. */
+ * call writes every partial it reads.  A matrix with a hub split is
+ * multiplied here in one pass over its own arrays (its parts are not used),
+ * so results are bitwise those of sag_spmm_csr on the same matrix without
+ * the split. */
 size_t sag_spmm_noalloc_scratch_bytes(void);
 sag_status sag_spmm_csr_noalloc(const sag_csr* A, const void* X, int64_t ldx, sag_dtype xt, int64_t d,
                                 void* Y, int64_t ldy, sag_dtype yt,
@@ -338,7 +379,9 @@ sag_status sag_spmm_csr_noalloc(const sag_csr* A, const void* X, int64_t ldx, sa
  * aggregate -> transform kernel (sag_aggregate_transform) where it applies
  * (the layer aggregates first and the widths fit); otherwise, and by
  * default (0), the separate SpMM and product run.  Both give the same
- * results up to fp32 summation order.  Unknown bits return SAG_E_INVALID.
+ * results up to fp32 summation order (the fused kernel reads A's own arrays,
+ * so it takes no hub split into account).  Unknown bits return
+ * SAG_E_INVALID.
  *
  * Widths.  The SpMM width min(d_in, d_out) is at most 1024 (fp32) or 2048
  * (bf16).  The dense products keep their weight slice in LDS, so the K of

@@ -31,6 +31,7 @@ class SagCsr(ctypes.Structure):
         ("sched", vp),
         ("n_short", i64), ("n_medium", i64), ("n_long", i64), ("n_seg", i64),
         ("seg_len", i32), ("row_mean", i32),
+        ("hub_part", vp), ("cold_part", vp),
     ]
 
 
@@ -45,6 +46,8 @@ SIGNATURES = {
     "sag_csr_schedule_bytes": (sz, [i64, i64, i32]),
     "sag_csr_schedule_workspace_bytes": (sz, [i64]),
     "sag_csr_schedule": (cint, [PCSR, i32, vp, sz, vp, sz, vp]),
+    "sag_csr_hub_split_workspace_bytes": (sz, [i64, i64]),
+    "sag_csr_hub_split": (cint, [PCSR, i64, i64, vp, vp, vp, i64, vp, vp, vp, P(i64), vp, sz, vp]),
     "sag_halo_gather": (cint, [vp, i64, vp, i64, i64, i64, cint, vp, i64, vp]),
     "sag_halo_push": (cint, [vp, i64, vp, i64, i64, i64, cint, cint, vp, i64, i64, vp]),
     "sag_code_row_bytes": (sz, [i64, cint]),

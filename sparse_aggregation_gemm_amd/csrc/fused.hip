@@ -395,7 +395,7 @@ size_t agg_transform_ws_bytes(const sag_csr& A, int64_t d_in, int64_t d_out, boo
     c.take<uint4>(static_cast<size_t>(pl.kgroups) * pl.NB * 64);
     if (A.sched && A.n_long > 0) {
         c.take<char>(dense_bytes(A.n_long, d_in, dt));
-        c.take<char>(spmm_ws_bytes(A, d_in));
+        c.take<char>(spmm_long_ws_bytes(A, d_in));
     }
     return c.used();
 }
@@ -426,7 +426,7 @@ sag_status run_typed(const sag_csr& A, const void* H_ext, int64_t ldh, int64_t d
     const int64_t ldzl = ldv(d_in, dt);
     if (has_long) {
         zl = c.take<char>(dense_bytes(A.n_long, d_in, dt));
-        sws_bytes = spmm_ws_bytes(A, d_in);
+        sws_bytes = spmm_long_ws_bytes(A, d_in);
         sws = c.take<char>(sws_bytes);
     }
     if (!c.fits()) return fail(SAG_E_WORKSPACE, "aggregate_transform: workspace too small");

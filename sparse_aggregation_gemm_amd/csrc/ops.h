@@ -18,6 +18,9 @@ struct Epilogue {
     void* pre = nullptr;            // output type, same ld as the output; nullable
     int row_mean = 0;               // SpMM: every value of row r is 1/len(r) (the mean
                                     // normalisation): values not read, each row's sum scaled
+    const float* part = nullptr;    // SpMM: fp32 partial rows (ld ld_part) of the same product
+    int64_t ld_part = 0;            // over the other part of a hub split, added to each row's
+                                    // sum before everything else
 };
 
 // Leading dimension of the library's own dense buffers: rows wider than 64
@@ -39,6 +42,8 @@ inline size_t dense_bytes(int64_t rows, int64_t d, sag_dtype dt) {
 // ---- SpMM ----------------------------------------------------------------------
 // Y[r, :d] = sum_p val[p] X[idx[p], :d]  for every row of A, with the epilogue.
 size_t spmm_ws_bytes(const sag_csr& A, int64_t d);
+// Long-row partials of a one-pass product over A's own arrays.
+size_t spmm_long_ws_bytes(const sag_csr& A, int64_t d);
 sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
                     int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, size_t ws_bytes,
                     hipStream_t s);

@@ -18,6 +18,13 @@
 // handed to the group that needs them with lane shuffles, so each lane keeps
 // several independent 16-byte loads in flight.  Accumulation is fp32 in a
 // fixed order, so results are bitwise reproducible.
+//
+// A matrix with a hub split takes two passes: its hub part (the entries in
+// the few columns holding the most entries) into fp32 partial rows, then its
+// cold part, each row adding its partial before the epilogue.  During the
+// first pass every gather lands on the same few rows of X, which stay in L2;
+// on graphs with hundreds of entries per row that outweighs writing and
+// reading the partial rows.
 #include <mutex>
 
 #include "ops.h"
@@ -43,6 +50,8 @@ struct EpiArgs {
     int relu;
     int d;
     int row_mean;   // scale each row's sum by 1/len (values not read)
+    const float* part;   // fp32 partial rows added to the sums first (or null)
+    int64_t ld_part;
 };
 
 template <class XT, class YT>
@@ -99,6 +108,21 @@ __device__ __forceinline__ void epi_store(const EpiArgs<YT>& e, int64_t row, int
     if (col0 >= e.d) return;
     const int n = min(V, e.d - col0);
     constexpr int VY = Vec<YT>::N;
+    if (e.part) {
+        // the partial row of the hub pass, read here rather than with the
+        // addend so that products without one hold no registers for it
+        // (whole 16-byte vectors: ld_part is a multiple of 8; one at a time)
+#pragma unroll 1
+        for (int q = 0; q < V; q += 4) {
+            if (col0 + q < e.d) {
+                const float4 t = *reinterpret_cast<const float4*>(e.part + row * e.ld_part + col0 + q);
+                a[q] += t.x;
+                a[q + 1] += t.y;
+                a[q + 2] += t.z;
+                a[q + 3] += t.w;
+            }
+        }
+    }
     if (e.row_mean && len > 0) {
         // the value the mean normalisation stores, 1/len rounded once
         const float rs = 1.f / static_cast<float>(len);
@@ -366,6 +390,8 @@ sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, vo
     p.e.relu = epi.relu;
     p.e.d = static_cast<int>(d);
     p.e.row_mean = epi.row_mean;
+    p.e.part = epi.part;
+    p.e.ld_part = epi.ld_part;
     const int C = p.C;
     if (C <= 4) return launch_bins<XT, YT, 4, 1>(A, p, s, long_only);
     if (C <= 8) return launch_bins<XT, YT, 8, 1>(A, p, s, long_only);
@@ -383,7 +409,7 @@ sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, vo
 sag_status spmm_long_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype dt, int64_t d, void* Y, int64_t ldy,
                          void* ws, size_t ws_bytes, hipStream_t s) {
     if (!A.sched || A.n_long == 0 || d == 0) return SAG_OK;
-    if (ws_bytes < spmm_ws_bytes(A, d) || !ws) return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
+    if (ws_bytes < spmm_long_ws_bytes(A, d) || !ws) return fail(SAG_E_WORKSPACE, "spmm: workspace too small");
     Epilogue e;
     e.row_mean = A.row_mean != 0;
     if (dt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, e, ws, s, true);
@@ -406,13 +432,44 @@ sag_status check_csr(const char* name, const sag_csr* A) {
             return fail(SAG_E_INVALID, n + ": inconsistent long-row schedule");
         if (!aligned16(A->sched)) return fail(SAG_E_ALIGN, n + ": schedule not 16-B aligned");
     }
+    if (A->hub_part || A->cold_part) {
+        if (!A->hub_part || !A->cold_part) return fail(SAG_E_INVALID, n + ": a hub split needs both parts");
+        for (const sag_csr* P : {A->hub_part, A->cold_part}) {
+            if (P->hub_part || P->cold_part) return fail(SAG_E_INVALID, n + ": a part of a hub split has a split");
+            SAG_TRY(check_csr(name, P));
+            if (P->n_rows != A->n_rows || P->n_cols != A->n_cols)
+                return fail(SAG_E_INVALID, n + ": the parts of a hub split must have the matrix's shape");
+            if (P->row_mean) return fail(SAG_E_INVALID, n + ": the parts of a hub split carry their values (row_mean 0)");
+            if (A->values && P->nnz > 0 && !P->values)
+                return fail(SAG_E_INVALID, n + ": the parts of a matrix with values must carry them");
+        }
+        if (A->hub_part->nnz + A->cold_part->nnz != A->nnz)
+            return fail(SAG_E_INVALID, n + ": the parts of a hub split must hold the matrix's entries");
+        if (A->row_mean && !A->values)
+            return fail(SAG_E_INVALID, n + ": a row_mean matrix with a hub split must store its values");
+    }
     return SAG_OK;
 }
 
-size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
+size_t spmm_long_ws_bytes(const sag_csr& A, int64_t d) {
     if (!A.sched || A.n_long == 0) return 0;
     const int64_t C = cdiv(d, 4);   // fp32 partials: C4 = ceil(d / 4) float4 vectors at most
     return static_cast<size_t>(A.n_seg) * static_cast<size_t>(round_up(C * 4, 8)) * sizeof(float);
+}
+
+// fp32 partial rows of a split product: round_up(d, 8) floats per row, so
+// that the epilogue reads them as whole 16-byte vectors
+static int64_t part_ld(int64_t d) { return round_up(d > 0 ? d : 1, 8); }
+static size_t part_bytes(const sag_csr& A, int64_t d) {
+    return static_cast<size_t>(round_up(A.n_rows * part_ld(d) * static_cast<int64_t>(sizeof(float)), 256));
+}
+
+size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
+    if (A.hub_part && A.cold_part) {
+        const size_t h = spmm_long_ws_bytes(*A.hub_part, d), c = spmm_long_ws_bytes(*A.cold_part, d);
+        return part_bytes(A, d) + (h > c ? h : c);
+    }
+    return spmm_long_ws_bytes(A, d);
 }
 
 namespace {
@@ -443,7 +500,17 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
                                                   A.n_rows, A.nnz, d)
                                      : std::string(),
                      s, bytes, 2 * A.nnz * d);
-    return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
+    if (!(A.hub_part && A.cold_part)) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
+    // hub pass into fp32 partial rows (the parts carry their values), then
+    // the cold pass with the partials added before the caller's epilogue
+    float* P = static_cast<float*>(ws);
+    void* ws2 = static_cast<char*>(ws) + part_bytes(A, d);
+    SAG_TRY(spmm_dispatch(*A.hub_part, X, ldx, xt, d, P, part_ld(d), SAG_F32, Epilogue{}, ws2, s));
+    Epilogue e2 = epi;
+    e2.row_mean = 0;
+    e2.part = P;
+    e2.ld_part = part_ld(d);
+    return spmm_dispatch(*A.cold_part, X, ldx, xt, d, Y, ldy, yt, e2, ws2, s);
 }
 
 }  // namespace sag
@@ -542,7 +609,7 @@ extern "C" sag_status sag_spmm_csr_noalloc(const sag_csr* A, const void* X, int6
                                            void* Y, int64_t ldy, sag_dtype yt, const void* addend,
                                            int64_t ld_add, int64_t n_add, void* stream) {
     SAG_TRY(spmm_check("spmm_csr_noalloc", A, X, ldx, xt, d, Y, ldy, yt, addend, ld_add, n_add));
-    const size_t need = spmm_ws_bytes(*A, d);
+    const size_t need = spmm_long_ws_bytes(*A, d);   // one pass: a hub split is not used here
     if (need > kScratchBytes)
         return fail(SAG_E_WORKSPACE, "spmm_csr_noalloc: the long rows' partial sums need " + std::to_string(need) +
                                          " bytes, above the fixed scratch of " + std::to_string(kScratchBytes) +

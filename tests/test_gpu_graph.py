@@ -27,13 +27,16 @@ class Pass:
     same values); layer l writes its output into the local rows of layer
     l + 1's input."""
 
-    def __init__(self, w, dt, dims, relu, seed):
+    def __init__(self, w, dt, dims, relu, seed, hub_cols=None):
         src, dst = w.edges
         norm = "gcn" if w.model == "gcn" else "mean"
         self.b = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, w.lo, w.hi, w.symmetrize,
                                          w.self_loops, norm)
         sag.csr_schedule(self.b.A, 256)
         sag.csr_schedule(self.b.AT, 256)
+        if hub_cols:
+            sag.csr_hub_split(self.b.A, hub_cols, 256)
+            sag.csr_hub_split(self.b.AT, hub_cols, 256)
         A = self.b.A
         self.n_l, self.n_ext = A.n_rows, A.n_cols
         self.n_h = self.n_ext - self.n_l
@@ -134,3 +137,11 @@ def test_tiny_gcn_f32():
     w = gen.make_config(1, 1.0)
     say("graph capture: tiny gcn f32")
     check_graph(Pass(w, "f32", [64, 16], [True], seed=5))
+
+
+def test_dense_gcn_over_hub_split_f32():
+    """The dense power-law graph's GCN with both matrices split: every
+    product takes two passes through the partial rows in the workspace."""
+    w = gen.make_config(2, 0.004)
+    say("graph capture: dense gcn over a hub split f32")
+    check_graph(Pass(w, "f32", [64, 32, 16], [True, False], seed=6, hub_cols=100))

@@ -31,7 +31,7 @@ def _bits_or_f32(x, dt):
 
 
 def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_out, relu,
-             stale_rows=0, stale_base=0, seed=0, seg_len=256, label="", fused=False):
+             stale_rows=0, stale_base=0, seed=0, seg_len=256, label="", fused=False, hub_cols=None):
     g = np.random.default_rng(seed)
     n_l = hi - lo
     say(f"layer {label} model={model} dt={dt} n_global={n_global} [{lo},{hi}) {d_in}->{d_out}")
@@ -51,6 +51,10 @@ def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_ou
     if seg_len:
         sag.csr_schedule(gb.A, seg_len)
         sag.csr_schedule(gb.AT, seg_len)
+    if hub_cols:
+        # both products of the layer take two passes (hub part, cold part)
+        sag.csr_hub_split(gb.A, hub_cols, seg_len or 1024)
+        sag.csr_hub_split(gb.AT, hub_cols, seg_len or 1024)
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     H_ext = sag.empty_dense(n_l + n_h, d_in, tdt, DEV)
     H_ext[:n_l].copy_(to_dev_dense(H_loc, dt))
@@ -109,6 +113,26 @@ def test_power_law_gcn_layers(d_in, d_out, relu):
     src, dst = w.edges
     run_case("gcn", "f32", src, dst, w.n_global, 0, w.n_global, True, True, "gcn", d_in, d_out, relu,
              seed=d_in, label="power-law GCN")
+
+
+@pytest.mark.parametrize("hub_cols", [1, 64, 700])
+@pytest.mark.parametrize("model,dt,d_in,d_out,relu", [("gcn", "f32", 602, 128, True), ("gcn", "f32", 128, 41, False),
+                                                      ("sage", "bf16", 100, 256, True), ("sage", "f32", 256, 47, False)])
+def test_layers_over_hub_split(hub_cols, model, dt, d_in, d_out, relu):
+    """The dense power-law graph with both of the layer's matrices split
+    (the SAGE cases: the mean-normalised A, whose parts carry its values)."""
+    w = gen.make_config(2, 0.004)
+    src, dst = w.edges
+    run_case(model, dt, src, dst, w.n_global, 0, w.n_global, True, True, "gcn" if model == "gcn" else "mean",
+             d_in, d_out, relu, seed=hub_cols + d_in, seg_len=128, label="hub split", hub_cols=hub_cols)
+
+
+def test_partition_with_halo_over_hub_split():
+    w = gen.make_config(3, 1 / 64)
+    src, dst = w.edges
+    run_case("sage", "f32", src, dst, w.n_global, w.lo, w.hi, True, False, "mean", 64, 96, True,
+             stale_rows=w.stale_rows, stale_base=w.stale_base, seed=5, seg_len=64, label="partition hub split",
+             hub_cols=300)
 
 
 def test_rmat_partition_sage_with_stale_halo():
