@@ -53,7 +53,7 @@ CALIB_KERNEL = "gather_rows<32>"   # the 512-byte-row instance
 CSRC = os.path.join(ROOT, "sparse_aggregation_gemm_amd", "csrc")
 # sources whose text decides each op family's kernels (a counter summary is
 # valid only for the sources it was taken on)
-OP_SOURCES = {"spmm": ["spmm.hip", "rowsum.h", "common.h", "ops.h"], "gemm_nn": ["gemm.hip", "common.h", "ops.h"],
+OP_SOURCES = {"spmm": ["spmm.hip", "rowsum.h", "common.h", "ops.h", "split.hip"], "gemm_nn": ["gemm.hip", "common.h", "ops.h"],
               "gemm_tn": ["gemm.hip", "common.h", "ops.h"], "gather": ["gather.hip", "common.h"]}
 
 
