@@ -356,8 +356,9 @@ class Model:
         for name, M in (("A", self.built.A), ("AT", self.built.AT)):
             if sag.hub_split_pays(M):
                 sag.csr_hub_split(M, seg_len=seg_len)
-                self.hub_split[name] = {"hub_cols": sag.ops.HUB_COLS,
-                                        "hub_share_of_nnz": round(M.hub_part.nnz / max(M.nnz, 1), 4)}
+                chain = sag.hub_chain(M)
+                self.hub_split[name] = {"cols_per_group": sag.ops.HUB_COLS, "groups": len(chain) - 1,
+                                        "share_of_nnz": [round(c / max(M.nnz, 1), 4) for c in chain]}
         torch.cuda.synchronize()
         self.build_ms = (time.perf_counter() - t0) * 1e3
         del s_d, d_d

@@ -132,6 +132,9 @@ enum {
  * two passes: the hub part into fp32 partial rows, whose gathers keep
  * hitting the same few rows of X and so are served from L2, then the cold
  * part with each row's partial added to its sum before the epilogue.  The
+ * cold part may carry a split of its own (the next-busiest columns; the hub
+ * part may not), so a chain of hub sets, each small enough for L2, takes one
+ * pass each, every pass adding the previous partial rows to its own.  The
  * result differs from the one-pass product only by fp32 summation order.
  * The split pays on graphs with many entries per row, where the partial
  * rows cost little next to the gathers they speed up. */

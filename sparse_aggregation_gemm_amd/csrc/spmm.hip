@@ -434,8 +434,9 @@ sag_status check_csr(const char* name, const sag_csr* A) {
     }
     if (A->hub_part || A->cold_part) {
         if (!A->hub_part || !A->cold_part) return fail(SAG_E_INVALID, n + ": a hub split needs both parts");
+        if (A->hub_part->hub_part || A->hub_part->cold_part)
+            return fail(SAG_E_INVALID, n + ": the hub part of a hub split has a split (only the cold part may)");
         for (const sag_csr* P : {A->hub_part, A->cold_part}) {
-            if (P->hub_part || P->cold_part) return fail(SAG_E_INVALID, n + ": a part of a hub split has a split");
             SAG_TRY(check_csr(name, P));
             if (P->n_rows != A->n_rows || P->n_cols != A->n_cols)
                 return fail(SAG_E_INVALID, n + ": the parts of a hub split must have the matrix's shape");
@@ -464,9 +465,11 @@ static size_t part_bytes(const sag_csr& A, int64_t d) {
     return static_cast<size_t>(round_up(A.n_rows * part_ld(d) * static_cast<int64_t>(sizeof(float)), 256));
 }
 
+// A split matrix: its partial rows, then what its hub pass and the product
+// over its cold part (which may carry a split of its own) need.
 size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
     if (A.hub_part && A.cold_part) {
-        const size_t h = spmm_long_ws_bytes(*A.hub_part, d), c = spmm_long_ws_bytes(*A.cold_part, d);
+        const size_t h = spmm_long_ws_bytes(*A.hub_part, d), c = spmm_ws_bytes(*A.cold_part, d);
         return part_bytes(A, d) + (h > c ? h : c);
     }
     return spmm_long_ws_bytes(A, d);
@@ -484,6 +487,27 @@ sag_status spmm_dispatch(const sag_csr& A, const void* X, int64_t ldx, sag_dtype
 
 }  // namespace
 
+// The product over A with epi (whose partial rows, if any, come from an
+// earlier pass).  A split matrix: its hub pass into fp32 partial rows (the
+// parts carry their values; an incoming partial is added there), then the
+// product over its cold part with those rows added before the epilogue;
+// the cold part may itself be split, one level further into the workspace.
+static sag_status spmm_chain(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
+                             int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s) {
+    if (!(A.hub_part && A.cold_part)) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
+    float* P = static_cast<float*>(ws);
+    void* ws2 = static_cast<char*>(ws) + part_bytes(A, d);
+    Epilogue e1;
+    e1.part = epi.part;
+    e1.ld_part = epi.ld_part;
+    SAG_TRY(spmm_dispatch(*A.hub_part, X, ldx, xt, d, P, part_ld(d), SAG_F32, e1, ws2, s));
+    Epilogue e2 = epi;
+    e2.row_mean = 0;
+    e2.part = P;
+    e2.ld_part = part_ld(d);
+    return spmm_chain(*A.cold_part, X, ldx, xt, d, Y, ldy, yt, e2, ws2, s);
+}
+
 sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
                     int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, size_t ws_bytes,
                     hipStream_t s) {
@@ -500,17 +524,7 @@ sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, 
                                                   A.n_rows, A.nnz, d)
                                      : std::string(),
                      s, bytes, 2 * A.nnz * d);
-    if (!(A.hub_part && A.cold_part)) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
-    // hub pass into fp32 partial rows (the parts carry their values), then
-    // the cold pass with the partials added before the caller's epilogue
-    float* P = static_cast<float*>(ws);
-    void* ws2 = static_cast<char*>(ws) + part_bytes(A, d);
-    SAG_TRY(spmm_dispatch(*A.hub_part, X, ldx, xt, d, P, part_ld(d), SAG_F32, Epilogue{}, ws2, s));
-    Epilogue e2 = epi;
-    e2.row_mean = 0;
-    e2.part = P;
-    e2.ld_part = part_ld(d);
-    return spmm_dispatch(*A.cold_part, X, ldx, xt, d, Y, ldy, yt, e2, ws2, s);
+    return spmm_chain(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
 }
 
 }  // namespace sag

@@ -212,13 +212,17 @@ def csr_schedule(A: Csr, seg_len: int = 1024) -> Csr:
     return A
 
 
-# A hub split pays where rows hold many entries: the fp32 partial rows it
-# writes and reads back then cost little next to the gathers it moves into L2
-# (measured: 493 entries per row, two-pass products 13-19% faster; 51 entries
-# per row, 10% slower).  The hub set is sized so that its rows fit a few
-# megabytes at the widths the workloads use.
+# A hub split pays where rows hold many entries: the fp32 partial rows each
+# pass writes and the next reads back then cost little next to the gathers
+# they move into L2 (measured: 493 entries per row, products 35% faster over
+# a chain of twelve 12,288-column groups; 51 entries per row, one 16,384-
+# column group already 10% slower).  A group of 12,288 rows of X is 3-6 MB
+# at the widths the workloads use, about one XCD's L2.  The chain goes on
+# while the last group held at least 2% of the matrix's entries.
 HUB_SPLIT_MIN_ENTRIES_PER_ROW = 128
-HUB_COLS = 16384
+HUB_COLS = 12288
+HUB_MIN_SHARE = 0.02
+HUB_MAX_LEVELS = 32
 
 
 def hub_split_pays(A: Csr) -> bool:
@@ -226,14 +230,44 @@ def hub_split_pays(A: Csr) -> bool:
     return A.n_rows > 0 and A.nnz >= HUB_SPLIT_MIN_ENTRIES_PER_ROW * A.n_rows and A.n_cols > 2 * HUB_COLS
 
 
-def csr_hub_split(A: Csr, n_hub: int = HUB_COLS, seg_len: int | None = None) -> Csr:
+def csr_hub_split(A: Csr, n_hub: int = HUB_COLS, seg_len: int | None = None, levels: int | None = None) -> Csr:
     """sag_csr_hub_split: split A's entries into those of the n_hub columns
     holding the most entries and the rest, schedule both parts (seg_len:
     A's own when it has a schedule, else 1024) and attach them to A (in
-    place).  Products over A then take two passes.  Synchronises the current
-    stream."""
+    place); then split the cold part the same way, and so on: `levels`
+    times, or (None) while the last hub part held at least HUB_MIN_SHARE of
+    A's entries (at most HUB_MAX_LEVELS).  Products over A take one pass per
+    hub part plus one.  Synchronises the current stream."""
     if A.hub_part is not None:
         raise ValueError("the matrix already has a hub split")
+    if levels is not None and levels < 1:
+        raise ValueError("levels must be at least 1")
+    M, k = A, 0
+    while True:
+        _split_once(M, n_hub, seg_len)
+        k += 1
+        if levels is not None:
+            if k >= levels:
+                break
+        elif M.hub_part.nnz < HUB_MIN_SHARE * A.nnz or k >= HUB_MAX_LEVELS:
+            break
+        M = M.cold_part
+        if M.nnz == 0:
+            break
+    return A
+
+
+def hub_chain(A: Csr) -> list:
+    """The entry counts of A's hub parts, first to last, and of its final
+    cold part (empty when A has no split)."""
+    out, M = [], A
+    while M.hub_part is not None:
+        out.append(M.hub_part.nnz)
+        M = M.cold_part
+    return out + [M.nnz] if out else []
+
+
+def _split_once(A: Csr, n_hub: int, seg_len: int | None) -> None:
     lib = L.lib()
     dev = A.device
     cap = max(A.nnz, 1)
@@ -252,13 +286,13 @@ def csr_hub_split(A: Csr, n_hub: int = HUB_COLS, seg_len: int | None = None) -> 
     L.check("sag_csr_hub_split", st)
     nh = nh.value
     for (ip, ix, vv), k in zip(bufs, (nh, A.nnz - nh)):
-        P = Csr(A.n_rows, A.n_cols, ip, ix[:k], vv[:k] if vv is not None else None)
+        # exact-size copies, so that the parts hold no spare capacity
+        P = Csr(A.n_rows, A.n_cols, ip, ix[:k].clone(), vv[:k].clone() if vv is not None else None)
         csr_schedule(P, seg_len or (A.raw.seg_len if A.sched is not None else 1024))
         parts.append(P)
     A.hub_part, A.cold_part = parts
     A.raw.hub_part = ctypes.addressof(parts[0].raw)
     A.raw.cold_part = ctypes.addressof(parts[1].raw)
-    return A
 
 
 def csr_info(A: Csr) -> dict:

@@ -1,4 +1,4 @@
-"""Hub split of a CSR and the two-pass products over it.
+"""Hub split of a CSR (one level or a chain) and the products over it.
 
 The split's structure is checked against its definition on the host: the
 hub columns are the n_hub columns holding the most entries (ties to the
@@ -8,7 +8,8 @@ over a split matrix are compared with the oracle (the same bounds as the
 one-pass SpMM), bit for bit with exact sums on small-integer data, with
 the one-pass product on every edge case of the split (one hub column,
 every column a hub, rows with entries in one part only, rows longer than a
-segment), and with themselves for determinism."""
+segment), and with themselves for determinism.  A chain splits each cold
+part again: every level's hub columns are the busiest of what remains."""
 import numpy as np
 import pytest
 import torch
@@ -59,24 +60,45 @@ def _check_structure(A, n_hub):
 def test_split_structure(n_hub, cfg, scale, norm):
     w, _, _, gb = _built(cfg, scale, norm)
     say(f"hub split structure cfg={cfg} n_hub={n_hub}")
-    sag.csr_hub_split(gb.A, n_hub, 64)
+    sag.csr_hub_split(gb.A, n_hub, 64, levels=1)
     _check_structure(gb.A, min(n_hub, gb.A.n_cols))
-    sag.csr_hub_split(gb.AT, n_hub, 64)
+    sag.csr_hub_split(gb.AT, n_hub, 64, levels=1)
     _check_structure(gb.AT, min(n_hub, gb.AT.n_cols))
 
 
-@pytest.mark.parametrize("n_hub", [16, 300])
+@pytest.mark.parametrize("levels", [3, None])
+def test_chain_structure(levels):
+    """Each level of a chain is the split of the previous level's cold part."""
+    w, _, _, gb = _built(2, 0.004, "gcn", transpose=False)
+    say(f"hub chain structure levels={levels}")
+    sag.csr_hub_split(gb.A, 40, 64, levels=levels)
+    chain = sag.hub_chain(gb.A)
+    assert sum(chain) == gb.A.nnz and len(chain) >= 2
+    if levels:
+        assert len(chain) == levels + 1
+    else:
+        # the automatic depth stops after the first group under 2% of the
+        # entries (or when nothing is left to split)
+        assert chain[-2] < 0.02 * gb.A.nnz or chain[-1] == 0
+        assert all(c >= 0.02 * gb.A.nnz for c in chain[:-2])
+    M = gb.A
+    while M.hub_part is not None:
+        _check_structure(M, min(40, M.n_cols))
+        M = M.cold_part
+
+
+@pytest.mark.parametrize("n_hub,levels", [(16, 1), (300, 1), (30, 5), (60, None)])
 @pytest.mark.parametrize("dt,out_dt", [("f32", "f32"), ("bf16", "bf16"), ("bf16", "f32")])
 @pytest.mark.parametrize("d", [1, 41, 128, 256])
-def test_two_pass_spmm_against_oracle(n_hub, dt, out_dt, d):
+def test_two_pass_spmm_against_oracle(n_hub, levels, dt, out_dt, d):
     w, src, dst, gb = _built(2, 0.004, "gcn")
     sag.csr_schedule(gb.A, 128)
-    sag.csr_hub_split(gb.A, n_hub, 128)
+    sag.csr_hub_split(gb.A, n_hub, 128, levels=levels)
     ob = ocsr.build(src, dst, w.n_global, 0, w.n_global, True, True, "gcn")
     X = gen.normal_f32((ob.A.n_cols, d), np.random.default_rng(d + n_hub))
     Xd = to_dev_dense(X if dt == "f32" else gen.f32_to_bf16_bits(X), dt)
     X64 = f64(Xd)
-    say(f"two-pass spmm n_hub={n_hub} {dt}->{out_dt} d={d}")
+    say(f"two-pass spmm n_hub={n_hub} levels={levels} {dt}->{out_dt} d={d}")
     Y = sag.spmm_csr(gb.A, Xd, out_dtype=torch.float32 if out_dt == "f32" else torch.bfloat16)
     ref = native.spmm(ob.A.indptr, ob.A.indices, ob.A.values, X64)
     den = native.spmm(ob.A.indptr, ob.A.indices, ob.A.values, np.abs(X64), abs_mode=True)
@@ -91,7 +113,7 @@ def test_two_pass_addend_epilogue_and_transpose():
     w, src, dst, gb = _built(2, 0.004, "mean")
     for M in (gb.A, gb.AT):
         sag.csr_schedule(M, 64)
-        sag.csr_hub_split(M, 100, 64)
+        sag.csr_hub_split(M, 100, 64, levels=3)
     ob = ocsr.build(src, dst, w.n_global, 0, w.n_global, True, True, "mean")
     g = np.random.default_rng(2)
     n, d = gb.A.n_rows, 40
@@ -113,19 +135,19 @@ def test_two_pass_addend_epilogue_and_transpose():
     assert abs(np.sum(Yv * AX) - np.sum(ATY * X)) <= 1e-5 * np.sum(np.abs(Yv) * f64(sag.spmm_csr(gb.A, to_dev_dense(np.abs(X)))))
 
 
-@pytest.mark.parametrize("n_hub", [1, 5, 250, 10 ** 6])
+@pytest.mark.parametrize("n_hub,levels", [(1, 1), (5, 1), (250, 1), (10 ** 6, 1), (1, 6), (50, None)])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_two_pass_exact_small_integers(n_hub, dt):
+def test_two_pass_exact_small_integers(n_hub, levels, dt):
     """Values 1 (no normalisation) and integer features: every sum is exact,
     so the two-pass product equals the exact result bit for bit, whatever the
     split (one hub column, a few, every column)."""
     w, src, dst, gb = _built(2, 0.004, "none", transpose=False)
     sag.csr_schedule(gb.A, 64)
-    sag.csr_hub_split(gb.A, n_hub, 64)
+    sag.csr_hub_split(gb.A, n_hub, 64, levels=levels)
     ob = ocsr.build(src, dst, w.n_global, 0, w.n_global, True, True, "none")
     X = np.random.default_rng(n_hub).integers(-8, 9, (gb.A.n_cols, 72)).astype(np.float32)
     Xd = to_dev_dense(X if dt == "f32" else gen.f32_to_bf16_bits(X), dt)
-    say(f"two-pass exact n_hub={n_hub} dt={dt}")
+    say(f"two-pass exact n_hub={n_hub} levels={levels} dt={dt}")
     Y = sag.spmm_csr(gb.A, Xd, out_dtype=torch.float32)
     ref = native.spmm(ob.A.indptr, ob.A.indices, ob.A.values, X.astype(np.float64))
     assert np.array_equal(f64(Y), ref)
@@ -141,8 +163,9 @@ def test_two_pass_long_rows_and_one_part_rows(dt):
     dst = np.concatenate([np.full(n - 10, c, np.int32) for c in (0, 1, 2)] + [g.integers(3, n - 50, 20000).astype(np.int32)])
     gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 0, n, False, False, "none", transpose=False)
     sag.csr_schedule(gb.A, 64)
-    sag.csr_hub_split(gb.A, 900, 64)
+    sag.csr_hub_split(gb.A, 900, 64, levels=2)
     assert sag.csr_info(gb.A.hub_part)["n_long"] > 0 and sag.csr_info(gb.A.cold_part)["n_long"] > 0
+    assert sag.csr_info(gb.A.cold_part.cold_part)["n_long"] > 0
     ip = gb.A.indptr.cpu().numpy()
     assert np.any(np.diff(ip) == 0)
     ob = ocsr.build(src, dst, n, 0, n, False, False, "none")
@@ -163,7 +186,7 @@ def test_two_pass_deterministic_and_noalloc_one_pass():
     X = to_dev_dense(gen.normal_f32((gb.A.n_cols, 100), np.random.default_rng(0)))
     say("two-pass determinism / noalloc")
     one = sag.spmm_csr(gb.A, X)
-    sag.csr_hub_split(gb.A, 200, 64)
+    sag.csr_hub_split(gb.A, 100, 64)
     a = sag.spmm_csr(gb.A, X)
     b = sag.spmm_csr(gb.A, X)
     assert torch.equal(a, b)
