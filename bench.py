@@ -188,8 +188,8 @@ rocprofv3 --pmc {' '.join(names)} --output-format csv -d {args.sizes_dir} -o siz
 {chr(10).join(rows)}
 """
     k_arg = f" --dispatches-per-launch {k}" if k != 1 else ""
-    k_note = (f"\nOne launch of the op is {k} dispatches of this kernel (a product over a hub split: the hub pass,\n"
-              f"then the cold pass), so the per-launch figures below are {k} times the per-dispatch means.\n"
+    k_note = (f"\nOne launch of the op is {k} dispatches of this kernel (a product over a hub split: its hub\n"
+              f"passes, then the cold pass), so the per-launch figures below are {k} times the per-dispatch means.\n"
               if k != 1 else "")
     text = f"""# HBM traffic of `{args.op}` from TCC byte counters
 
