@@ -465,14 +465,27 @@ static size_t part_bytes(const sag_csr& A, int64_t d) {
     return static_cast<size_t>(round_up(A.n_rows * part_ld(d) * static_cast<int64_t>(sizeof(float)), 256));
 }
 
-// A split matrix: its partial rows, then what its hub pass and the product
-// over its cold part (which may carry a split of its own) need.
+// Hub groups of a split matrix (the length of its chain; 0 without a split).
+static int chain_levels(const sag_csr& A) {
+    int k = 0;
+    for (const sag_csr* M = &A; M->hub_part && M->cold_part; M = M->cold_part) ++k;
+    return k;
+}
+
+// A split matrix: partial rows (two buffers used in turn along a chain of
+// several groups), then the largest long-row need of any pass.
 size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
-    if (A.hub_part && A.cold_part) {
-        const size_t h = spmm_long_ws_bytes(*A.hub_part, d), c = spmm_ws_bytes(*A.cold_part, d);
-        return part_bytes(A, d) + (h > c ? h : c);
+    const int levels = chain_levels(A);
+    if (levels == 0) return spmm_long_ws_bytes(A, d);
+    size_t lw = 0;
+    const sag_csr* M = &A;
+    for (; M->hub_part && M->cold_part; M = M->cold_part) {
+        const size_t h = spmm_long_ws_bytes(*M->hub_part, d);
+        lw = h > lw ? h : lw;
     }
-    return spmm_long_ws_bytes(A, d);
+    const size_t c = spmm_long_ws_bytes(*M, d);
+    lw = c > lw ? c : lw;
+    return (levels > 1 ? 2 : 1) * part_bytes(A, d) + lw;
 }
 
 namespace {
@@ -487,25 +500,33 @@ sag_status spmm_dispatch(const sag_csr& A, const void* X, int64_t ldx, sag_dtype
 
 }  // namespace
 
-// The product over A with epi (whose partial rows, if any, come from an
-// earlier pass).  A split matrix: its hub pass into fp32 partial rows (the
-// parts carry their values; an incoming partial is added there), then the
-// product over its cold part with those rows added before the epilogue;
-// the cold part may itself be split, one level further into the workspace.
+// The product over A with epi.  A split matrix: one pass per hub group into
+// fp32 partial rows (the parts carry their values), each adding the previous
+// group's partial rows (two buffers used in turn), then the pass over the
+// final cold part with the last partial rows added before the epilogue.
 static sag_status spmm_chain(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
                              int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s) {
-    if (!(A.hub_part && A.cold_part)) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
-    float* P = static_cast<float*>(ws);
-    void* ws2 = static_cast<char*>(ws) + part_bytes(A, d);
-    Epilogue e1;
-    e1.part = epi.part;
-    e1.ld_part = epi.ld_part;
-    SAG_TRY(spmm_dispatch(*A.hub_part, X, ldx, xt, d, P, part_ld(d), SAG_F32, e1, ws2, s));
+    const int levels = chain_levels(A);
+    if (levels == 0) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
+    const size_t pb = part_bytes(A, d);
+    char* base = static_cast<char*>(ws);
+    void* lws = base + (levels > 1 ? 2 : 1) * pb;
+    const int64_t ldp = part_ld(d);
+    const float* prev = nullptr;
+    const sag_csr* M = &A;
+    for (int k = 0; M->hub_part && M->cold_part; M = M->cold_part, ++k) {
+        float* P = reinterpret_cast<float*>(base + (k % 2) * pb);
+        Epilogue e1;
+        e1.part = prev;
+        e1.ld_part = ldp;
+        SAG_TRY(spmm_dispatch(*M->hub_part, X, ldx, xt, d, P, ldp, SAG_F32, e1, lws, s));
+        prev = P;
+    }
     Epilogue e2 = epi;
     e2.row_mean = 0;
-    e2.part = P;
-    e2.ld_part = part_ld(d);
-    return spmm_chain(*A.cold_part, X, ldx, xt, d, Y, ldy, yt, e2, ws2, s);
+    e2.part = prev;
+    e2.ld_part = ldp;
+    return spmm_dispatch(*M, X, ldx, xt, d, Y, ldy, yt, e2, lws, s);
 }
 
 sag_status spmm_run(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
