@@ -1,6 +1,7 @@
 """Parity at the workloads' full sizes, in the configuration bench.py times
-(GPU CSR build with the degree-binned schedule, seg_len 1024), on outputs the
-oracle can compute one row at a time.
+(GPU CSR build with the degree-binned schedule, seg_len 1024, and the chain
+of hub splits on matrices whose rows average at least 128 entries: the dense
+GCN graph's), on outputs the oracle can compute one row at a time.
 
 For each workload the graph is drawn at full size and built on the GPU; the
 halo list is compared whole, and a sample of rows (random ones plus the
@@ -45,6 +46,10 @@ class Full:
                                           w.symmetrize, w.self_loops, w.norm)
         sag.csr_schedule(self.gb.A, SEG_LEN)
         sag.csr_schedule(self.gb.AT, SEG_LEN)
+        for M in (self.gb.A, self.gb.AT):
+            if sag.hub_split_pays(M):
+                sag.csr_hub_split(M, seg_len=SEG_LEN)
+                say(f"full-size workload {cfg}: hub chain of {len(sag.hub_chain(M)) - 1} groups")
         torch.cuda.synchronize()
         self.n_l = w.hi - w.lo
         # HALO list by definition: distinct sources outside [lo, hi) of edges into the range
