@@ -95,3 +95,18 @@ def test_split_pays_rule():
     assert not rule(SimpleNamespace(n_rows=2_450_000, n_cols=2_450_000, nnz=126_150_500))
     assert not rule(SimpleNamespace(n_rows=900, n_cols=900, nnz=400_000))
     assert not rule(SimpleNamespace(n_rows=0, n_cols=0, nnz=0))
+
+
+def test_chain_arguments_and_counts():
+    """The binding refuses a depth below one and a second split of a split
+    matrix before calling the library; hub_chain lists the entry counts of
+    the hub parts, then of the final cold part."""
+    with pytest.raises(ValueError, match="levels"):
+        sag.csr_hub_split(SimpleNamespace(hub_part=None), levels=0)
+    with pytest.raises(ValueError, match="already has a hub split"):
+        sag.csr_hub_split(SimpleNamespace(hub_part=object()))
+    last = SimpleNamespace(hub_part=None, nnz=5)
+    mid = SimpleNamespace(hub_part=SimpleNamespace(nnz=7), cold_part=last)
+    top = SimpleNamespace(hub_part=SimpleNamespace(nnz=30), cold_part=mid)
+    assert sag.hub_chain(top) == [30, 7, 5]
+    assert sag.hub_chain(last) == []
