@@ -224,6 +224,10 @@ sag_status sag_csr_schedule(sag_csr* A, int32_t seg_len, void* buf, size_t buf_b
                             void* ws, size_t ws_bytes, void* stream);
 
 /* Hub split of a CSR (setup, once per matrix; synchronises `stream`).
+ * The product of a split matrix is the sum of the products of its parts:
+ * the CAGNET page's 1D algorithm section sums the product block column by
+ * block column; here a block is a group of the busiest columns (and, along
+ * a chain, the next-busiest), so that its rows of X fit one L2.
  * The hub columns are the n_hub columns holding the most entries of A
  * (ties to the lower column id; all columns when n_hub >= n_cols).  Writes
  * two CSRs over A's rows and columns: the hub part (every entry of A in a
