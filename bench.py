@@ -742,6 +742,24 @@ def gat_layer(m, sag, torch, np, heads=4, reps=5, cpu_rows=4096):
     table.sort(key=lambda t: -t["ms_per_layer"])
     del H, W, G, Out, dH, ws
     torch.cuda.empty_cache()
+    # the bare gather of F-wide rows over A's and A^T's column ids: the access
+    # pattern of the sweeps over A (forward aggregation, backward row sweep:
+    # rows of Wh) and of the column sweep over A^T (rows of the output
+    # gradient, which also reads a small per-row record)
+    Xp = sag.empty_dense(m.n_ext, F, m.tdt, dev, fill=1.0)
+    probe = {}
+    for name, M in (("A", A), ("AT", AT)):
+        sink = sag.gather_probe(Xp, M.indices)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            sag.gather_probe(Xp, M.indices, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        probe[f"over_{name}_ms"] = round(e0.elapsed_time(e1) / reps, 4)
+    del Xp, sink
+    torch.cuda.empty_cache()
 
     # the oracle on a bounded sample of the same graph
     src, dst = w.edges
@@ -759,6 +777,8 @@ def gat_layer(m, sag, torch, np, heads=4, reps=5, cpu_rows=4096):
     scale = m.n_l / R
     return {"layer": f"GAT {d} -> {heads} x {dh}, ReLU", "dtype": w.dtype, "n_local": m.n_l,
             "n_ext": m.n_ext, "nnz": A.nnz, "ms_fwd_bwd": round(ms, 3), "ops": table,
+            "gather_probe": dict(probe, note=f"sag_gather_probe over the column ids with rows {F} wide: the bare "
+                                             "gather each sweep of the layer makes"),
             "cpu_baseline": {"value": round(cpu_s * scale * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
                              "sample": (f"local rows [0,{R}) as a partition ({ob.A.n_cols - R} halo columns), "
                                         f"fwd+bwd in float64 took {cpu_s:.2f} s, scaled by {scale:.1f}")}}
