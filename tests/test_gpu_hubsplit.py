@@ -193,3 +193,35 @@ def test_two_pass_deterministic_and_noalloc_one_pass():
     Y = sag.empty_dense(gb.A.n_rows, 100, torch.float32, DEV)
     sag.spmm_csr_noalloc(gb.A, X, Y)
     assert torch.equal(Y, one)
+
+
+def _gat_pass(gb, H, W, asrc, adst, b, G):
+    out, ctx = sag.gat_layer_forward(gb.A, H, W, asrc, adst, b, heads=4, relu=True)
+    dW, das, dad, db, dH = sag.gat_layer_backward(ctx, gb.A, gb.AT, out, G)
+    return [out, dW, das, dad, db, dH]
+
+
+def test_gat_reads_the_matrix_itself():
+    """GAT works on the matrix's own arrays, so a split changes none of its
+    bits (forward and backward)."""
+    w, _, _, gb = _built(2, 0.004, "none")
+    for M in (gb.A, gb.AT):
+        sag.csr_schedule(M, 64)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(8)
+    n, d, F = gb.A.n_cols, 64, 64
+    H = sag.empty_dense(n, d, torch.float32, DEV)
+    H.copy_(torch.randn(n, d, device=DEV, generator=g))
+    W = (torch.randn(d, F, device=DEV, generator=g) * 0.1).contiguous()
+    asrc = torch.randn(4, 16, device=DEV, generator=g) * 0.3
+    adst = torch.randn(4, 16, device=DEV, generator=g) * 0.3
+    b = torch.randn(F, device=DEV, generator=g) * 0.1
+    G = sag.empty_dense(gb.A.n_rows, F, torch.float32, DEV)
+    G.copy_(torch.randn(gb.A.n_rows, F, device=DEV, generator=g))
+    say("gat over a split matrix")
+    ref = [t.clone() for t in _gat_pass(gb, H, W, asrc, adst, b, G)]
+    for M in (gb.A, gb.AT):
+        sag.csr_hub_split(M, 50, 64, levels=3)
+    got = _gat_pass(gb, H, W, asrc, adst, b, G)
+    for a, r in zip(got, ref):
+        assert torch.equal(a, r)

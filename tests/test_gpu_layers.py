@@ -127,6 +127,15 @@ def test_layers_over_hub_split(hub_cols, model, dt, d_in, d_out, relu):
              d_in, d_out, relu, seed=hub_cols + d_in, seg_len=128, label="hub split", hub_cols=hub_cols)
 
 
+def test_fused_layer_over_hub_split():
+    """The fused aggregate -> transform kernel reads the matrix's own arrays,
+    so it runs (and matches the oracle) over a split matrix too."""
+    w = gen.make_config(2, 0.004)
+    src, dst = w.edges
+    run_case("sage", "bf16", src, dst, w.n_global, 0, w.n_global, True, True, "mean", 100, 256, True, seed=9,
+             seg_len=128, label="fused over hub split", fused=True, hub_cols=64)
+
+
 def test_partition_with_halo_over_hub_split():
     w = gen.make_config(3, 1 / 64)
     src, dst = w.edges
