@@ -368,6 +368,18 @@ class Model:
         log(f"[bench] built: n_local={self.n_l} n_halo={self.n_h} nnz={A.nnz} in {self.build_ms:.1f} ms; "
             f"schedule {sag.csr_info(A)}")
         self.graph_stats = graph_stats(A, self.n_l, torch)
+        # products over unsplit matrices whose rows span more than two cache
+        # lines: one pass per 128-byte column slice where that is measured to
+        # be faster on the matrix (timed here, before any timed step)
+        self.col_slices = {}
+        for name, M in (("A", self.built.A), ("AT", self.built.AT)):
+            ds = [d for d in w.dims if sag.col_slices_apply(M, d, self.tdt)]
+            if ds:
+                r = sag.csr_tune_col_slices(M, max(ds), self.tdt)
+                self.col_slices[name] = {"d": max(ds), "on": r["on"], "whole_ms": round(r["whole_ms"], 4),
+                                         "sliced_ms": round(r["sliced_ms"], 4)}
+        if self.col_slices:
+            log(f"[bench] column slices: {self.col_slices}")
 
         def dev_dense(x):
             t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16) \
@@ -975,7 +987,7 @@ def config_run(w, sag, torch, args):
     roof["gather_probe"] = gather_probe_of(roof, m.built, sag, torch) if w.cfg != 1 else None
     out = {"workload": w.name, "config": w.cfg, "dtype": w.dtype, "dims": w.dims, "layer": w.model,
            "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
-           "hub_split": m.hub_split or None,
+           "hub_split": m.hub_split or None, "col_slices": m.col_slices or None,
            "ms_per_step": round(min(ms, g_ms) if g_ms is not None else ms, 4),
            "mode": "graph" if g_ms is not None and g_ms < ms else "eager",
            "step_ms": pct(g_per if g_ms is not None and g_ms < ms else per), "steps": steps,
@@ -1082,7 +1094,7 @@ def run(args, cfgs, jobs):
     conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
             "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion,
-            "hub_split": m.hub_split or None,
+            "hub_split": m.hub_split or None, "col_slices": m.col_slices or None,
             "graph": m.graph_stats}
     build_ms = m.build_ms
     overlap = fused = gat = halo = None

@@ -137,7 +137,29 @@ enum {
  * pass each, every pass adding the previous partial rows to its own.  The
  * result differs from the one-pass product only by fp32 summation order.
  * The split pays on graphs with many entries per row, where the partial
- * rows cost little next to the gathers they speed up. */
+ * rows cost little next to the gathers they speed up.
+ *
+ * col_slices: nonzero asks products over this matrix (sag_spmm_csr,
+ * sag_spmm_csr_t, sag_spmm_csr_noalloc and the layers' SpMMs) whose rows of X
+ * span more than 256 bytes to run as one pass per 128-byte column slice of
+ * X (the last slice narrower), each pass writing its columns of Y with the
+ * epilogue applied.  This is the column-block split of H in [CAGNET]'s 2D
+ * and 3D algorithms ("Reducing Communication in Graph Neural Network
+ * Training", the 2D section's block decomposition and the 3D section's
+ * shorter, fatter pieces of H), run one block after another on one GPU:
+ * every gather of a pass reads one cache line, so each L2 holds the lines of
+ * four times as many rows of X as with whole rows, and on degree laws whose
+ * busiest columns carry much of the matrix more of them hit.  The price is
+ * one more pass over the indices (and values) per slice and per-row work
+ * repeated per slice, so whether it pays depends on the matrix (measured:
+ * about 5% saved at 512-byte rows on a 2.45M-node power-law graph with 51
+ * entries per row, 3-8% lost on some R-MAT matrices), and is best decided
+ * by timing both on the matrix.  Rows of at most 256 bytes are always
+ * gathered whole (two slices gain too little L2 reach for the second pass).
+ * The result differs from the whole-row product only by fp32 summation
+ * order.
+ * Ignored by a matrix with a hub split (its passes take whole rows), by the
+ * fused aggregate -> transform kernel and by GAT. */
 typedef struct sag_csr {
     int64_t n_rows;
     int64_t n_cols;
@@ -154,6 +176,7 @@ typedef struct sag_csr {
     int32_t row_mean;
     const struct sag_csr* hub_part;
     const struct sag_csr* cold_part;
+    int32_t col_slices;
 } sag_csr;
 
 /* ---------------------------------------------------------------------------

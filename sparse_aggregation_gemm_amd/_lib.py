@@ -32,6 +32,7 @@ class SagCsr(ctypes.Structure):
         ("n_short", i64), ("n_medium", i64), ("n_long", i64), ("n_seg", i64),
         ("seg_len", i32), ("row_mean", i32),
         ("hub_part", vp), ("cold_part", vp),
+        ("col_slices", i32),
     ]
 
 

@@ -284,7 +284,7 @@ __device__ __forceinline__ void segments(const SpArgs<XT, YT>& p, int64_t block)
 // All three bins in one launch: the workgroups of long-row segments come
 // first (the longest work starts first), then medium rows, then short rows.
 template <class XT, class YT, int G, int NV>
-__global__ __launch_bounds__(256) void spmm_bins(SpArgs<XT, YT> p) {
+__device__ __forceinline__ void bins(const SpArgs<XT, YT>& p) {
     int64_t b = blockIdx.x;
     if (b < p.nb_seg) {
         segments<XT, YT, G, NV>(p, b);
@@ -296,6 +296,19 @@ __global__ __launch_bounds__(256) void spmm_bins(SpArgs<XT, YT> p) {
         return;
     }
     short_rows<XT, YT, G, NV>(p, b - p.nb_medium);
+}
+
+template <class XT, class YT, int G, int NV>
+__global__ __launch_bounds__(256) void spmm_bins(SpArgs<XT, YT> p) {
+    bins<XT, YT, G, NV>(p);
+}
+
+// One 128-byte column slice of every row (eight lanes of one 16-byte vector
+// each): the same code as spmm_bins<XT, YT, 8, 1>, under a name of its own so
+// that a profile tells slice passes from whole narrow rows.
+template <class XT, class YT>
+__global__ __launch_bounds__(256) void spmm_slice(SpArgs<XT, YT> p) {
+    bins<XT, YT, 8, 1>(p);
 }
 
 // Adds the partial rows of each long row in segment order, then the epilogue.
@@ -331,7 +344,7 @@ __global__ __launch_bounds__(256) void spmm_long_reduce(SpArgs<XT, YT> p) {
 }
 
 template <class XT, class YT, int G, int NV>
-sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s, bool long_only) {
+sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s, bool long_only, bool slice = false) {
     constexpr int P = 64 / G;
     const int4* rec = reinterpret_cast<const int4*>(A.sched);
     if (!rec) {
@@ -358,7 +371,14 @@ sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s, bool l
     const int64_t nb_short = cdiv(p.n_short, kWaves * P);
     const int64_t blocks = p.nb_seg + p.nb_medium + nb_short;
     if (blocks > 0) {
-        spmm_bins<XT, YT, G, NV><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(p);
+        if constexpr (G == 8 && NV == 1) {
+            if (slice)
+                spmm_slice<XT, YT><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(p);
+            else
+                spmm_bins<XT, YT, G, NV><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(p);
+        } else {
+            spmm_bins<XT, YT, G, NV><<<dim3(static_cast<unsigned>(blocks)), 256, 0, s>>>(p);
+        }
         SAG_LAUNCH_CHECK();
     }
     if (p.n_long > 0) {
@@ -370,7 +390,7 @@ sag_status launch_bins(const sag_csr& A, SpArgs<XT, YT> p, hipStream_t s, bool l
 
 template <class XT, class YT>
 sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, void* Y, int64_t ldy,
-                     const Epilogue& epi, void* ws, hipStream_t s, bool long_only = false) {
+                     const Epilogue& epi, void* ws, hipStream_t s, bool long_only = false, bool slice = false) {
     constexpr int V = Vec<XT>::N;
     SpArgs<XT, YT> p{};
     p.X = static_cast<const XT*>(X);
@@ -393,6 +413,10 @@ sag_status run_typed(const sag_csr& A, const void* X, int64_t ldx, int64_t d, vo
     p.e.part = epi.part;
     p.e.ld_part = epi.ld_part;
     const int C = p.C;
+    if (slice) {
+        if (C > 8) return fail(SAG_E_INVALID, "spmm: a column slice spans more than 128 bytes");
+        return launch_bins<XT, YT, 8, 1>(A, p, s, long_only, true);
+    }
     if (C <= 4) return launch_bins<XT, YT, 4, 1>(A, p, s, long_only);
     if (C <= 8) return launch_bins<XT, YT, 8, 1>(A, p, s, long_only);
     if (C <= 16) return launch_bins<XT, YT, 16, 1>(A, p, s, long_only);
@@ -491,11 +515,39 @@ size_t spmm_ws_bytes(const sag_csr& A, int64_t d) {
 namespace {
 
 sag_status spmm_dispatch(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
-                         int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s) {
-    if (xt == SAG_F32 && yt == SAG_F32) return run_typed<float, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
-    if (xt == SAG_BF16 && yt == SAG_BF16) return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, epi, ws, s);
-    if (xt == SAG_BF16 && yt == SAG_F32) return run_typed<uint16_t, float>(A, X, ldx, d, Y, ldy, epi, ws, s);
+                         int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s,
+                         bool slice = false) {
+    if (xt == SAG_F32 && yt == SAG_F32) return run_typed<float, float>(A, X, ldx, d, Y, ldy, epi, ws, s, false, slice);
+    if (xt == SAG_BF16 && yt == SAG_BF16)
+        return run_typed<uint16_t, uint16_t>(A, X, ldx, d, Y, ldy, epi, ws, s, false, slice);
+    if (xt == SAG_BF16 && yt == SAG_F32)
+        return run_typed<uint16_t, float>(A, X, ldx, d, Y, ldy, epi, ws, s, false, slice);
     return fail(SAG_E_UNSUPPORTED, "spmm: unsupported (X, Y) dtype pair");
+}
+
+constexpr int64_t kSliceBytes = 128;   // one cache line of each row per pass
+
+// The one-pass product, or, when A asks for column slices and a row of X
+// spans more than two of them, one pass per 128-byte column slice of X (the
+// last narrower) writing the same columns of Y: each pass gathers one line
+// per entry, so L2 holds the lines of four times as many rows of X.  The
+// epilogue is per element, so each slice takes its own columns of the
+// addend, bias and Y_pre.  Every slice reuses the long-row partials (stream
+// order: a slice's reduce finishes before the next slice's segments write).
+sag_status spmm_one_pass(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
+                         int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s) {
+    const int64_t ex = elt_size(xt), ey = elt_size(yt);
+    if (!A.col_slices || d * ex <= 2 * kSliceBytes) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
+    const int64_t w = kSliceBytes / ex;
+    for (int64_t c0 = 0; c0 < d; c0 += w) {
+        Epilogue e = epi;
+        if (e.addend) e.addend = static_cast<const char*>(e.addend) + c0 * ey;
+        if (e.bias) e.bias += c0;
+        if (e.pre) e.pre = static_cast<char*>(e.pre) + c0 * ey;
+        SAG_TRY(spmm_dispatch(A, static_cast<const char*>(X) + c0 * ex, ldx, xt, w < d - c0 ? w : d - c0,
+                              static_cast<char*>(Y) + c0 * ey, ldy, yt, e, ws, s, true));
+    }
+    return SAG_OK;
 }
 
 }  // namespace
@@ -507,7 +559,7 @@ sag_status spmm_dispatch(const sag_csr& A, const void* X, int64_t ldx, sag_dtype
 static sag_status spmm_chain(const sag_csr& A, const void* X, int64_t ldx, sag_dtype xt, int64_t d, void* Y,
                              int64_t ldy, sag_dtype yt, const Epilogue& epi, void* ws, hipStream_t s) {
     const int levels = chain_levels(A);
-    if (levels == 0) return spmm_dispatch(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
+    if (levels == 0) return spmm_one_pass(A, X, ldx, xt, d, Y, ldy, yt, epi, ws, s);
     const size_t pb = part_bytes(A, d);
     char* base = static_cast<char*>(ws);
     void* lws = base + (levels > 1 ? 2 : 1) * pb;
@@ -652,6 +704,6 @@ extern "C" sag_status sag_spmm_csr_noalloc(const sag_csr* A, const void* X, int6
     if (A->n_rows == 0 || d == 0) return SAG_OK;
     void* ws = nullptr;
     if (need > 0) SAG_TRY(scratch_address(&ws));
-    return spmm_dispatch(*A, X, ldx, xt, d, Y, ldy, yt, entry_epilogue(A, addend, ld_add, n_add), ws,
+    return spmm_one_pass(*A, X, ldx, xt, d, Y, ldy, yt, entry_epilogue(A, addend, ld_add, n_add), ws,
                          static_cast<hipStream_t>(stream));
 }

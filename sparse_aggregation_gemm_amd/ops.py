@@ -95,6 +95,7 @@ class Csr:
     raw: L.SagCsr = field(default_factory=L.SagCsr)
     hub_part: "Csr | None" = None    # hub split (csr_hub_split): entries in the hub columns
     cold_part: "Csr | None" = None   # and the rest
+    col_slices: bool = False   # products gather X in 128-byte column slices (csr_set_col_slices)
 
     def __post_init__(self):
         self.raw.n_rows = self.n_rows
@@ -104,6 +105,7 @@ class Csr:
         self.raw.indices = _ptr(self.indices)
         self.raw.values = _ptr(self.values)
         self.raw.row_mean = int(bool(self.row_mean))
+        self.raw.col_slices = int(bool(self.col_slices))
 
     @property
     def nnz(self) -> int:
@@ -293,6 +295,61 @@ def _split_once(A: Csr, n_hub: int, seg_len: int | None) -> None:
     A.hub_part, A.cold_part = parts
     A.raw.hub_part = ctypes.addressof(parts[0].raw)
     A.raw.cold_part = ctypes.addressof(parts[1].raw)
+
+
+COL_SLICE_BYTES = 128        # one cache line of each row of X per pass
+COL_SLICE_MIN_ROW_BYTES = 257   # rows of at most two slices are gathered whole
+COL_SLICE_MARGIN = 0.02     # slices are kept only when this much faster
+
+
+def csr_set_col_slices(A: Csr, on: bool) -> Csr:
+    """Set A's col_slices flag: products over A whose rows of X span more
+    than 256 bytes run one pass per 128-byte column slice of X."""
+    A.col_slices = bool(on)
+    A.raw.col_slices = int(A.col_slices)
+    return A
+
+
+def col_slices_apply(A: Csr, d: int, dtype: torch.dtype) -> bool:
+    """Whether a product of width d in dtype over A runs in column slices
+    when A asks for them (no hub split, rows wider than two slices)."""
+    es = torch.empty(0, dtype=dtype).element_size()
+    return A.hub_part is None and d * es >= COL_SLICE_MIN_ROW_BYTES
+
+
+def csr_tune_col_slices(A: Csr, d: int, dtype: torch.dtype, reps: int = 3,
+                        margin: float = COL_SLICE_MARGIN) -> dict:
+    """Time the product over A at width d both ways (random X, the library's
+    own entry point, HIP events on the current stream, rounds alternated,
+    medians) and set A's col_slices when slices are faster by more than
+    `margin`.  Whether slices pay depends on how much of the matrix its
+    busiest columns carry, so it is measured on the matrix itself.  Returns
+    {"on", "whole_ms", "sliced_ms"} (timings None where slices cannot
+    apply)."""
+    if not col_slices_apply(A, d, dtype) or A.nnz == 0:
+        csr_set_col_slices(A, False)
+        return {"on": False, "whole_ms": None, "sliced_ms": None}
+    dev = A.device
+    X = empty_dense(A.n_cols, d, dtype, dev)
+    X.normal_()
+    Y = empty_dense(A.n_rows, d, dtype, dev)
+    times = {False: [], True: []}
+    for r in range(reps + 1):
+        for on in (False, True):
+            csr_set_col_slices(A, on)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            spmm_csr(A, X, Y=Y)
+            b.record()
+            b.synchronize()
+            if r > 0:   # the first round warms both
+                times[on].append(a.elapsed_time(b))
+    whole = sorted(times[False])[len(times[False]) // 2]
+    sliced = sorted(times[True])[len(times[True]) // 2]
+    on = sliced < (1.0 - margin) * whole
+    csr_set_col_slices(A, on)
+    return {"on": on, "whole_ms": whole, "sliced_ms": sliced}
 
 
 def csr_info(A: Csr) -> dict:

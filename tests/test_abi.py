@@ -162,3 +162,23 @@ def test_workspace_queries_are_host_only():
     assert lib.sag_gat_save_bytes(100, 150, 4, 8, 1) == 9728 + 2560 + 2560 + 1792
     assert lib.sag_gat_save_bytes(100, 150, 4, 12, 1) == 0
     assert lib.sag_gat_forward_workspace_bytes(ctypes.byref(A), 64, 4, 8, 1) > 0
+
+
+def test_csr_struct_layout_matches_the_header(tmp_path):
+    """The binding's ctypes mirror of sag_csr has the header's size and field
+    offsets (a C program built from include/sag.h prints them)."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None:
+        pytest.skip("no C compiler")
+    fields = [f[0] for f in L.SagCsr._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "sag.h"\nint main(void) {\n'
+                   '    printf("%zu\\n", sizeof(sag_csr));\n' +
+                   "".join(f'    printf("%zu\\n", offsetof(sag_csr, {n}));\n' for n in fields) +
+                   "    return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    assert got[0] == ctypes.sizeof(L.SagCsr)
+    assert got[1:] == [getattr(L.SagCsr, n).offset for n in fields]

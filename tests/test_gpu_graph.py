@@ -27,7 +27,7 @@ class Pass:
     same values); layer l writes its output into the local rows of layer
     l + 1's input."""
 
-    def __init__(self, w, dt, dims, relu, seed, hub_cols=None):
+    def __init__(self, w, dt, dims, relu, seed, hub_cols=None, col_slices=False):
         src, dst = w.edges
         norm = "gcn" if w.model == "gcn" else "mean"
         self.b = sag.csr_build_normalize(to_dev(src), to_dev(dst), w.n_global, w.lo, w.hi, w.symmetrize,
@@ -37,6 +37,9 @@ class Pass:
         if hub_cols:
             sag.csr_hub_split(self.b.A, hub_cols, 256)
             sag.csr_hub_split(self.b.AT, hub_cols, 256)
+        if col_slices:
+            sag.csr_set_col_slices(self.b.A, True)
+            sag.csr_set_col_slices(self.b.AT, True)
         A = self.b.A
         self.n_l, self.n_ext = A.n_rows, A.n_cols
         self.n_h = self.n_ext - self.n_l
@@ -145,3 +148,11 @@ def test_dense_gcn_over_hub_split_f32():
     w = gen.make_config(2, 0.004)
     say("graph capture: dense gcn over a hub split f32")
     check_graph(Pass(w, "f32", [64, 32, 16], [True, False], seed=6, hub_cols=100))
+
+
+def test_sage_over_column_slices_bf16():
+    """The large power-law graph's SAGE (reduced) with both matrices in
+    column slices: every 256-wide product is four launches in the graph."""
+    w = gen.make_config(4, 0.002)
+    say("graph capture: sage over column slices bf16")
+    check_graph(Pass(w, "bf16", [100, 256, 256, 47], [True, True, False], seed=7, col_slices=True))

@@ -31,7 +31,8 @@ def _bits_or_f32(x, dt):
 
 
 def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_out, relu,
-             stale_rows=0, stale_base=0, seed=0, seg_len=256, label="", fused=False, hub_cols=None):
+             stale_rows=0, stale_base=0, seed=0, seg_len=256, label="", fused=False, hub_cols=None,
+             col_slices=False):
     g = np.random.default_rng(seed)
     n_l = hi - lo
     say(f"layer {label} model={model} dt={dt} n_global={n_global} [{lo},{hi}) {d_in}->{d_out}")
@@ -55,6 +56,10 @@ def run_case(model, dt, src, dst, n_global, lo, hi, sym, loops, norm, d_in, d_ou
         # both products of the layer take two passes (hub part, cold part)
         sag.csr_hub_split(gb.A, hub_cols, seg_len or 1024)
         sag.csr_hub_split(gb.AT, hub_cols, seg_len or 1024)
+    if col_slices:
+        # products with rows over 256 bytes take one pass per 128-byte column slice
+        sag.csr_set_col_slices(gb.A, True)
+        sag.csr_set_col_slices(gb.AT, True)
     tdt = torch.float32 if dt == "f32" else torch.bfloat16
     H_ext = sag.empty_dense(n_l + n_h, d_in, tdt, DEV)
     H_ext[:n_l].copy_(to_dev_dense(H_loc, dt))
@@ -134,6 +139,19 @@ def test_fused_layer_over_hub_split():
     src, dst = w.edges
     run_case("sage", "bf16", src, dst, w.n_global, 0, w.n_global, True, True, "mean", 100, 256, True, seed=9,
              seg_len=128, label="fused over hub split", fused=True, hub_cols=64)
+
+
+@pytest.mark.parametrize("model,dt,d_in,d_out,relu", [("gcn", "f32", 602, 128, True), ("gcn", "f32", 96, 200, False),
+                                                      ("sage", "bf16", 256, 256, True), ("sage", "f32", 256, 160, True),
+                                                      ("sage", "bf16", 300, 47, False)])
+def test_layers_over_column_slices(model, dt, d_in, d_out, relu):
+    """Both of the layer's matrices gather in 128-byte column slices: the
+    epilogue (bias, Y_pre, ReLU, the SAGE self-term addend) lands on each
+    slice's own columns."""
+    w = gen.make_config(4, 0.002)
+    src, dst = w.edges
+    run_case(model, dt, src, dst, w.n_global, 0, w.n_global, True, True, "gcn" if model == "gcn" else "mean",
+             d_in, d_out, relu, seed=d_in + d_out, seg_len=64, label="column slices", col_slices=True)
 
 
 def test_partition_with_halo_over_hub_split():
