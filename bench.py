@@ -84,6 +84,9 @@ def parse():
     p.add_argument("--fusion", action="store_true",
                    help="layers use the fused aggregate -> transform kernel where it applies")
     p.add_argument("--cpu-rows", type=int, default=0, help="rows of the CPU baseline sample (0: auto)")
+    p.add_argument("--col-slices", default="tune",
+                   help="products in 128-byte column slices: 'tune' (timed on each matrix at set-up), 'off', "
+                        "or the matrices to slice ('A', 'AT', 'A,AT')")
     p.add_argument("--copy-calib", action="store_true",
                    help="run one 1 GiB identity row gather before the steps (a copy kernel of known "
                         "traffic for scaling hardware byte counters)")
@@ -91,11 +94,14 @@ def parse():
                    help="no GPU work: read two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) "
                         "of a --copy-calib run and write the dominant kernel's HBM traffic summary")
     p.add_argument("--op", help="trace op name the summary is for (with --summarize-counters)")
-    p.add_argument("--kernel", help="kernel name substring of that op (with --summarize-counters)")
+    p.add_argument("--kernel", action="append",
+                   help="kernel name substring of that op (with --summarize-counters; repeat for an op whose "
+                        "launches run several kernels, each with its own --dispatches-per-launch)")
     p.add_argument("--out", help="summary file to write (with --summarize-counters)")
-    p.add_argument("--dispatches-per-launch", type=int, default=1,
-                   help="dispatches of the kernel that make one launch of the op: 2 for a product over a hub "
-                        "split (hub pass, cold pass); with --summarize-counters")
+    p.add_argument("--dispatches-per-launch", type=float, action="append",
+                   help="dispatches of the matching --kernel in one average launch of the op (default 1 each): "
+                        "e.g. one per pass of a product over a hub split, one per column slice, 0.5 for a "
+                        "kernel that runs in one of the op's two launches per step; with --summarize-counters")
     p.add_argument("--sizes-dir", help="optional third pass (TCC_EA0_RDREQ_sum and its 32B/64B/128B parts) "
                                        "for an independent count of the bytes read (with --summarize-counters)")
     return p.parse_args()
@@ -135,84 +141,108 @@ def _pick(per, sub):
 
 
 def summarize_counters(args):
-    """HBM traffic of one kernel from FETCH_SIZE / WRITE_SIZE passes, each
-    scaled by what the counter reads for the calibration copy of known size."""
+    """HBM traffic of one op from FETCH_SIZE / WRITE_SIZE passes, each scaled
+    by what the counter reads for the calibration copy of known size.  An op
+    whose launches run several kernels (hub passes, column slices, launches
+    of one op that take different paths) names each kernel with the number
+    of its dispatches in one average launch of the op."""
+    kernels = args.kernel
+    ks = args.dispatches_per_launch or [1.0] * len(kernels)
+    if len(ks) != len(kernels):
+        raise SystemExit("give one --dispatches-per-launch per --kernel")
     fetch = _counter_means(args.summarize_counters[0], "FETCH_SIZE")
     write = _counter_means(args.summarize_counters[1], "WRITE_SIZE")
     _, cf = _pick(fetch, CALIB_KERNEL)
     _, cw = _pick(write, CALIB_KERNEL)
-    kname, kf = _pick(fetch, args.kernel)
-    _, kw = _pick(write, args.kernel)
     f_fetch = CALIB_READ / (sum(cf) / len(cf) * 1024)
     f_write = CALIB_WRITE / (sum(cw) / len(cw) * 1024)
-    k = args.dispatches_per_launch
-    fetch_b = sum(kf) / len(kf) * 1024 * f_fetch * k
-    write_b = sum(kw) / len(kw) * 1024 * f_write * k
-    rec = {"op": args.op, "kernel": kname, "sources_sha256_16": sources_digest(args.op),
-           "dispatches": [len(kf), len(kw)], "calib_fetch_kib": sum(cf) / len(cf),
-           "calib_write_kib": sum(cw) / len(cw), "calib_read_bytes": CALIB_READ,
-           "calib_write_bytes": CALIB_WRITE, "scale_fetch": round(f_fetch, 4), "scale_write": round(f_write, 4),
-           "kernel_fetch_kib": sum(kf) / len(kf), "kernel_write_kib": sum(kw) / len(kw),
+    names, kfs, kws, fetch_b, write_b, rows = [], [], [], 0.0, 0.0, []
+    for sub, k in zip(kernels, ks):
+        kname, kf = _pick(fetch, sub)
+        _, kw = _pick(write, sub)
+        mf, mw = sum(kf) / len(kf), sum(kw) / len(kw)
+        names.append(kname)
+        kfs.append(mf)
+        kws.append(mw)
+        fetch_b += mf * 1024 * f_fetch * k
+        write_b += mw * 1024 * f_write * k
+        rows.append(f"| `{sub}` | {k:g} | {mf:.0f} (mean of {len(kf)}) | {mw:.0f} (mean of {len(kw)}) |")
+    rec = {"op": args.op, "kernel": " + ".join(names), "sources_sha256_16": sources_digest(args.op),
+           "calib_fetch_kib": sum(cf) / len(cf), "calib_write_kib": sum(cw) / len(cw),
+           "calib_read_bytes": CALIB_READ, "calib_write_bytes": CALIB_WRITE,
+           "scale_fetch": round(f_fetch, 4), "scale_write": round(f_write, 4),
+           "kernel_fetch_kib": kfs, "kernel_write_kib": kws,
            "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
            "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
-           "dispatches_per_launch": k}
+           "dispatches_per_launch": ks}
     cfg_arg = f" --config {args.config}" if args.config != 4 else ""
+    cs_arg = f" --col-slices {args.col_slices}" if args.col_slices != "tune" else ""
     sizes_arg = f" --sizes-dir {args.sizes_dir}" if args.sizes_dir else ""
-    cmd = f"python3 bench.py{cfg_arg} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --configs '' --copy-calib"
+    cmd = f"python3 bench.py{cfg_arg}{cs_arg} --steps 2 --warmup 1 --no-cpu-baseline --no-extras --configs '' --copy-calib"
     sizes = ""
     if args.sizes_dir:
-        names = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
-        per = {n: _counter_means(args.sizes_dir, n) for n in names}
-        rows = []
-        for label, sub in (("calibration copy", CALIB_KERNEL), ("kernel", args.kernel)):
+        names_c = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
+        per = {n: _counter_means(args.sizes_dir, n) for n in names_c}
+        srows = []
+        tot = {"calib": [0.0, 0.0], "kernel": [0.0, 0.0]}
+        for label, sub, k in [("calibration copy", CALIB_KERNEL, 1.0)] + [(f"`{x}`", x, kx) for x, kx in zip(kernels, ks)]:
             v = {}
-            for n in names:
+            for n in names_c:
                 _, vals = _pick(per[n], sub)
                 v[n] = sum(vals) / len(vals)
-            b = 32 * v[names[1]] + 64 * v[names[2]] + 128 * v[names[3]]
-            rows.append(f"| {label} | {v[names[0]]:.0f} | {v[names[1]]:.0f} | {v[names[2]]:.0f} | "
-                        f"{v[names[3]]:.0f} | {b:.4e} |")
-            tag = "calib" if label.startswith("cal") else "kernel"
-            per_launch = k if tag == "kernel" else 1   # the op's launch: k dispatches of the kernel
-            rec["sized_read_bytes_" + tag] = int(round(b * per_launch))
-            rec["read_requests_" + tag] = int(round(v[names[0]] * per_launch))
+            by = 32 * v[names_c[1]] + 64 * v[names_c[2]] + 128 * v[names_c[3]]
+            srows.append(f"| {label} | {v[names_c[0]]:.0f} | {v[names_c[1]]:.0f} | {v[names_c[2]]:.0f} | "
+                         f"{v[names_c[3]]:.0f} | {by:.4e} |")
+            tag = "calib" if sub == CALIB_KERNEL else "kernel"
+            tot[tag][0] += by * k
+            tot[tag][1] += v[names_c[0]] * k
+        for tag in ("calib", "kernel"):
+            rec["sized_read_bytes_" + tag] = int(round(tot[tag][0]))
+            rec["read_requests_" + tag] = int(round(tot[tag][1]))
         sizes = f"""
-Cross-check: read requests by size (one more pass), bytes = 32 n32 + 64 n64 + 128 n128:
+Cross-check: read requests by size (one more pass), bytes = 32 n32 + 64 n64 + 128 n128, per
+dispatch (the op's launch: the dispatches above, {rec['read_requests_kernel']} requests and
+{rec['sized_read_bytes_kernel']:.4e} bytes):
 
 ```
-rocprofv3 --pmc {' '.join(names)} --output-format csv -d {args.sizes_dir} -o sizes -- {cmd}
+rocprofv3 --pmc {' '.join(names_c)} --output-format csv -d {args.sizes_dir} -o sizes -- {cmd}
 ```
 
 | | requests | 32 B | 64 B | 128 B | bytes/dispatch |
 |---|---|---|---|---|---|
-{chr(10).join(rows)}
+{chr(10).join(srows)}
 """
-    k_arg = f" --dispatches-per-launch {k}" if k != 1 else ""
-    k_note = (f"\nOne launch of the op is {k} dispatches of this kernel (a product over a hub split: its hub\n"
-              f"passes, then the cold pass), so the per-launch figures below are {k} times the per-dispatch means.\n"
-              if k != 1 else "")
+    k_arg = "".join(f" --kernel '{x}'" for x in kernels)
+    if args.dispatches_per_launch:
+        k_arg += "".join(f" --dispatches-per-launch {kx:g}" for kx in ks)
     text = f"""# HBM traffic of `{args.op}` from TCC byte counters
 
-Kernel: `{kname}`
+Kernels: {", ".join(f"`{n}`" for n in names)}
 
 Commands (each a run of its own, from the repository root):
 
 ```
 rocprofv3 --pmc FETCH_SIZE --output-format csv -d {args.summarize_counters[0]} -o fetch -- {cmd}
 rocprofv3 --pmc WRITE_SIZE --output-format csv -d {args.summarize_counters[1]} -o write -- {cmd}
-python3 bench.py{cfg_arg} --summarize-counters {args.summarize_counters[0]} {args.summarize_counters[1]}{sizes_arg} \\
-    --op '{args.op}' --kernel '{args.kernel}' --out {args.out}{k_arg}
+python3 bench.py{cfg_arg}{cs_arg} --summarize-counters {args.summarize_counters[0]} {args.summarize_counters[1]}{sizes_arg} \\
+    --op '{args.op}'{k_arg} --out {args.out}
 ```
-{k_note}
+
+One average launch of the op is the dispatches below (per kernel: dispatches per launch, then
+the per-dispatch means of the counters in KiB); the per-launch bytes are their weighted sum.
+
+| kernel | dispatches per launch | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch |
+|---|---|---|---|
+{chr(10).join(rows)}
 
 `--copy-calib` runs one identity row gather through the library before the steps:
 {CALIB_ROWS} rows of {CALIB_ROW_BYTES} B, so {CALIB_READ} bytes read (rows + int32 row list) and
 {CALIB_WRITE} bytes written.  Each counter is scaled by known bytes / counted bytes of that copy.
 
-| | calibration copy (KiB/dispatch) | scale | kernel (KiB/dispatch, mean of {len(kf)}) | kernel bytes/launch |
-|---|---|---|---|---|
-| FETCH_SIZE | {rec['calib_fetch_kib']:.0f} | {f_fetch:.4f} | {rec['kernel_fetch_kib']:.0f} | {fetch_b:.4e} |
-| WRITE_SIZE | {rec['calib_write_kib']:.0f} | {f_write:.4f} | {rec['kernel_write_kib']:.0f} | {write_b:.4e} |
+| | calibration copy (KiB/dispatch) | scale | op bytes/launch |
+|---|---|---|---|
+| FETCH_SIZE | {rec['calib_fetch_kib']:.0f} | {f_fetch:.4f} | {fetch_b:.4e} |
+| WRITE_SIZE | {rec['calib_write_kib']:.0f} | {f_write:.4f} | {write_b:.4e} |
 
 Traffic per launch: {fetch_b + write_b:.4e} bytes.  The counters count L2 <-> fabric bytes, so
 hits in the memory-side cache (MALL) are included: an upper proxy for DRAM bytes.
@@ -336,7 +366,7 @@ def pct(xs):
 class Model:
     """Device-resident inputs, weights and buffers of one workload."""
 
-    def __init__(self, w, sag, torch, seg_len, fused=False):
+    def __init__(self, w, sag, torch, seg_len, fused=False, col_slices="tune"):
         import numpy as np
         self.fused = fused
         dev = torch.device("cuda:0")
@@ -374,10 +404,16 @@ class Model:
         self.col_slices = {}
         for name, M in (("A", self.built.A), ("AT", self.built.AT)):
             ds = [d for d in w.dims if sag.col_slices_apply(M, d, self.tdt)]
-            if ds:
+            if not ds:
+                continue
+            if col_slices == "tune":
                 r = sag.csr_tune_col_slices(M, max(ds), self.tdt)
                 self.col_slices[name] = {"d": max(ds), "on": r["on"], "whole_ms": round(r["whole_ms"], 4),
                                          "sliced_ms": round(r["sliced_ms"], 4)}
+            else:   # fixed by the command line (profiling runs: no tuning launches)
+                on = name in col_slices.split(",")
+                sag.csr_set_col_slices(M, on)
+                self.col_slices[name] = {"d": max(ds), "on": on, "whole_ms": None, "sliced_ms": None}
         if self.col_slices:
             log(f"[bench] column slices: {self.col_slices}")
 
@@ -975,7 +1011,7 @@ def workload_with_edges(cfg, jobs, gen):
 
 def config_run(w, sag, torch, args):
     """Step time and dominant operation of one other workload at full size."""
-    m = Model(w, sag, torch, args.seg_len)
+    m = Model(w, sag, torch, args.seg_len, col_slices=args.col_slices)
     for _ in range(3):
         m.step()
     torch.cuda.synchronize()
@@ -1047,7 +1083,7 @@ def run(args, cfgs, jobs):
     t0 = time.perf_counter()
     _ = w.edges
     log(f"[bench] graph drawn in {time.perf_counter() - t0:.1f} s")
-    m = Model(w, sag, torch, args.seg_len, fused=args.fusion)
+    m = Model(w, sag, torch, args.seg_len, fused=args.fusion, col_slices=args.col_slices)
 
     if args.copy_calib:
         es = CALIB_ROW_BYTES // 2
