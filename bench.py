@@ -174,7 +174,7 @@ def summarize_counters(args):
            "kernel_fetch_kib": kfs, "kernel_write_kib": kws,
            "traffic_bytes_per_launch": int(round(fetch_b + write_b)),
            "fetch_bytes_per_launch": int(round(fetch_b)), "write_bytes_per_launch": int(round(write_b)),
-           "dispatches_per_launch": ks}
+           "dispatches_per_launch": ks, "col_slices": args.col_slices}
     cfg_arg = f" --config {args.config}" if args.config != 4 else ""
     cs_arg = f" --col-slices {args.col_slices}" if args.col_slices != "tune" else ""
     sizes_arg = f" --sizes-dir {args.sizes_dir}" if args.sizes_dir else ""
@@ -256,24 +256,34 @@ Machine-readable record (bench.py reads it while the kernel sources keep this di
     print(json.dumps(rec))
 
 
-def stored_counters(op: str):
+def col_slices_in_use(m) -> str:
+    """The matrices a model's products take in column slices ("A", "AT",
+    "A,AT"), or "off"."""
+    on = [k for k, v in sorted(m.col_slices.items()) if v["on"]]
+    return ",".join(on) if on else "off"
+
+
+def stored_counters(op: str, slices: str = "off"):
     """The counter record of `op` from a committed summary taken on the
-    current kernel sources (and the summary's path), else (None, None)."""
+    current kernel sources, and for an SpMM with the same column-slice
+    choice (and the summary's path), else (None, None)."""
     dig = sources_digest(op)
     for f in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         with open(f) as fh:
             for m in re.finditer(r"<!-- counters (\{.*\}) -->", fh.read()):
                 rec = json.loads(m.group(1))
-                if rec.get("op") == op and rec.get("sources_sha256_16") == dig:
+                same_slices = not op.startswith("spmm") or rec.get("col_slices", "off") == slices
+                if rec.get("op") == op and rec.get("sources_sha256_16") == dig and same_slices:
                     return rec, os.path.relpath(f, ROOT)
     return None, None
 
 
 
-def with_traffic(roof):
+def with_traffic(roof, slices="off"):
     """roof plus the HBM traffic of its kernel from a committed counter
-    summary taken on the current kernel sources (null fields without one)."""
-    crec, tsrc = stored_counters(roof["kernel"])
+    summary taken on the current kernel sources and the same column-slice
+    choice (null fields without one)."""
+    crec, tsrc = stored_counters(roof["kernel"], slices)
     avg_s = roof["avg_launch_ms"] / 1e3
     roof["traffic"] = crec["traffic_bytes_per_launch"] if crec else None
     roof["traffic_source"] = tsrc
@@ -1019,7 +1029,7 @@ def config_run(w, sag, torch, args):
     ms, per, recs = timed_steps(m, sag, torch, steps)
     g_ms, g_per, g_err = graph_steps(m, torch, steps)
     table, ops = op_table(recs, steps)
-    roof = with_traffic(roofline_of(table, ops, w.dtype))
+    roof = with_traffic(roofline_of(table, ops, w.dtype), col_slices_in_use(m))
     roof["gather_probe"] = gather_probe_of(roof, m.built, sag, torch) if w.cfg != 1 else None
     out = {"workload": w.name, "config": w.cfg, "dtype": w.dtype, "dims": w.dims, "layer": w.model,
            "n_local": m.n_l, "n_halo": m.n_h, "nnz": m.built.A.nnz, "build_ms": round(m.build_ms, 1),
@@ -1114,7 +1124,7 @@ def run(args, cfgs, jobs):
         errors["graph"] = g_err
     table, ops = op_table(recs, args.steps)
     spmm = [t for t in table if t["op"].startswith("spmm")]
-    roof = with_traffic(roofline_of(table, ops, w.dtype))
+    roof = with_traffic(roofline_of(table, ops, w.dtype), col_slices_in_use(m))
     log("[bench] row-gather probe over the dominant SpMM's column ids")
     roof["gather_probe"] = gather_probe_of(roof, m.built, sag, torch)
 
