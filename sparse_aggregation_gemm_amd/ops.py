@@ -299,7 +299,7 @@ def _split_once(A: Csr, n_hub: int, seg_len: int | None) -> None:
 
 COL_SLICE_BYTES = 128        # one cache line of each row of X per pass
 COL_SLICE_MIN_ROW_BYTES = 257   # rows of at most two slices are gathered whole
-COL_SLICE_MARGIN = 0.02     # slices are kept only when this much faster
+COL_SLICE_MARGIN = 0.01     # slices are kept only when this much faster
 
 
 def csr_set_col_slices(A: Csr, on: bool) -> Csr:
