@@ -1,7 +1,9 @@
 """Parity at the workloads' full sizes, in the configuration bench.py times
-(GPU CSR build with the degree-binned schedule, seg_len 1024, and the chain
-of hub splits on matrices whose rows average at least 128 entries: the dense
-GCN graph's), on outputs the oracle can compute one row at a time.
+(GPU CSR build with the degree-binned schedule, seg_len 1024, the chain of
+hub splits on matrices whose rows average at least 128 entries: the dense
+GCN graph's, and column slices on every other A: the choice the bench's
+set-up timing makes for the A of the workloads whose rows are wide enough),
+on outputs the oracle can compute one row at a time.
 
 For each workload the graph is drawn at full size and built on the GPU; the
 halo list is compared whole, and a sample of rows (random ones plus the
@@ -50,6 +52,8 @@ class Full:
             if sag.hub_split_pays(M):
                 sag.csr_hub_split(M, seg_len=SEG_LEN)
                 say(f"full-size workload {cfg}: hub chain of {len(sag.hub_chain(M)) - 1} groups")
+        if self.gb.A.hub_part is None:
+            sag.csr_set_col_slices(self.gb.A, True)
         torch.cuda.synchronize()
         self.n_l = w.hi - w.lo
         # HALO list by definition: distinct sources outside [lo, hi) of edges into the range
@@ -416,7 +420,8 @@ def check_full_output(full, d=256):
     products of the forward (A, mean-normalised: the pattern-only path) and
     of the backward (A^T, with values) compared in full, every element,
     against the oracle's fp64 SpMM (bf16 inputs and outputs, fp32
-    accumulation: within 2e-2 of the same product on absolute values)."""
+    accumulation: within 2e-2 of the same product on absolute values), each
+    both in whole rows and in 128-byte column slices."""
     w = full.w
     gb = full.gb
     say(f"full-size whole build and full-output products, workload {w.cfg}: oracle build of {gb.A.nnz} entries")
@@ -431,15 +436,22 @@ def check_full_output(full, d=256):
     Xd = to_dev_dense(X, "bf16")
     X64 = olay.as_f64(X, "bf16")
     for name, Gm, Om, fn in (("A X", gb.A, ob.A, sag.spmm_csr), ("A^T X", gb.AT, ob.AT, sag.spmm_csr_t)):
-        say(f"  {name}: GPU product, then the oracle's fp64 product and bound ({native.num_threads()} threads)")
-        Y = f64(fn(Gm, Xd))
+        say(f"  {name}: GPU products, then the oracle's fp64 product and bound ({native.num_threads()} threads)")
+        kept = Gm.col_slices
+        Ys = {}
+        for sliced in (False, True):
+            sag.csr_set_col_slices(Gm, sliced)
+            Ys[sliced] = f64(fn(Gm, Xd))
+        sag.csr_set_col_slices(Gm, kept)
         ref = native.spmm(Om.indptr, Om.indices, Om.values, X64)
-        err = 0.0
-        step = 1 << 18
         den = native.spmm(Om.indptr, Om.indices, Om.values, np.abs(X64), abs_mode=True)
-        for r0 in range(0, Y.shape[0], step):
-            sl = slice(r0, r0 + step)
-            err = max(err, float(np.max(np.abs(Y[sl] - ref[sl]) / (den[sl] + 1e-30))))
-        say(f"  {name}: max error {err:.2e} of the bound over {Y.size} elements")
-        assert err <= tol("bf16"), f"{name} err {err:.2e}"
-        del Y, ref, den
+        step = 1 << 18
+        for sliced, Y in Ys.items():
+            err = 0.0
+            for r0 in range(0, Y.shape[0], step):
+                sl = slice(r0, r0 + step)
+                err = max(err, float(np.max(np.abs(Y[sl] - ref[sl]) / (den[sl] + 1e-30))))
+            how = "column slices" if sliced else "whole rows"
+            say(f"  {name} ({how}): max error {err:.2e} of the bound over {Y.size} elements")
+            assert err <= tol("bf16"), f"{name} ({how}) err {err:.2e}"
+        del Ys, ref, den
