@@ -317,15 +317,15 @@ def col_slices_apply(A: Csr, d: int, dtype: torch.dtype) -> bool:
     return A.hub_part is None and d * es >= COL_SLICE_MIN_ROW_BYTES
 
 
-def csr_tune_col_slices(A: Csr, d: int, dtype: torch.dtype, reps: int = 3,
+def csr_tune_col_slices(A: Csr, d: int, dtype: torch.dtype, reps: int = 5,
                         margin: float = COL_SLICE_MARGIN) -> dict:
     """Time the product over A at width d both ways (random X, the library's
-    own entry point, HIP events on the current stream, rounds alternated,
-    medians) and set A's col_slices when slices are faster by more than
-    `margin`.  Whether slices pay depends on how much of the matrix its
-    busiest columns carry, so it is measured on the matrix itself.  Returns
-    {"on", "whole_ms", "sliced_ms"} (timings None where slices cannot
-    apply)."""
+    own entry point, HIP events on the current stream, a warm round then
+    `reps` rounds alternated, medians) and set A's col_slices when slices
+    are faster by more than `margin`.  Whether slices pay depends on how much
+    of the matrix its busiest columns carry, so it is measured on the matrix
+    itself.  Returns {"on", "whole_ms", "sliced_ms"} (timings None where
+    slices cannot apply)."""
     if not col_slices_apply(A, d, dtype) or A.nnz == 0:
         csr_set_col_slices(A, False)
         return {"on": False, "whole_ms": None, "sliced_ms": None}
