@@ -64,8 +64,9 @@ def test_sliced_spmm_against_oracle(dt, out_dt, d, cfg, scale, norm):
     assert e <= bound, f"A^T: err {e:.3e}"
 
 
+@pytest.mark.parametrize("scheduled", [True, False])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-def test_sliced_exact_small_integers_with_long_and_empty_rows(dt):
+def test_sliced_exact_small_integers_with_long_and_empty_rows(dt, scheduled):
     """Star centres far longer than a segment, rows without entries, values 1
     and integer features: every sum is exact, so each slice's columns equal
     the exact result bit for bit (a slice reading the wrong columns of X or
@@ -76,14 +77,15 @@ def test_sliced_exact_small_integers_with_long_and_empty_rows(dt):
     dst = np.concatenate([np.full(n - 10, c, np.int32) for c in (0, 1, 2)] +
                          [g.integers(3, n - 50, 20000).astype(np.int32)])
     gb = sag.csr_build_normalize(to_dev(src), to_dev(dst), n, 0, n, False, False, "none", transpose=False)
-    sag.csr_schedule(gb.A, 64)
-    assert sag.csr_info(gb.A)["n_long"] > 0
+    if scheduled:   # else every row is summed as a medium row, in natural order
+        sag.csr_schedule(gb.A, 64)
+        assert sag.csr_info(gb.A)["n_long"] > 0
     sag.csr_set_col_slices(gb.A, True)
     ob = ocsr.build(src, dst, n, 0, n, False, False, "none")
     d = 150 if dt == "f32" else 230
     X = g.integers(-4, 5, (n, d)).astype(np.float32)
     Xd = to_dev_dense(X if dt == "f32" else gen.f32_to_bf16_bits(X), dt)
-    say(f"sliced exact integers dt={dt} d={d}")
+    say(f"sliced exact integers dt={dt} d={d} scheduled={scheduled}")
     Y = sag.spmm_csr(gb.A, Xd, out_dtype=torch.float32)
     assert np.array_equal(f64(Y), native.spmm(ob.A.indptr, ob.A.indices, ob.A.values, X.astype(np.float64)))
 
