@@ -68,7 +68,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--config", type=int, default=4)
     p.add_argument("--scale", type=float, default=1.0)
-    p.add_argument("--seg-len", type=int, default=1024)
+    p.add_argument("--seg-len", type=int, default=0,
+                   help="long-row segment length of every schedule (0: the binding's auto_seg_len per matrix)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--configs", default="1,2,3,5",
                    help="other workloads timed at full size after the headline (comma list; empty: none)")
@@ -389,6 +390,7 @@ class Model:
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         self.built = sag.csr_build_normalize(s_d, d_d, w.n_global, w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
+        seg_len = seg_len or None   # None: each matrix's own auto_seg_len
         sag.csr_schedule(self.built.A, seg_len)
         sag.csr_schedule(self.built.AT, seg_len)
         # graphs with many entries per row: products in two passes (hub columns, then the rest)
@@ -656,8 +658,8 @@ def overlapped_pull(sag, torch, np, w, steps=10):
     src, dst = w.edges
     gb = sag.csr_build_normalize(torch.from_numpy(src).to(dev), torch.from_numpy(dst).to(dev), w.n_global,
                                  w.lo, w.hi, w.symmetrize, w.self_loops, w.norm)
-    sag.csr_schedule(gb.A, 1024)
-    sag.csr_schedule(gb.AT, 1024)
+    sag.csr_schedule(gb.A)
+    sag.csr_schedule(gb.AT)
     d, bf = 128, torch.bfloat16
     g = torch.Generator(device=dev)
     g.manual_seed(3)
@@ -1139,7 +1141,8 @@ def run(args, cfgs, jobs):
     A = m.built.A
     conf = {"workload": w.name, "config": args.config, "scale": args.scale, "n_local": m.n_l,
             "n_halo": m.n_h, "nnz": A.nnz, "dims": w.dims, "layer": w.model,
-            "seg_len": args.seg_len, "schedule": sag.csr_info(A), "fusion": args.fusion,
+            "seg_len": {"A": m.built.A.raw.seg_len, "AT": m.built.AT.raw.seg_len},
+            "schedule": sag.csr_info(A), "fusion": args.fusion,
             "hub_split": m.hub_split or None, "col_slices": m.col_slices or None,
             "graph": m.graph_stats}
     build_ms = m.build_ms

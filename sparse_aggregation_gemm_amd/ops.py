@@ -11,6 +11,7 @@ such a tensor with the row padded.  bf16 tensors are torch.bfloat16.
 from __future__ import annotations
 
 import ctypes
+import math
 from dataclasses import dataclass, field
 
 import torch
@@ -200,9 +201,32 @@ def csr_build_normalize(src: torch.Tensor, dst: torch.Tensor, n_global: int, lo:
     return Built(A, AT, deg[:n_ext], halo[:n_halo])
 
 
-def csr_schedule(A: Csr, seg_len: int = 1024) -> Csr:
-    """sag_csr_schedule: attach the degree-binned schedule to A (in place).
-    Synchronises the current stream."""
+# Long rows are cut into segments of seg_len entries, one wavefront each.
+# Longer segments mean fewer fp32 partial rows and reduce steps, shorter ones
+# a smaller last wavefront at the end of a launch.  Measured per product
+# (2.45M-node graph 126M entries: 1024 -> 4096 saves 0.3 ms of the step's
+# SpMMs; 100M-graph share 194M entries: 7.49 -> 7.26 ms; R-MAT partition
+# 7.9M entries and the hub parts of the dense GCN graph, 2-42M entries each:
+# 1024 best, 8192 up to 40% slower), so the length follows the entries a
+# launch spreads over the chip's ~8,192 resident wavefronts: a quarter of
+# each one's share, nnz / 32768, to the nearest power of two in [1024, 4096].
+SEG_LEN_ENTRIES = 32768
+SEG_LEN_MIN, SEG_LEN_MAX = 1024, 4096
+
+
+def auto_seg_len(A: Csr) -> int:
+    """The segment length csr_schedule uses for A when given none."""
+    x = max(A.nnz, 1) / SEG_LEN_ENTRIES
+    p = 1 << max(0, round(math.log2(x)))
+    return min(max(p, SEG_LEN_MIN), SEG_LEN_MAX)
+
+
+def csr_schedule(A: Csr, seg_len: int | None = None) -> Csr:
+    """sag_csr_schedule: attach the degree-binned schedule to A (in place),
+    with long rows cut into segments of seg_len entries (None:
+    auto_seg_len(A)).  Synchronises the current stream."""
+    if seg_len is None:
+        seg_len = auto_seg_len(A)
     lib = L.lib()
     dev = A.device
     nb = lib.sag_csr_schedule_bytes(A.n_rows, A.nnz, seg_len)
@@ -234,8 +258,8 @@ def hub_split_pays(A: Csr) -> bool:
 
 def csr_hub_split(A: Csr, n_hub: int = HUB_COLS, seg_len: int | None = None, levels: int | None = None) -> Csr:
     """sag_csr_hub_split: split A's entries into those of the n_hub columns
-    holding the most entries and the rest, schedule both parts (seg_len:
-    A's own when it has a schedule, else 1024) and attach them to A (in
+    holding the most entries and the rest, schedule both parts (seg_len;
+    None: each part's own auto_seg_len) and attach them to A (in
     place); then split the cold part the same way, and so on: `levels`
     times, or (None) while the last hub part held at least HUB_MIN_SHARE of
     A's entries (at most HUB_MAX_LEVELS).  Products over A take one pass per
@@ -290,7 +314,7 @@ def _split_once(A: Csr, n_hub: int, seg_len: int | None) -> None:
     for (ip, ix, vv), k in zip(bufs, (nh, A.nnz - nh)):
         # exact-size copies, so that the parts hold no spare capacity
         P = Csr(A.n_rows, A.n_cols, ip, ix[:k].clone(), vv[:k].clone() if vv is not None else None)
-        csr_schedule(P, seg_len or (A.raw.seg_len if A.sched is not None else 1024))
+        csr_schedule(P, seg_len)
         parts.append(P)
     A.hub_part, A.cold_part = parts
     A.raw.hub_part = ctypes.addressof(parts[0].raw)

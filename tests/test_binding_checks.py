@@ -72,3 +72,11 @@ def test_gather_push_and_gemm_sizes():
         sag.gemm(z(6, 4), z(4, 3), addend=z(5, 3))
     with pytest.raises(ValueError, match="gemm_tn B has 5 rows"):
         sag.gemm_tn(z(6, 4), z(5, 3))
+
+
+@pytest.mark.parametrize("nnz,want", [(0, 1024), (36_864, 1024), (7_918_846, 1024), (41_900_000, 1024),
+                                      (50_000_000, 2048), (114_828_449, 4096), (126_150_500, 4096),
+                                      (193_750_000, 4096), (3 * 10 ** 9, 4096)])
+def test_auto_segment_length(nnz, want):
+    """nnz / 32768 to the nearest power of two, within [1024, 4096]."""
+    assert sag.auto_seg_len(SimpleNamespace(nnz=nnz)) == want

@@ -1,5 +1,6 @@
 """Parity at the workloads' full sizes, in the configuration bench.py times
-(GPU CSR build with the degree-binned schedule, seg_len 1024, the chain of
+(GPU CSR build with the degree-binned schedule, each matrix's automatic
+segment length (1024 or 4096 entries by its size), the chain of
 hub splits on matrices whose rows average at least 128 entries: the dense
 GCN graph's, and column slices on every other A: the choice the bench's
 set-up timing makes for the A of the workloads whose rows are wide enough),
@@ -29,7 +30,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 sag = pytest.importorskip("sparse_aggregation_gemm_amd")
 from gpu_util import DEV, f64, round_to, say, to_dev, to_dev_dense, tol  # noqa: E402
 
-SEG_LEN = 1024
+SEG_LEN = None   # each matrix's own auto_seg_len, as the bench schedules
 
 
 def _bits_or_f32(x, dt):
