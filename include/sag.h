@@ -148,8 +148,9 @@ enum {
  * Training", the 2D section's block decomposition and the 3D section's
  * shorter, fatter pieces of H), run one block after another on one GPU:
  * every gather of a pass reads one cache line, so each L2 holds the lines of
- * four times as many rows of X as with whole rows, and on degree laws whose
- * busiest columns carry much of the matrix more of them hit.  The price is
+ * as many times more rows of X as a whole row spans lines (four at 512-byte
+ * rows), and on degree laws whose busiest columns carry much of the matrix
+ * more of the gathers hit.  The price is
  * one more pass over the indices (and values) per slice and per-row work
  * repeated per slice, so whether it pays depends on the matrix (measured:
  * about 5% saved at 512-byte rows on a 2.45M-node power-law graph with 51
@@ -157,8 +158,7 @@ enum {
  * by timing both on the matrix.  Rows of at most 256 bytes are always
  * gathered whole (two slices gain too little L2 reach for the second pass).
  * The result differs from the whole-row product only by fp32 summation
- * order.
- * Ignored by a matrix with a hub split (its passes take whole rows), by the
+ * order.  Ignored by a matrix with a hub split (its passes take whole rows), by the
  * fused aggregate -> transform kernel and by GAT. */
 typedef struct sag_csr {
     int64_t n_rows;
